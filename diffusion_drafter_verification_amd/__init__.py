@@ -1,0 +1,179 @@
+"""MI355X (gfx950) verify-and-supervise pass for diffusion-drafter speculative decoding.
+
+A thin ctypes binding over the C ABI in ``include/adaflash.h`` (built into
+``libadaflash.so`` next to this file).  The binding only marshals arguments:
+torch tensors provide device memory and the current HIP stream; every step of
+the computation runs in the library's kernels.  There is no CPU fallback: if
+the library is missing or the tensors are not on the GPU, calls raise.
+
+Entry points (same names as the C ABI):
+  adaflash_verify(...)            speculative verification, optional fused supervision
+  adaflash_opd_loss_fwd_bwd(...)  supervision only
+  adaflash_workspace_bytes(B, k, V)
+Convenience wrappers allocating the outputs: ``verify`` and ``opd_loss_fwd_bwd``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libadaflash.so")
+
+ADAFLASH_F32 = 0
+ADAFLASH_BF16 = 1
+FLAG_BAD_VERIFY_LEN = 1
+FLAG_BAD_TOKEN = 2
+FLAG_NONFINITE = 4
+FLAG_SYNC_TIMEOUT = 8
+
+_lib = None
+
+
+class AdaflashError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"adaflash error {code}: {msg}")
+        self.code = code
+
+
+def load_library() -> ctypes.CDLL:
+    """Loads libadaflash.so (after torch, so both share one HIP runtime)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                              "(the GPU path has no fallback)")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        lib.adaflash_version.restype = i32
+        lib.adaflash_version.argtypes = []
+        lib.adaflash_last_error.restype = ctypes.c_char_p
+        lib.adaflash_last_error.argtypes = []
+        lib.adaflash_workspace_bytes.restype = sz
+        lib.adaflash_workspace_bytes.argtypes = [i32, i32, i32]
+        lib.adaflash_verify.restype = i32
+        lib.adaflash_verify.argtypes = [i32, vp, vp, vp, vp, vp, i32, i32, i32, f32, vp, vp, vp,
+                                        f32, f32, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.adaflash_opd_loss_fwd_bwd.restype = i32
+        lib.adaflash_opd_loss_fwd_bwd.argtypes = [i32, vp, vp, vp, i32, i32, i32, f32, f32, vp, vp,
+                                                  vp, vp, vp, vp, sz, vp]
+        _lib = lib
+    return _lib
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("adaflash works on GPU tensors only")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return ADAFLASH_BF16
+    if t.dtype == torch.float32:
+        return ADAFLASH_F32
+    raise TypeError("logits must be bfloat16 or float32")
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise AdaflashError(rc, load_library().adaflash_last_error().decode())
+
+
+def adaflash_workspace_bytes(B: int, k: int, V: int) -> int:
+    return int(load_library().adaflash_workspace_bytes(B, k, V))
+
+
+def workspace(B: int, k: int, V: int, device="cuda") -> torch.Tensor:
+    n = adaflash_workspace_bytes(B, k, V)
+    if n == 0:
+        raise ValueError("invalid sizes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def adaflash_verify(target, draft, tokens, verify_len, uniforms, T, accept_len, out_tokens, margins,
+                    clip_c, lam, row_offsets, loss_ce, loss_rkl, grad_draft, status, ws,
+                    stream=None) -> None:
+    """Direct binding of adaflash_verify (see include/adaflash.h)."""
+    B, k1, V = target.shape
+    rc = load_library().adaflash_verify(
+        _dtype_code(target), _ptr(target), _ptr(draft), _ptr(tokens), _ptr(verify_len), _ptr(uniforms),
+        B, k1 - 1, V, float(T), _ptr(accept_len), _ptr(out_tokens), _ptr(margins), float(clip_c),
+        float(lam), _ptr(row_offsets), _ptr(loss_ce), _ptr(loss_rkl), _ptr(grad_draft), _ptr(status),
+        _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream))
+    _check(rc)
+
+
+def adaflash_opd_loss_fwd_bwd(target, draft, verify_len, clip_c, lam, row_offsets, loss_ce,
+                              loss_rkl, grad_draft, status, ws, stream=None) -> None:
+    """Direct binding of adaflash_opd_loss_fwd_bwd (see include/adaflash.h)."""
+    B, k1, V = target.shape
+    rc = load_library().adaflash_opd_loss_fwd_bwd(
+        _dtype_code(target), _ptr(target), _ptr(draft), _ptr(verify_len), B, k1 - 1, V, float(clip_c),
+        float(lam), _ptr(row_offsets), _ptr(loss_ce), _ptr(loss_rkl), _ptr(grad_draft), _ptr(status),
+        _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream))
+    _check(rc)
+
+
+def verify(target: torch.Tensor, draft: Optional[torch.Tensor], tokens: torch.Tensor,
+           verify_len: torch.Tensor, uniforms: Optional[torch.Tensor], T: float,
+           opd: bool = False, clip_c: float = 10.0, lam: float = 1.0, margins: bool = True,
+           ws: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """Allocates the outputs and calls adaflash_verify.  The supervision
+    outputs (loss_ce, loss_rkl, grad [B*k, V] of which N rows are written)
+    are produced only when ``opd`` is true."""
+    B, k1, V = target.shape
+    k = k1 - 1
+    dev = target.device
+    out = {
+        "accept_len": torch.empty(B, dtype=torch.int32, device=dev),
+        "out_tokens": torch.empty(B, k1, dtype=torch.int32, device=dev),
+        "margins": torch.empty(B, k1, dtype=torch.float32, device=dev) if margins else None,
+        "row_offsets": torch.empty(B + 1, dtype=torch.int32, device=dev),
+        "status": torch.empty(1, dtype=torch.int32, device=dev),
+        "loss_ce": None, "loss_rkl": None, "grad": None,
+    }
+    if opd:
+        out["loss_ce"] = torch.empty(B * k, dtype=torch.float32, device=dev)
+        out["loss_rkl"] = torch.empty(B * k, dtype=torch.float32, device=dev)
+        out["grad"] = torch.empty(B * k, V, dtype=target.dtype, device=dev)
+    if ws is None:
+        ws = workspace(B, k, V, dev)
+    adaflash_verify(target, draft, tokens, verify_len, uniforms, T, out["accept_len"],
+                    out["out_tokens"], out["margins"], clip_c, lam, out["row_offsets"], out["loss_ce"],
+                    out["loss_rkl"], out["grad"], out["status"], ws, stream)
+    return out
+
+
+def opd_loss_fwd_bwd(target: torch.Tensor, draft: torch.Tensor, verify_len: Optional[torch.Tensor],
+                     clip_c: float = 10.0, lam: float = 1.0, with_grad: bool = True,
+                     ws: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """Allocates the outputs and calls adaflash_opd_loss_fwd_bwd."""
+    B, k1, V = target.shape
+    k = k1 - 1
+    dev = target.device
+    out = {
+        "row_offsets": torch.empty(B + 1, dtype=torch.int32, device=dev),
+        "status": torch.empty(1, dtype=torch.int32, device=dev),
+        "loss_ce": torch.empty(B * k, dtype=torch.float32, device=dev),
+        "loss_rkl": torch.empty(B * k, dtype=torch.float32, device=dev),
+        "grad": torch.empty(B * k, V, dtype=target.dtype, device=dev) if with_grad else None,
+    }
+    if ws is None:
+        ws = workspace(B, k, V, dev)
+    adaflash_opd_loss_fwd_bwd(target, draft, verify_len, clip_c, lam, out["row_offsets"],
+                              out["loss_ce"], out["loss_rkl"], out["grad"], out["status"], ws, stream)
+    return out

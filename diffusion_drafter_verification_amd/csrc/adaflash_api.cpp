@@ -1,0 +1,185 @@
+// C-ABI entry points: argument validation, workspace layout, launch.
+// The maths lives in adaflash_kernels.hip; see include/adaflash.h for the
+// contract of every entry point.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/adaflash.h"
+#include "adaflash_internal.h"
+
+namespace adaflash {
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, const char* detail = "") {
+  std::snprintf(g_err, sizeof(g_err), fmt, detail);
+  return code;
+}
+
+inline size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool sizes_ok(int B, int k, int V) {
+  if (B < 0 || k < 1 || k > 64 || V < 1 || V > (1 << 20)) return false;
+  if ((long long)B * (k + 1) >= (1LL << 24)) return false;
+  return true;
+}
+
+}  // namespace
+
+size_t workspace_layout(int B, int k, int V, char* base, Workspace* ws) {
+  const size_t rows = (size_t)B * (k + 1);
+  const size_t G = (size_t)num_chunks(V);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = align_up(off + bytes);
+    return base ? base + at : nullptr;
+  };
+  char* nrows = take(sizeof(int32_t));
+  char* Lc = take(sizeof(int32_t) * (size_t)(B > 0 ? B : 1));
+  char* roff = take(sizeof(int32_t) * (size_t)(B + 1));
+  char* rowlist = take(sizeof(int32_t) * (rows > 0 ? rows : 1));
+  char* rowcnt = take(sizeof(int32_t) * (rows > 0 ? rows : 1));
+  char* reqcnt = take(sizeof(int32_t) * (size_t)(B > 0 ? B : 1));
+  char* part1 = take(sizeof(float4) * 2 * (rows > 0 ? rows : 1) * G);
+  char* part2 = take(sizeof(float4) * (rows > 0 ? rows : 1) * G);
+  char* rowrec = take(sizeof(int4) * (rows > 0 ? rows : 1));
+  if (ws) {
+    ws->nrows = (int32_t*)nrows;
+    ws->Lc = (int32_t*)Lc;
+    ws->roff = (int32_t*)roff;
+    ws->rowlist = (int32_t*)rowlist;
+    ws->rowcnt = (int32_t*)rowcnt;
+    ws->reqcnt = (int32_t*)reqcnt;
+    ws->part1 = (float4*)part1;
+    ws->part2 = (float4*)part2;
+    ws->rowrec = (int4*)rowrec;
+  }
+  return off;
+}
+
+}  // namespace adaflash
+
+using namespace adaflash;
+
+extern "C" {
+
+int adaflash_version(void) { return 100; }
+
+const char* adaflash_last_error(void) { return g_err; }
+
+size_t adaflash_workspace_bytes(int B, int k, int V) {
+  if (!sizes_ok(B, k, V)) return 0;
+  return workspace_layout(B, k, V, nullptr, nullptr);
+}
+
+static int common_checks(adaflash_dtype dtype, const void* target, const void* draft, int B, int k,
+                         int V, int32_t* row_offsets, void* workspace, size_t workspace_bytes,
+                         bool need_draft) {
+  if (dtype != ADAFLASH_F32 && dtype != ADAFLASH_BF16) return fail(ADAFLASH_E_INVALID, "invalid dtype%s");
+  if (!sizes_ok(B, k, V))
+    return fail(ADAFLASH_E_INVALID,
+                "invalid sizes%s: need B >= 0, 1 <= k <= 64, 1 <= V <= 2^20, B*(k+1) < 2^24");
+  if (!row_offsets) return fail(ADAFLASH_E_INVALID, "row_offsets must not be NULL%s");
+  if (B > 0 && !target) return fail(ADAFLASH_E_INVALID, "target_logits must not be NULL%s");
+  if (B > 0 && need_draft && !draft) return fail(ADAFLASH_E_INVALID, "draft_logits must not be NULL%s");
+  const size_t need = workspace_layout(B, k, V, nullptr, nullptr);
+  if (!workspace || workspace_bytes < need)
+    return fail(ADAFLASH_E_WORKSPACE, "workspace missing or smaller than adaflash_workspace_bytes()%s");
+  return ADAFLASH_OK;
+}
+
+static int run(LaunchArgs& a, void* workspace) {
+  workspace_layout(a.B, a.k, a.V, (char*)workspace, &a.ws);
+  const hipError_t e = launch(a);
+  if (e != hipSuccess) return fail(ADAFLASH_E_HIP, "HIP launch failed: %s", hipGetErrorString(e));
+  g_err[0] = 0;
+  return ADAFLASH_OK;
+}
+
+int adaflash_verify(adaflash_dtype dtype, const void* target_logits, const void* draft_logits,
+                    const int32_t* draft_tokens, const int32_t* verify_len, const float* uniforms,
+                    int B, int k, int V, float T, int32_t* accept_len, int32_t* out_tokens,
+                    float* margins, float clip_c, float lambda, int32_t* row_offsets,
+                    float* loss_ce, float* loss_rkl, void* grad_draft, int32_t* status_flags,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  const bool opd = loss_ce || loss_rkl || grad_draft;
+  if (!(T >= 0.f) || std::isinf(T)) return fail(ADAFLASH_E_INVALID, "T must be finite and >= 0%s");
+  const bool need_draft = T > 0.f || opd;
+  int rc = common_checks(dtype, target_logits, draft_logits, B, k, V, row_offsets, workspace,
+                         workspace_bytes, need_draft);
+  if (rc != ADAFLASH_OK) return rc;
+  if (B > 0 && (!draft_tokens || !verify_len || !accept_len || !out_tokens))
+    return fail(ADAFLASH_E_INVALID, "draft_tokens, verify_len, accept_len and out_tokens must not be NULL%s");
+  if (B > 0 && T > 0.f && !uniforms) return fail(ADAFLASH_E_INVALID, "uniforms must not be NULL when T > 0%s");
+  if (opd && !(clip_c > 0.f)) return fail(ADAFLASH_E_INVALID, "clip_c must be > 0%s");
+  if (opd && !(lambda >= 0.f) ) return fail(ADAFLASH_E_INVALID, "lambda must be >= 0%s");
+  if (opd && (std::isinf(lambda))) return fail(ADAFLASH_E_INVALID, "lambda must be finite%s");
+
+  LaunchArgs a{};
+  a.bf16 = dtype == ADAFLASH_BF16;
+  a.target = target_logits;
+  a.draft = draft_logits;
+  a.tokens = draft_tokens;
+  a.verify_len = verify_len;
+  a.uniforms = uniforms;
+  a.B = B;
+  a.k = k;
+  a.V = V;
+  a.T = T;
+  a.verify = 1;
+  a.opd = opd ? 1 : 0;
+  a.clip_c = clip_c;
+  a.lambda = lambda;
+  a.accept_len = accept_len;
+  a.out_tokens = out_tokens;
+  a.margins = margins;
+  a.row_offsets = row_offsets;
+  a.loss_ce = loss_ce;
+  a.loss_rkl = loss_rkl;
+  a.grad = grad_draft;
+  a.status = status_flags;
+  a.stream = (hipStream_t)stream;
+  return run(a, workspace);
+}
+
+int adaflash_opd_loss_fwd_bwd(adaflash_dtype dtype, const void* target_logits,
+                              const void* draft_logits, const int32_t* verify_len, int B, int k,
+                              int V, float clip_c, float lambda, int32_t* row_offsets,
+                              float* loss_ce, float* loss_rkl, void* grad_draft,
+                              int32_t* status_flags, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  int rc = common_checks(dtype, target_logits, draft_logits, B, k, V, row_offsets, workspace,
+                         workspace_bytes, true);
+  if (rc != ADAFLASH_OK) return rc;
+  if (!(clip_c > 0.f)) return fail(ADAFLASH_E_INVALID, "clip_c must be > 0%s");
+  if (!(lambda >= 0.f) || std::isinf(lambda)) return fail(ADAFLASH_E_INVALID, "lambda must be finite and >= 0%s");
+
+  LaunchArgs a{};
+  a.bf16 = dtype == ADAFLASH_BF16;
+  a.target = target_logits;
+  a.draft = draft_logits;
+  a.verify_len = verify_len;
+  a.B = B;
+  a.k = k;
+  a.V = V;
+  a.T = 1.f;
+  a.verify = 0;
+  a.opd = 1;
+  a.clip_c = clip_c;
+  a.lambda = lambda;
+  a.row_offsets = row_offsets;
+  a.loss_ce = loss_ce;
+  a.loss_rkl = loss_rkl;
+  a.grad = grad_draft;
+  a.status = status_flags;
+  a.stream = (hipStream_t)stream;
+  return run(a, workspace);
+}
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// Internal interface between the C-ABI entry points (adaflash_api.cpp) and
+// the gfx950 kernels (adaflash_kernels.hip).  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace adaflash {
+
+// Workgroup size and elements of each logit row a thread keeps in registers.
+constexpr int kThreads = 256;
+constexpr int kElems = 16;
+constexpr int kChunk = kThreads * kElems;  // elements of one row per workgroup
+
+inline int num_chunks(int V) { return (V + kChunk - 1) / kChunk; }
+
+// Device scratch carved out of the caller's workspace.
+struct Workspace {
+  int32_t* nrows;    // [1]    rows in the row list
+  int32_t* Lc;       // [B]    clamped verify lengths
+  int32_t* roff;     // [B+1]  start of each request in the row list
+  int32_t* rowlist;  // [B*(k+1)] target row index b*(k+1)+i of each listed row
+  int32_t* rowcnt;   // [B*(k+1)] per-row arrival counters (zeroed per call)
+  int32_t* reqcnt;   // [B]    per-request arrival counters (zeroed per call)
+  float4* part1;     // [B*(k+1)*G*2] per-chunk row statistics
+  float4* part2;     // [B*(k+1)*G]   per-chunk supervision / residual partials
+  int4* rowrec;      // [B*(k+1)] per-row accept flag and margin
+};
+
+// Layout of the workspace for (B, k, V); returns the bytes needed.  With
+// base == nullptr only the size is computed.
+size_t workspace_layout(int B, int k, int V, char* base, Workspace* ws);
+
+struct LaunchArgs {
+  int bf16;               // 1: bf16 logits, 0: fp32
+  const void* target;     // [B, k+1, V]
+  const void* draft;      // [B, k, V] (may be null for greedy verify without supervision)
+  const int32_t* tokens;  // [B, k] (verify only)
+  const int32_t* verify_len;  // [B] or null (= k)
+  const float* uniforms;  // [B, k+1] (sampled verify only)
+  int B, k, V;
+  float T;                // verify temperature (0: greedy)
+  int verify;             // 1: verify the batch
+  int opd;                // 1: supervision outputs requested
+  float clip_c, lambda;
+  int32_t* accept_len;
+  int32_t* out_tokens;
+  float* margins;
+  int32_t* row_offsets;
+  float* loss_ce;
+  float* loss_rkl;
+  void* grad;
+  int32_t* status;
+  Workspace ws;
+  hipStream_t stream;
+};
+
+// Enqueues the pack kernel and the row kernel.  Returns hipSuccess or the
+// launch error.
+hipError_t launch(const LaunchArgs& a);
+
+}  // namespace adaflash

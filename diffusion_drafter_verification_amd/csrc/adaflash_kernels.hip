@@ -1,0 +1,954 @@
+// gfx950 (CDNA4) kernels for the ragged verify-and-supervise pass.
+//
+// Work decomposition
+//   The pack kernel clamps the verify lengths, builds the list of rows that
+//   must be read -- request b contributes its L_b verified rows plus, when
+//   verifying, its bonus row L_b -- and clears the arrival counters.
+//
+//   The row kernel gives each (row, chunk) pair one 256-thread workgroup.  A
+//   chunk is kChunk = 4096 consecutive vocabulary entries; each thread keeps
+//   16 entries of the target row and 16 of the draft row in registers, loaded
+//   with 16-byte coalesced loads.  Row-global quantities (maxima, sums of
+//   exponentials, the supervision sums) are exchanged between the chunks of a
+//   row through per-chunk partial records and an arrival counter: every
+//   workgroup publishes its partial, increments the row counter and waits for
+//   the others, then combines all partials in chunk order (so every chunk
+//   derives bit-identical row statistics).  The logits therefore cross HBM
+//   exactly once however many logical passes the maths needs.
+//
+//   Each wait is bounded: past the bound the workgroup sets
+//   ADAFLASH_FLAG_SYNC_TIMEOUT and leaves, so the grid always drains.  A
+//   row's workgroups have consecutive ids and depend only on each other;
+//   with workgroups dispatched in id order, a waiting workgroup's partners are
+//   resident or next in line, so the bound is never reached in practice.
+//
+//   The last workgroup of a request to finish (request arrival counter) runs
+//   the finaliser: first rejection, then the correction draw from the residual
+//   max(0, p - q) of row A or the bonus draw from target row L, by locating
+//   the chunk whose cumulative mass crosses the threshold and scanning only
+//   that chunk.
+//
+// Maths (pages cited in adaflash.h):
+//   p = softmax(z_p / T), q = softmax(z_q / T); accept x_i iff u_i q(x_i) < p(x_i);
+//   residual r = max(0, p_A - q_A); draw = smallest v with running sum > u Z.
+//   Supervision at temperature 1, per verified row:
+//     lq = z_q - lse_q, lp = z_p - lse_p, q = exp(lq), f = q (lq - lp),
+//     U = {v : f_v <= c}, R = sum_U f + c |V \ U|, S = sum_U (f + q),
+//     CE = lse_q - z_q[x*], grad = q - e_{x*} + lambda q (1_U (lq - lp + 1) - S).
+//   Exponentials use v_exp_f32 (2^x) on log2-scaled arguments.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "adaflash_internal.h"
+
+#define ADAFLASH_FLAG_BAD_VERIFY_LEN 1
+#define ADAFLASH_FLAG_BAD_TOKEN 2
+#define ADAFLASH_FLAG_NONFINITE 4
+#define ADAFLASH_FLAG_SYNC_TIMEOUT 8
+
+namespace adaflash {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.69314718055994531f;
+constexpr int kWaves = kThreads / 64;
+constexpr int kIntMax = 0x7fffffff;
+constexpr int kSpinLimit = 1 << 18;  // bound on polls (s_sleep between polls)
+
+struct KParams {
+  const void* target;
+  const void* draft;
+  const int32_t* tokens;
+  const float* uniforms;
+  int32_t* accept_len;
+  int32_t* out_tokens;
+  float* margins;
+  const int32_t* row_offsets;
+  float* loss_ce;
+  float* loss_rkl;
+  void* grad;
+  int32_t* status;
+  const int32_t* nrows;
+  const int32_t* Lc;
+  const int32_t* roff;
+  const int32_t* rowlist;
+  int32_t* rowcnt;
+  int32_t* reqcnt;
+  float4* part1;
+  float4* part2;
+  int4* rowrec;
+  int B, k, V, G;
+  float kT;  // log2(e) / T (0 in greedy mode)
+  float clip_c, lambda;
+};
+
+// ---------------------------------------------------------------- primitives
+
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float flog2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(dpp_i<CTRL>(__float_as_int(v)));
+}
+
+// Butterfly inside each 16-lane row (xor 1, xor 2, mirror 8, mirror 16): every
+// lane of a row ends with the bit-identical row result; the four row results
+// are then combined in a fixed order.  Must be called with all lanes active.
+enum { OP_SUM = 0, OP_MAX = 1, OP_MINI = 2 };
+
+template <int OP>
+__device__ __forceinline__ float op2(float a, float b) {
+  if constexpr (OP == OP_SUM) return a + b;
+  if constexpr (OP == OP_MAX) return fmaxf(a, b);
+  return __int_as_float(min(__float_as_int(a), __float_as_int(b)));
+}
+
+template <int OP>
+__device__ __forceinline__ float wave_reduce(float v) {
+  v = op2<OP>(v, dpp_f<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = op2<OP>(v, dpp_f<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = op2<OP>(v, dpp_f<0x141>(v));  // row_half_mirror
+  v = op2<OP>(v, dpp_f<0x140>(v));  // row_mirror
+  float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return op2<OP>(op2<OP>(r0, r1), op2<OP>(r2, r3));
+}
+
+// Workgroup reduction of N values with per-value operators; every thread gets
+// the same results.  `red` is shared scratch of kWaves*N floats.
+template <int N>
+__device__ __forceinline__ void wg_reduce(float (&v)[N], const int (&ops)[N], float* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    float x = v[n];
+    if (ops[n] == OP_SUM) x = wave_reduce<OP_SUM>(x);
+    else if (ops[n] == OP_MAX) x = wave_reduce<OP_MAX>(x);
+    else x = wave_reduce<OP_MINI>(x);
+    v[n] = x;
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int n = 0; n < N; ++n) red[wave * N + n] = v[n];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    float a = red[0 * N + n], b = red[1 * N + n], c = red[2 * N + n], d = red[3 * N + n];
+    float x;
+    if (ops[n] == OP_SUM) x = (a + b) + (c + d);
+    else if (ops[n] == OP_MAX) x = fmaxf(fmaxf(a, b), fmaxf(c, d));
+    else x = op2<OP_MINI>(op2<OP_MINI>(a, b), op2<OP_MINI>(c, d));
+    v[n] = x;
+  }
+  __syncthreads();
+}
+
+// Exclusive prefix sum over the workgroup in thread order; *total gets the
+// sum of all values.  Deterministic (fixed shuffle tree).  `red` holds kWaves floats.
+__device__ __forceinline__ float wg_scan_excl(float x, float* red, float* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float v = x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float t = __shfl_up(v, off, 64);
+    if (lane >= off) v += t;
+  }
+  float ex = __shfl_up(v, 1, 64);
+  if (lane == 0) ex = 0.f;
+  if (lane == 63) red[wave] = v;
+  __syncthreads();
+  float wb = 0.f;
+  for (int w = 0; w < wave; ++w) wb += red[w];
+  *total = (red[0] + red[1]) + (red[2] + red[3]);
+  __syncthreads();
+  return wb + ex;
+}
+
+// Arrive at a counter and wait until it reaches `target`.  Thread 0 publishes
+// (release, agent scope) and polls; the rest of the workgroup waits at the
+// barrier.  Returns false if the wait hit its bound.
+__device__ bool arrive_and_wait(int32_t* cnt, int target, int32_t* status, int* sh) {
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int ok = 1, spins = 0;
+    while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      __builtin_amdgcn_s_sleep(4);
+      ++spins;
+      // Give up at the bound, or at once when another wait has already given up.
+      if (spins > kSpinLimit ||
+          ((spins & 63) == 0 && status &&
+           (__hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & ADAFLASH_FLAG_SYNC_TIMEOUT))) {
+        ok = 0;
+        break;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (!ok && status) __hip_atomic_fetch_or(status, ADAFLASH_FLAG_SYNC_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *sh = ok;
+  }
+  __syncthreads();
+  int ok = *sh;
+  __syncthreads();
+  return ok != 0;
+}
+
+__device__ __forceinline__ void flag(int32_t* status, int bits) {
+  if (status) __hip_atomic_fetch_or(status, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ------------------------------------------------------------ chunk storage
+
+// 16 consecutive-slot entries of one row held by one thread.  Entry e sits at
+// vocabulary index v0 + (e / VEC) * kThreads * VEC + tid * VEC + e % VEC, so
+// each slot is one coalesced 16-byte load across the workgroup.  Entries past
+// V read as -inf.
+template <bool BF16>
+struct Chunk {
+  static constexpr int VEC = BF16 ? 8 : 4;
+  static constexpr int NW = BF16 ? kElems / 2 : kElems;
+  uint32_t w[NW];
+
+  __device__ __forceinline__ float get(int e) const {
+    if constexpr (BF16) {
+      uint32_t x = w[e >> 1];
+      return __uint_as_float((e & 1) ? (x & 0xffff0000u) : (x << 16));
+    } else {
+      return __uint_as_float(w[e]);
+    }
+  }
+};
+
+template <bool BF16>
+__device__ __forceinline__ int entry_index(int v0, int e) {
+  constexpr int VEC = Chunk<BF16>::VEC;
+  return v0 + (e / VEC) * (kThreads * VEC) + (int)threadIdx.x * VEC + (e % VEC);
+}
+
+template <bool BF16, bool ALIGNED>
+__device__ __forceinline__ void load_chunk(Chunk<BF16>& c, const void* row, int v0, int V) {
+  constexpr int VEC = Chunk<BF16>::VEC;
+  constexpr int NV = kElems / VEC;
+  const uint32_t ninf = BF16 ? 0xff80ff80u : 0xff800000u;
+#pragma unroll
+  for (int s = 0; s < NV; ++s) {
+    const int idx0 = v0 + s * (kThreads * VEC) + (int)threadIdx.x * VEC;
+    if constexpr (ALIGNED) {
+      if (idx0 < V) {
+        const uint4 q = BF16 ? *(const uint4*)((const uint16_t*)row + idx0)
+                             : *(const uint4*)((const float*)row + idx0);
+        c.w[s * 4 + 0] = q.x;
+        c.w[s * 4 + 1] = q.y;
+        c.w[s * 4 + 2] = q.z;
+        c.w[s * 4 + 3] = q.w;
+      } else {
+        c.w[s * 4 + 0] = ninf;
+        c.w[s * 4 + 1] = ninf;
+        c.w[s * 4 + 2] = ninf;
+        c.w[s * 4 + 3] = ninf;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < VEC; ++u) {
+        const int idx = idx0 + u;
+        if constexpr (BF16) {
+          uint32_t h = idx < V ? (uint32_t)((const uint16_t*)row)[idx] : 0xff80u;
+          const int wi = s * 4 + (u >> 1);
+          if (u & 1) c.w[wi] |= h << 16;
+          else c.w[wi] = h;
+        } else {
+          c.w[s * VEC + u] = idx < V ? __float_as_uint(((const float*)row)[idx]) : ninf;
+        }
+      }
+    }
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ float load_logit(const void* row, int v) {
+  if constexpr (BF16) return __uint_as_float((uint32_t)((const uint16_t*)row)[v] << 16);
+  else return ((const float*)row)[v];
+}
+
+// Two rounded values packed for a bf16 store (round to nearest even).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const __bf16 a = (__bf16)lo, b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// ------------------------------------------------------------ row statistics
+
+struct RowStats {
+  float Mp, Mq;      // row maxima of z_p, z_q
+  float SpT, SqT;    // sum exp2((z - M) kT)
+  float Sp1, Sq1;    // sum exp2((z - M) log2 e)
+  int xstar;         // lowest index of the maximum of z_p
+};
+
+// Combines the G chunk records of row r in a fixed order (identical in every
+// workgroup that calls it).
+template <bool NEED_T, bool NEED_1>
+__device__ RowStats combine_part1(const KParams& P, int r, float kT, float* red) {
+  // Thread t holds the record of chunk t (G <= kThreads).
+  float4 a = make_float4(neg_inf(), __int_as_float(kIntMax), 0.f, 0.f);
+  float4 c = make_float4(neg_inf(), 0.f, 0.f, 0.f);
+  if ((int)threadIdx.x < P.G) {
+    a = P.part1[((size_t)r * P.G + threadIdx.x) * 2 + 0];
+    c = P.part1[((size_t)r * P.G + threadIdx.x) * 2 + 1];
+  }
+  float m[2] = {a.x, c.x};
+  const int mops[2] = {OP_MAX, OP_MAX};
+  wg_reduce<2>(m, mops, red);
+  const float mp = m[0], mq = m[1];
+  float spT = 0.f, sqT = 0.f, sp1 = 0.f, sq1 = 0.f;
+  if (a.x != neg_inf()) {
+    if constexpr (NEED_T) spT = a.z * fexp2((a.x - mp) * kT);
+    if constexpr (NEED_1) sp1 = a.w * fexp2((a.x - mp) * kLog2e);
+  }
+  if (c.x != neg_inf()) {
+    if constexpr (NEED_T) sqT = c.y * fexp2((c.x - mq) * kT);
+    if constexpr (NEED_1) sq1 = c.z * fexp2((c.x - mq) * kLog2e);
+  }
+  const int xi = (a.x == mp) ? __float_as_int(a.y) : kIntMax;
+  float v[5] = {spT, sqT, sp1, sq1, __int_as_float(xi)};
+  const int ops[5] = {OP_SUM, OP_SUM, OP_SUM, OP_SUM, OP_MINI};
+  wg_reduce<5>(v, ops, red);
+  RowStats s;
+  s.Mp = mp;
+  s.Mq = mq;
+  s.SpT = v[0];
+  s.SqT = v[1];
+  s.Sp1 = v[2];
+  s.Sq1 = v[3];
+  s.xstar = __float_as_int(v[4]);
+  return s;
+}
+
+// ----------------------------------------------------------------- finaliser
+
+struct FinShared {
+  float red[kWaves * 8];
+  float f[8];
+  int i[8];
+};
+
+// Chunk-level inverse CDF: thread t < G holds the mass of chunk t.  Returns the
+// chunk whose cumulative mass first exceeds u * total (else the last chunk with
+// positive mass, else 0) and the cumulative mass before it.
+__device__ void locate_chunk(float mj, int G, float us, FinShared& fs, int* jc_out, float* before_out,
+                             float* thr_out, float* tot_out) {
+  const int tid = threadIdx.x;
+  float tot;
+  const float ex = wg_scan_excl(mj, fs.red, &tot);
+  const float thr = us * tot;
+  const int cross = (tid < G && ex + mj > thr) ? tid : kIntMax;
+  const int lastpos = (tid < G && mj > 0.f) ? -tid : kIntMax;
+  float v[2] = {__int_as_float(cross), __int_as_float(lastpos)};
+  const int ops[2] = {OP_MINI, OP_MINI};
+  wg_reduce<2>(v, ops, fs.red);
+  int jc = __float_as_int(v[0]);
+  if (jc == kIntMax) {
+    const int lp = __float_as_int(v[1]);
+    jc = lp == kIntMax ? 0 : -lp;
+  }
+  if (tid == jc) fs.f[0] = ex;
+  __syncthreads();
+  *before_out = fs.f[0];
+  *jc_out = jc;
+  *thr_out = thr;
+  *tot_out = tot;
+  __syncthreads();
+}
+
+// Draws the correction or bonus token for request b.  Runs on one workgroup.
+template <bool BF16, bool ALIGNED, int VMODE>
+__device__ void finalize_request(const KParams& P, int b, FinShared& fs) {
+  const int k = P.k, V = P.V, G = P.G;
+  const int tid = threadIdx.x;
+  const int L = P.Lc[b];
+  const int r0 = P.roff[b];
+  int A = L, token = 0;
+  float sample_margin = __int_as_float(0x7fc00000);
+
+  if constexpr (VMODE == 1) {
+    // Greedy: row argmax from the chunk records; stop at the first mismatch.
+    for (int i = 0; i <= L; ++i) {
+      const int r = r0 + i;
+      float4 a = make_float4(neg_inf(), __int_as_float(kIntMax), 0.f, 0.f);
+      if (tid < G) a = P.part1[((size_t)r * G + tid) * 2];
+      float v1[1] = {a.x};
+      const int o1[1] = {OP_MAX};
+      wg_reduce<1>(v1, o1, fs.red);
+      float v2[1] = {__int_as_float(a.x == v1[0] ? __float_as_int(a.y) : kIntMax)};
+      const int o2[1] = {OP_MINI};
+      wg_reduce<1>(v2, o2, fs.red);
+      int am = __float_as_int(v2[0]);
+      if (am == kIntMax) {  // NaN row: no chunk holds the maximum
+        am = 0;
+        if (tid == 0) flag(P.status, ADAFLASH_FLAG_NONFINITE);
+      }
+      if (i < L) {
+        int x = P.tokens[(size_t)b * k + i];
+        x = x < 0 ? 0 : (x >= V ? V - 1 : x);
+        if (x != am) {
+          A = i;
+          token = am;
+          break;
+        }
+      } else {
+        token = am;
+      }
+    }
+  } else {
+    // Sampled: first rejected row from the per-row accept flags.
+    int first = kIntMax;
+    for (int i = tid; i < L; i += kThreads)
+      if (P.rowrec[r0 + i].y == 0) first = min(first, i);
+    float v1[1] = {__int_as_float(first)};
+    const int o1[1] = {OP_MINI};
+    wg_reduce<1>(v1, o1, fs.red);
+    first = __float_as_int(v1[0]);
+    A = first < L ? first : L;
+
+    const int rs = r0 + A;  // row the draw reads: rejected row or bonus row L
+    const RowStats st = combine_part1<true, false>(P, rs, P.kT, fs.red);
+    const float us = P.uniforms[(size_t)b * (k + 1) + k];
+    const void* trow = BF16 ? (const void*)((const uint16_t*)P.target + ((size_t)b * (k + 1) + A) * V)
+                            : (const void*)((const float*)P.target + ((size_t)b * (k + 1) + A) * V);
+    const void* drow = nullptr;
+    const float invSp = 1.f / st.SpT, invSq = 1.f / st.SqT;
+    bool resid = false;
+    int jc = 0;
+    float base = 0.f, thr = 0.f, tot = 1.f;
+    if (A < L) {
+      drow = BF16 ? (const void*)((const uint16_t*)P.draft + ((size_t)b * k + A) * V)
+                  : (const void*)((const float*)P.draft + ((size_t)b * k + A) * V);
+      const float mj = tid < G ? P.part2[(size_t)rs * G + tid].z : 0.f;
+      locate_chunk(mj, G, us, fs, &jc, &base, &thr, &tot);
+      resid = tot > 0.f;
+    }
+    if (!resid) {
+      // Draw from p of row rs (bonus row, or the rejected row when Z == 0).
+      float mj = 0.f;
+      if (tid < G) {
+        const float4 a = P.part1[((size_t)rs * G + tid) * 2];
+        mj = a.x == neg_inf() ? 0.f : a.z * fexp2((a.x - st.Mp) * P.kT) * invSp;
+      }
+      locate_chunk(mj, G, us, fs, &jc, &base, &thr, &tot);
+    }
+
+    // Scan chunk jc in index order.
+    const int v0 = jc * kChunk;
+    Chunk<BF16> cp, cq;
+    load_chunk<BF16, ALIGNED>(cp, trow, v0, V);
+    if (resid) load_chunk<BF16, ALIGNED>(cq, drow, v0, V);
+    const float ap = -st.Mp * P.kT, aq = -st.Mq * P.kT;
+    constexpr int VEC = Chunk<BF16>::VEC;
+    constexpr int NV = kElems / VEC;
+    float carry = base;
+    int found = kIntMax, last_pos = -1;
+    float found_before = 0.f, found_at = 0.f, last_before = 0.f, last_at = 0.f;
+#pragma unroll
+    for (int s = 0; s < NV; ++s) {
+      float w[VEC];
+      float tsum = 0.f;
+#pragma unroll
+      for (int u = 0; u < VEC; ++u) {
+        const int e = s * VEC + u;
+        const float zp = cp.get(e);
+        float m;
+        if (resid) {
+          const float pv = fexp2(fmaf(zp, P.kT, ap)) * invSp;
+          const float qv = fexp2(fmaf(cq.get(e), P.kT, aq)) * invSq;
+          m = fmaxf(0.f, pv - qv);
+        } else {
+          m = zp == neg_inf() ? 0.f : fexp2(fmaf(zp, P.kT, ap)) * invSp;
+        }
+        w[u] = m;
+        tsum += m;
+      }
+      float slot_total;
+      const float excl = wg_scan_excl(tsum, fs.red, &slot_total);
+      float cum = carry + excl;
+#pragma unroll
+      for (int u = 0; u < VEC; ++u) {
+        const float before = cum;
+        cum += w[u];
+        const int idx = entry_index<BF16>(v0, s * VEC + u);
+        if (w[u] > 0.f && idx < V) {
+          last_pos = idx;
+          last_before = before;
+          last_at = cum;
+        }
+        if (found == kIntMax && cum > thr && idx < V) {
+          found = idx;
+          found_before = before;
+          found_at = cum;
+        }
+      }
+      // Stop at the first slot where any thread crossed (uniform decision).
+      float v[1] = {__int_as_float(found)};
+      const int o[1] = {OP_MINI};
+      wg_reduce<1>(v, o, fs.red);
+      const int slot_found = __float_as_int(v[0]);
+      carry += slot_total;
+      if (slot_found != kIntMax) {
+        if (found != slot_found) found = kIntMax;  // keep only the lowest index
+        break;
+      }
+    }
+    // Winner: the lowest crossing index, else the last positive-mass entry.
+    float v2[2] = {__int_as_float(found), __int_as_float(last_pos < 0 ? kIntMax : -last_pos)};
+    const int o2[2] = {OP_MINI, OP_MINI};
+    wg_reduce<2>(v2, o2, fs.red);
+    const int fmin = __float_as_int(v2[0]);
+    const int lmax = __float_as_int(v2[1]) == kIntMax ? -1 : -__float_as_int(v2[1]);
+    if (tid == 0) {
+      fs.f[5] = base;
+      fs.f[6] = base;
+    }
+    __syncthreads();
+    if (fmin != kIntMax) {
+      token = fmin;
+      if (found == fmin) {
+        fs.f[5] = found_before;
+        fs.f[6] = found_at;
+      }
+    } else {
+      token = lmax >= 0 ? lmax : v0;
+      if (lmax >= 0 && last_pos == lmax) {
+        fs.f[5] = last_before;
+        fs.f[6] = last_at;
+      }
+    }
+    __syncthreads();
+    const float cb = fs.f[5], ca = fs.f[6];
+    sample_margin = fminf(thr - cb, ca - thr) / tot;
+    __syncthreads();
+  }
+
+  // Outputs.
+  for (int i = tid; i <= k; i += kThreads) {
+    int32_t t = -1;
+    if (i < A) {
+      int x = P.tokens[(size_t)b * k + i];
+      t = x < 0 ? 0 : (x >= V ? V - 1 : x);
+    } else if (i == A) {
+      t = token;
+    }
+    P.out_tokens[(size_t)b * (k + 1) + i] = t;
+    if (P.margins) {
+      if (i == k) P.margins[(size_t)b * (k + 1) + k] = sample_margin;
+      else if (VMODE == 1 || i >= L) P.margins[(size_t)b * (k + 1) + i] = __int_as_float(0x7fc00000);
+    }
+  }
+  if (tid == 0) P.accept_len[b] = A;
+}
+
+// ---------------------------------------------------------------- row kernel
+
+template <bool BF16, bool ALIGNED, bool OPD, int VMODE, bool T1>
+__global__ __launch_bounds__(kThreads) void row_kernel(KParams P) {
+  constexpr bool SAMPLED = VMODE == 2, GREEDY = VMODE == 1, VERIFY = VMODE != 0;
+  constexpr int VEC = Chunk<BF16>::VEC;
+  __shared__ FinShared fs;
+  __shared__ int sh_ok;
+
+  const int tid = threadIdx.x;
+  const int G = P.G;
+  const int r = (int)blockIdx.x / G;
+  const int j = (int)blockIdx.x - r * G;
+  if (r >= *P.nrows) return;
+  const int k = P.k, V = P.V;
+  const int rid = P.rowlist[r];
+  const int b = rid / (k + 1), i = rid - b * (k + 1);
+  const int L = P.Lc[b];
+  const bool draft_row = i < L;
+  const bool need_q = draft_row && (OPD || SAMPLED);
+  const int v0 = j * kChunk;
+
+  const void* trow = BF16 ? (const void*)((const uint16_t*)P.target + (size_t)rid * V)
+                          : (const void*)((const float*)P.target + (size_t)rid * V);
+  const void* drow = nullptr;
+  if (need_q)
+    drow = BF16 ? (const void*)((const uint16_t*)P.draft + ((size_t)b * k + i) * V)
+                : (const void*)((const float*)P.draft + ((size_t)b * k + i) * V);
+
+  // ---- phase 1: load the chunk, chunk maxima, argmax, sums of exponentials.
+  Chunk<BF16> cp, cq;
+  load_chunk<BF16, ALIGNED>(cp, trow, v0, V);
+  if (need_q) load_chunk<BF16, ALIGNED>(cq, drow, v0, V);
+
+  float mp = neg_inf(), mq = neg_inf();
+#pragma unroll
+  for (int e = 0; e < kElems; ++e) mp = fmaxf(mp, cp.get(e));
+  if (need_q) {
+#pragma unroll
+    for (int e = 0; e < kElems; ++e) mq = fmaxf(mq, cq.get(e));
+  }
+  {
+    float v[2] = {mp, mq};
+    const int ops[2] = {OP_MAX, OP_MAX};
+    const float mp_t = mp;
+    wg_reduce<2>(v, ops, fs.red);
+    // Lowest index holding the chunk maximum of z_p (only lanes that hold it search).
+    int cand = kIntMax;
+    if (mp_t == v[0]) {
+#pragma unroll
+      for (int e = kElems - 1; e >= 0; --e)
+        if (cp.get(e) == v[0]) cand = entry_index<BF16>(v0, e);
+    }
+    mp = v[0];
+    mq = v[1];
+    float spT = 0.f, sqT = 0.f, sp1 = 0.f, sq1 = 0.f;
+    const float Mp = mp, Mq = mq;
+    if constexpr (SAMPLED) {
+      const float ap = Mp == neg_inf() ? 0.f : -Mp * P.kT;
+#pragma unroll
+      for (int e = 0; e < kElems; ++e) spT += fexp2(fmaf(cp.get(e), P.kT, ap));
+      if (need_q) {
+        const float aq = Mq == neg_inf() ? 0.f : -Mq * P.kT;
+#pragma unroll
+        for (int e = 0; e < kElems; ++e) sqT += fexp2(fmaf(cq.get(e), P.kT, aq));
+      }
+    }
+    if constexpr (OPD) {
+      if (draft_row) {
+        if constexpr (SAMPLED && T1) {
+          sp1 = spT;
+          sq1 = sqT;
+        } else {
+          const float ap = Mp == neg_inf() ? 0.f : -Mp * kLog2e;
+          const float aq = Mq == neg_inf() ? 0.f : -Mq * kLog2e;
+#pragma unroll
+          for (int e = 0; e < kElems; ++e) {
+            sp1 += fexp2(fmaf(cp.get(e), kLog2e, ap));
+            sq1 += fexp2(fmaf(cq.get(e), kLog2e, aq));
+          }
+        }
+      }
+    }
+    float s[5] = {spT, sqT, sp1, sq1, __int_as_float(cand)};
+    const int sops[5] = {OP_SUM, OP_SUM, OP_SUM, OP_SUM, OP_MINI};
+    wg_reduce<5>(s, sops, fs.red);
+    if (tid == 0) {
+      P.part1[((size_t)r * G + j) * 2 + 0] = make_float4(Mp, s[4], s[0], s[2]);
+      P.part1[((size_t)r * G + j) * 2 + 1] = make_float4(Mq, s[1], s[3], 0.f);
+    }
+  }
+
+  const bool do_rows = draft_row && (SAMPLED || OPD);
+  bool alive = true;
+  if (do_rows) {
+    // ---- barrier 1: all chunks of this row have published their statistics.
+    alive = arrive_and_wait(&P.rowcnt[r], G, P.status, &sh_ok);
+    if (alive) {
+      const RowStats st = combine_part1<SAMPLED, OPD && !(SAMPLED && T1)>(P, r, P.kT, fs.red);
+      float Sp1 = st.Sp1, Sq1 = st.Sq1;
+      if constexpr (SAMPLED && T1) {
+        Sp1 = st.SpT;
+        Sq1 = st.SqT;
+      }
+      if (tid == 0) {
+        const bool bad = !(st.Mp < __builtin_inff()) || !(st.SpT > 0.f || !SAMPLED);
+        if (bad) flag(P.status, ADAFLASH_FLAG_NONFINITE);
+      }
+      // Accept test for this row (sampled mode).
+      bool accept = true;
+      if constexpr (SAMPLED) {
+        int x = P.tokens[(size_t)b * k + i];
+        if (x < 0 || x >= V) {
+          if (tid == 0 && j == 0) flag(P.status, ADAFLASH_FLAG_BAD_TOKEN);
+          x = x < 0 ? 0 : V - 1;
+        }
+        const float zpx = load_logit<BF16>(trow, x), zqx = load_logit<BF16>(drow, x);
+        const float px = fexp2((zpx - st.Mp) * P.kT) / st.SpT;
+        const float qx = fexp2((zqx - st.Mq) * P.kT) / st.SqT;
+        const float u = P.uniforms[(size_t)b * (k + 1) + i];
+        accept = u * qx < px;
+        if (tid == 0 && j == 0) {
+          P.rowrec[r] = make_int4(0, accept ? 1 : 0, __float_as_int(px - u * qx), 0);
+          if (P.margins) P.margins[(size_t)b * (k + 1) + i] = px - u * qx;
+        }
+      }
+
+      // ---- phase 2: supervision sums and/or the residual mass of this chunk.
+      float Spart = 0.f, Rpart = 0.f, Zpart = 0.f;
+      float gc[kElems];
+      float qv[kElems];
+      const float lse_q2 = st.Mq * kLog2e + flog2(Sq1);  // log2-domain normalisers
+      const float lse_p2 = st.Mp * kLog2e + flog2(Sp1);
+      const float D = (lse_q2 - lse_p2) * kLn2;          // lse_q - lse_p
+      if constexpr (OPD) {
+        const float c = P.clip_c, lam = P.lambda;
+        const float nq = -lse_q2;
+#pragma unroll
+        for (int e = 0; e < kElems; ++e) {
+          const float zq = cq.get(e), zp = cp.get(e);
+          const float q = fexp2(fmaf(zq, kLog2e, nq));
+          const float d = (zq - zp) - D;
+          const float f = q > 0.f ? q * d : 0.f;
+          const bool inU = f <= c;
+          Rpart += inU ? f : c;
+          const float sterm = inU ? f + q : 0.f;
+          Spart += sterm;
+          gc[e] = fmaf(lam, sterm, q);
+          qv[e] = q;
+        }
+      }
+      if constexpr (SAMPLED) {
+        if (!accept) {
+          const float invSp = 1.f / st.SpT, invSq = 1.f / st.SqT;
+          const float ap = -st.Mp * P.kT, aq = -st.Mq * P.kT;
+#pragma unroll
+          for (int e = 0; e < kElems; ++e) {
+            const float pv = fexp2(fmaf(cp.get(e), P.kT, ap)) * invSp;
+            const float qq = fexp2(fmaf(cq.get(e), P.kT, aq)) * invSq;
+            Zpart += fmaxf(0.f, pv - qq);
+          }
+        }
+      }
+      {
+        float s[3] = {Spart, Rpart, Zpart};
+        const int ops[3] = {OP_SUM, OP_SUM, OP_SUM};
+        wg_reduce<3>(s, ops, fs.red);
+        if (tid == 0) P.part2[(size_t)r * G + j] = make_float4(s[0], s[1], s[2], 0.f);
+      }
+
+      if constexpr (OPD) {
+        // ---- barrier 2: supervision sums of every chunk are published.
+        alive = arrive_and_wait(&P.rowcnt[r], 2 * G, P.status, &sh_ok);
+        if (alive) {
+          float sr[2] = {0.f, 0.f};
+          if (tid < G) {
+            const float4 a = P.part2[(size_t)r * G + tid];
+            sr[0] = a.x;
+            sr[1] = a.y;
+          }
+          const int srops[2] = {OP_SUM, OP_SUM};
+          wg_reduce<2>(sr, srops, fs.red);
+          const float S = sr[0], R = sr[1];
+          const int n = P.row_offsets[b] + i;  // packed row
+          const float lamS = P.lambda * S;
+          // x* correction: only the thread holding x* takes this branch.
+          const int xs = st.xstar;
+          const int xo = xs - v0;
+          const bool xs_here = xo >= 0 && xo < kChunk && ((xo % (kThreads * VEC)) / VEC) == tid;
+          if (xs_here) {
+            const int es = (xo / (kThreads * VEC)) * VEC + (xo % VEC);
+#pragma unroll
+            for (int e = 0; e < kElems; ++e)
+              if (e == es) gc[e] -= 1.f;
+          }
+          if (P.grad) {
+            constexpr int NV = kElems / VEC;
+#pragma unroll
+            for (int s2 = 0; s2 < NV; ++s2) {
+              const int idx0 = v0 + s2 * (kThreads * VEC) + tid * VEC;
+              float g[VEC];
+#pragma unroll
+              for (int u = 0; u < VEC; ++u) g[u] = fmaf(-lamS, qv[s2 * VEC + u], gc[s2 * VEC + u]);
+              if constexpr (BF16) {
+                uint16_t* gr = (uint16_t*)P.grad + (size_t)n * V;
+                if constexpr (ALIGNED) {
+                  if (idx0 < V) {
+                    uint4 o;
+                    o.x = pack_bf16x2(g[0], g[1]);
+                    o.y = pack_bf16x2(g[2], g[3]);
+                    o.z = pack_bf16x2(g[4], g[5]);
+                    o.w = pack_bf16x2(g[6], g[7]);
+                    *(uint4*)(gr + idx0) = o;
+                  }
+                } else {
+#pragma unroll
+                  for (int u = 0; u < VEC; ++u)
+                    if (idx0 + u < V) gr[idx0 + u] = __builtin_bit_cast(uint16_t, (__bf16)g[u]);
+                }
+              } else {
+                float* gr = (float*)P.grad + (size_t)n * V;
+                if constexpr (ALIGNED) {
+                  if (idx0 < V) *(float4*)(gr + idx0) = make_float4(g[0], g[1], g[2], g[3]);
+                } else {
+#pragma unroll
+                  for (int u = 0; u < VEC; ++u)
+                    if (idx0 + u < V) gr[idx0 + u] = g[u];
+                }
+              }
+            }
+          }
+          // Losses: written by the chunk that holds x*.
+          if (tid == 0 && xs >= v0 && xs < v0 + kChunk) {
+            const float zqx = load_logit<BF16>(drow, xs);
+            if (P.loss_ce) P.loss_ce[n] = (lse_q2 * kLn2) - zqx;
+            if (P.loss_rkl) P.loss_rkl[n] = R;
+          }
+        }
+      }
+    }
+  }
+
+  if constexpr (VERIFY) {
+    // ---- request arrival: the last workgroup of the request finalises it.
+    if (tid == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      const int total = G * (L + 1);
+      const int old = __hip_atomic_fetch_add(&P.reqcnt[b], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int last = (old == total - 1) ? 1 : 0;
+      if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      sh_ok = last;
+    }
+    __syncthreads();
+    const int last = sh_ok;
+    __syncthreads();
+    if (last) finalize_request<BF16, ALIGNED, VMODE>(P, b, fs);
+  }
+  (void)alive;
+  (void)GREEDY;
+}
+
+// --------------------------------------------------------------- pack kernel
+
+// One workgroup of 1024 threads: clamp verify lengths, prefix sums, row list,
+// counter reset, status initialisation.
+__global__ __launch_bounds__(1024) void pack_kernel(const int32_t* verify_len, int B, int k, int bonus,
+                                                     int32_t* row_offsets, Workspace ws, int32_t* status) {
+  __shared__ int s_scan[1024];
+  __shared__ int s_scan2[1024];
+  __shared__ int s_flags;
+  const int tid = threadIdx.x;
+  if (tid == 0) s_flags = 0;
+  __syncthreads();
+  int carry = 0, carry2 = 0;
+  for (int base = 0; base < B; base += 1024) {
+    const int b = base + tid;
+    int L = 0;
+    if (b < B) {
+      L = verify_len ? verify_len[b] : k;
+      if (L < 1 || L > k) {
+        atomicOr(&s_flags, ADAFLASH_FLAG_BAD_VERIFY_LEN);
+        L = L < 1 ? 1 : k;
+      }
+      ws.Lc[b] = L;
+    }
+    const int n2 = b < B ? L + bonus : 0;
+    s_scan[tid] = L;
+    s_scan2[tid] = n2;
+    __syncthreads();
+    // Hillis-Steele inclusive scan.
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int a = tid >= off ? s_scan[tid - off] : 0;
+      const int a2 = tid >= off ? s_scan2[tid - off] : 0;
+      __syncthreads();
+      s_scan[tid] += a;
+      s_scan2[tid] += a2;
+      __syncthreads();
+    }
+    const int incl = s_scan[tid], incl2 = s_scan2[tid];
+    if (b < B) {
+      row_offsets[b] = carry + incl - L;
+      const int start = carry2 + incl2 - n2;
+      ws.roff[b] = start;
+      for (int ii = 0; ii < n2; ++ii) {
+        ws.rowlist[start + ii] = b * (k + 1) + ii;
+        ws.rowcnt[start + ii] = 0;
+      }
+      ws.reqcnt[b] = 0;
+    }
+    carry += s_scan[1023];
+    carry2 += s_scan2[1023];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    row_offsets[B] = carry;
+    ws.roff[B] = carry2;
+    *ws.nrows = carry2;
+    if (status) *status = s_flags;
+  }
+}
+
+template <bool BF16, bool ALIGNED, bool OPD, int VMODE, bool T1>
+hipError_t launch_rows(const KParams& p, int grid, hipStream_t st) {
+  hipLaunchKernelGGL((row_kernel<BF16, ALIGNED, OPD, VMODE, T1>), dim3(grid), dim3(kThreads), 0, st, p);
+  return hipGetLastError();
+}
+
+template <bool BF16, bool ALIGNED>
+hipError_t dispatch_mode(const KParams& p, int grid, int opd, int vmode, bool t1, hipStream_t st) {
+  if (!opd) {
+    if (vmode == 1) return launch_rows<BF16, ALIGNED, false, 1, false>(p, grid, st);
+    if (vmode == 2) return launch_rows<BF16, ALIGNED, false, 2, false>(p, grid, st);
+    return hipErrorInvalidValue;
+  }
+  if (vmode == 0) return launch_rows<BF16, ALIGNED, true, 0, false>(p, grid, st);
+  if (vmode == 1) return launch_rows<BF16, ALIGNED, true, 1, false>(p, grid, st);
+  if (t1) return launch_rows<BF16, ALIGNED, true, 2, true>(p, grid, st);
+  return launch_rows<BF16, ALIGNED, true, 2, false>(p, grid, st);
+}
+
+}  // namespace
+
+hipError_t launch(const LaunchArgs& a) {
+  const int bonus = a.verify ? 1 : 0;
+  hipLaunchKernelGGL(pack_kernel, dim3(1), dim3(1024), 0, a.stream, a.verify_len, a.B, a.k, bonus,
+                     a.row_offsets, a.ws, a.status);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.B == 0) return e;
+
+  KParams p;
+  p.target = a.target;
+  p.draft = a.draft;
+  p.tokens = a.tokens;
+  p.uniforms = a.uniforms;
+  p.accept_len = a.accept_len;
+  p.out_tokens = a.out_tokens;
+  p.margins = a.margins;
+  p.row_offsets = a.row_offsets;
+  p.loss_ce = a.loss_ce;
+  p.loss_rkl = a.loss_rkl;
+  p.grad = a.grad;
+  p.status = a.status;
+  p.nrows = a.ws.nrows;
+  p.Lc = a.ws.Lc;
+  p.roff = a.ws.roff;
+  p.rowlist = a.ws.rowlist;
+  p.rowcnt = a.ws.rowcnt;
+  p.reqcnt = a.ws.reqcnt;
+  p.part1 = a.ws.part1;
+  p.part2 = a.ws.part2;
+  p.rowrec = a.ws.rowrec;
+  p.B = a.B;
+  p.k = a.k;
+  p.V = a.V;
+  p.G = num_chunks(a.V);
+  p.kT = a.T > 0.f ? kLog2e / a.T : 0.f;
+  p.clip_c = a.clip_c;
+  p.lambda = a.lambda;
+
+  const int vmode = a.verify ? (a.T > 0.f ? 2 : 1) : 0;
+  const int rows_max = a.B * (a.k + bonus);
+  const long long grid = (long long)rows_max * p.G;
+  if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const int vec = a.bf16 ? 8 : 4;
+  const bool aligned = (a.V % vec == 0) && (((uintptr_t)a.target & 15) == 0) &&
+                       (a.draft == nullptr || ((uintptr_t)a.draft & 15) == 0) &&
+                       (a.grad == nullptr || ((uintptr_t)a.grad & 15) == 0);
+  const bool t1 = a.T == 1.0f;
+  if (a.bf16) {
+    if (aligned) return dispatch_mode<true, true>(p, (int)grid, a.opd, vmode, t1, a.stream);
+    return dispatch_mode<true, false>(p, (int)grid, a.opd, vmode, t1, a.stream);
+  }
+  if (aligned) return dispatch_mode<false, true>(p, (int)grid, a.opd, vmode, t1, a.stream);
+  return dispatch_mode<false, false>(p, (int)grid, a.opd, vmode, t1, a.stream);
+}
+
+}  // namespace adaflash

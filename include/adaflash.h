@@ -1,0 +1,166 @@
+/*
+ * adaflash.h -- C ABI of the MI355X (gfx950) verify-and-supervise library.
+ *
+ * One speculative-decoding round hands the verifier, per request b, the
+ * target model's logits for the verified positions plus one extra row, the
+ * drafter's logits and its sampled draft tokens, and the verify length the
+ * adaptive length head predicted.  The library
+ *   1. accepts draft x_i when u_i * q_i(x_i) < p_i(x_i) (acceptance
+ *      probability min(1, p/q): AdaFlash review, "Speculative Decoding: The
+ *      Basic Idea", step 3; DFlash reading notes, section 5.2, eq. 6), or, in
+ *      greedy mode (T == 0), when x_i is the target argmax (DFlash reading
+ *      notes, section 5.1);
+ *   2. stops at the first rejection inside the request's verify length
+ *      (AdaFlash review, step 4; adaptive length head, "Method Part 2");
+ *   3. draws the correction token from norm(max(0, p - q)) at the rejected
+ *      position, or a bonus token from the target row after the last verified
+ *      position when every draft is accepted (DFlash reading notes, section
+ *      5.2, eqs. 7-8, and Algorithm 1 step 9);
+ *   4. optionally, in the same read of the logits, computes the on-policy
+ *      distillation supervision of every verified row at temperature 1: the
+ *      hard-label cross entropy on the target's top-1 token plus lambda times
+ *      the entry-wise clipped reverse KL(q || p) (AdaFlash review, "The
+ *      Reverse-KL + Hard-Label Mixture Loss, Derived" and "Entry-Wise
+ *      Divergence Clipping, Derived", Algorithm 2), and its gradient with
+ *      respect to the draft logits.
+ *
+ * Conventions shared by every entry point
+ *  - All array arguments are DEVICE pointers owned by the caller; the library
+ *    allocates nothing and keeps no state between calls.  Calls are enqueued
+ *    on `stream` (a hipStream_t; NULL = the null stream) and return without
+ *    synchronising.  Concurrent calls must use distinct workspaces.
+ *  - Logits are row-major, contiguous; `dtype` selects fp32 or bf16 (raw
+ *    16-bit patterns).  The fast path needs V to be a multiple of 8 (bf16) or
+ *    4 (fp32) and 16-byte aligned base pointers; other shapes take a slower
+ *    element-wise path.
+ *  - Host-detectable argument errors return a negative status before anything
+ *    is enqueued; nothing is written.  adaflash_last_error() then describes
+ *    the error (thread-local string).
+ *  - Data errors only the device can see are repaired and reported in
+ *    *status_flags (see ADAFLASH_FLAG_*): verify lengths outside [1, k] are
+ *    clamped, draft tokens outside [0, V) are clamped, non-finite row
+ *    statistics are flagged.  Read the flags after synchronising the stream.
+ *  - Sizes: 1 <= k <= 64, 1 <= V <= 2^20, 0 <= B and B * (k + 1) < 2^24.
+ *    B == 0 is a valid empty call (row_offsets[0] is set to 0).
+ *  - Logit value -inf means probability 0.  +inf and NaN logits are caller
+ *    errors (flagged when they reach a row statistic; outputs undefined).
+ */
+#ifndef ADAFLASH_H
+#define ADAFLASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define ADAFLASH_API __attribute__((visibility("default")))
+#else
+#define ADAFLASH_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ADAFLASH_OK = 0,
+  ADAFLASH_E_INVALID = -1,     /* bad argument (NULL pointer, size, T, c, lambda) */
+  ADAFLASH_E_WORKSPACE = -2,   /* workspace NULL or smaller than adaflash_workspace_bytes() */
+  ADAFLASH_E_HIP = -3,         /* a HIP runtime call failed; see adaflash_last_error() */
+  ADAFLASH_E_UNSUPPORTED = -4  /* valid but unsupported configuration */
+} adaflash_status;
+
+typedef enum { ADAFLASH_F32 = 0, ADAFLASH_BF16 = 1 } adaflash_dtype;
+
+/* Bits OR-ed into *status_flags by the device. */
+#define ADAFLASH_FLAG_BAD_VERIFY_LEN 1 /* some verify_len outside [1, k]; clamped */
+#define ADAFLASH_FLAG_BAD_TOKEN 2      /* some draft token outside [0, V); clamped */
+#define ADAFLASH_FLAG_NONFINITE 4      /* a row maximum was +inf/NaN or a row had no mass */
+#define ADAFLASH_FLAG_SYNC_TIMEOUT 8   /* a cross-workgroup wait hit its bound; outputs invalid */
+
+/* Library version, as major*10000 + minor*100 + patch. */
+ADAFLASH_API int adaflash_version(void);
+
+/* Bytes of device workspace either entry point needs for these sizes
+ * (0 on invalid sizes).  The workspace needs no initialisation. */
+ADAFLASH_API size_t adaflash_workspace_bytes(int B, int k, int V);
+
+/* Description of the last error returned on this thread ("" if none). */
+ADAFLASH_API const char* adaflash_last_error(void);
+
+/*
+ * adaflash_verify -- speculative verification of a batch of B requests, with
+ * optional fused supervision of the verified rows.
+ *
+ *   target_logits [B, k+1, V]  z_p.  Row i of request b is the target's
+ *                              distribution for position i given the accepted
+ *                              prefix x_0..x_{i-1}; row L_b is the bonus row.
+ *   draft_logits  [B, k, V]    z_q, the proposal the drafter sampled from.
+ *                              May be NULL only when T == 0 and no supervision
+ *                              output is requested.
+ *   draft_tokens  [B, k]       x_i in [0, V).
+ *   verify_len    [B]          L_b in [1, k]: the verify length from the
+ *                              adaptive length head (AdaFlash review,
+ *                              Algorithm 3, k_hat = clamp(floor(gamma a k), 1, k)).
+ *   uniforms      [B, k+1]     in [0, 1): uniforms[b][i] (i < k) drives accept
+ *                              test i; uniforms[b][k] drives the single
+ *                              correction-or-bonus draw.  Ignored when T == 0.
+ *   T                          verification temperature; 0 = greedy.
+ *   accept_len    [B]    out   A_b: drafts accepted before the first rejection.
+ *   out_tokens    [B, k+1] out x_0..x_{A-1}, then the correction (A < L) or
+ *                              bonus (A == L) token, then -1.
+ *   margins       [B, k+1] out or NULL.  T > 0: margins[b][i] = p_i(x_i) -
+ *                              u_i q_i(x_i) for i < L_b (every test is
+ *                              evaluated); margins[b][k] = distance of the
+ *                              draw's threshold to the nearest boundary of the
+ *                              chosen token's CDF interval, divided by the
+ *                              total mass.  NaN elsewhere and when T == 0.
+ *   clip_c, lambda             supervision: clip threshold c > 0 and weight
+ *                              lambda >= 0 (ignored when every supervision
+ *                              output is NULL).
+ *   row_offsets   [B+1]  out   exclusive prefix sum of the clamped verify
+ *                              lengths: packed row n = row_offsets[b] + i
+ *                              holds request b, position i < L_b.  Required.
+ *   loss_ce       [N]    out or NULL  per-row hard-label cross entropy
+ *                              -log q_i(x*_i), x*_i = argmax z_p (lowest index).
+ *   loss_rkl      [N]    out or NULL  per-row clipped reverse KL
+ *                              sum_v min(q log(q/p), c) at temperature 1.
+ *   grad_draft    [N, V] out or NULL  d(ce + lambda * rkl)/d z_q per row, in the
+ *                              logits' dtype (bf16 rounded to nearest even).
+ *                              N = row_offsets[B]; N <= B*k, so a [B*k, V]
+ *                              buffer always suffices.  Only N rows are written.
+ *   status_flags  [1]    out or NULL  ADAFLASH_FLAG_* bits.
+ *   workspace, workspace_bytes     device scratch, >= adaflash_workspace_bytes.
+ *   stream                     hipStream_t.
+ * Returns ADAFLASH_OK or a negative adaflash_status.
+ */
+ADAFLASH_API int adaflash_verify(adaflash_dtype dtype, const void* target_logits, const void* draft_logits,
+                    const int32_t* draft_tokens, const int32_t* verify_len, const float* uniforms,
+                    int B, int k, int V, float T, int32_t* accept_len, int32_t* out_tokens,
+                    float* margins, float clip_c, float lambda, int32_t* row_offsets,
+                    float* loss_ce, float* loss_rkl, void* grad_draft, int32_t* status_flags,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * adaflash_opd_loss_fwd_bwd -- supervision only (no verification) for the
+ * verified rows of a replay batch (AdaFlash review, Algorithm 1 steps 4-6 and
+ * Algorithm 2, at temperature 1).
+ *
+ *   target_logits [B, k+1, V]  z_p; row k of each request is not read.
+ *   draft_logits  [B, k, V]    z_q.
+ *   verify_len    [B] or NULL  rows i < L_b are supervised (NULL: L_b = k).
+ *   clip_c > 0, lambda >= 0, and the outputs row_offsets (required),
+ *   loss_ce, loss_rkl, grad_draft (each may be NULL), status_flags, workspace
+ *   and stream exactly as in adaflash_verify.
+ */
+ADAFLASH_API int adaflash_opd_loss_fwd_bwd(adaflash_dtype dtype, const void* target_logits,
+                              const void* draft_logits, const int32_t* verify_len, int B, int k,
+                              int V, float clip_c, float lambda, int32_t* row_offsets,
+                              float* loss_ce, float* loss_rkl, void* grad_draft,
+                              int32_t* status_flags, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ADAFLASH_H */

@@ -256,7 +256,7 @@ int oracle_verify(int dtype, const void* target, const void* draft, const int32_
     accept_len[b] = A;
     for (int i = 0; i <= k; ++i) {
       int32_t t = -1;
-      if (i < A) t = tokens[b * k + i];
+      if (i < A) t = std::min(std::max(tokens[b * k + i], 0), V - 1);
       else if (i == A) t = token;
       out_tokens[b * (k + 1) + i] = t;
     }

@@ -1,0 +1,115 @@
+"""CPU-side checks of the C ABI: the library loads, exports every declared
+symbol, sizes its workspace, and rejects bad arguments before touching the GPU.
+No compute call is made here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "adaflash.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import diffusion_drafter_verification_amd as ada
+    if not os.path.exists(ada.LIB_PATH):
+        from diffusion_drafter_verification_amd import build
+        build.build()
+    return ada.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"ADAFLASH_API\s+[\w\s\*]*?\b(adaflash_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("adaflash_verify", "adaflash_opd_loss_fwd_bwd", "adaflash_workspace_bytes",
+              "adaflash_last_error", "adaflash_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_only_the_abi_is_exported():
+    import subprocess
+    import diffusion_drafter_verification_amd as ada
+    out = subprocess.run(["nm", "-D", "--defined-only", ada.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert {n for n in exported if "adaflash" in n} == set(declared_functions())
+
+
+def test_version(lib):
+    assert lib.adaflash_version() >= 100
+
+
+def test_workspace_bytes(lib):
+    assert lib.adaflash_workspace_bytes(128, 16, 151936) > 0
+    assert lib.adaflash_workspace_bytes(0, 16, 151936) > 0     # empty batch still valid
+    assert lib.adaflash_workspace_bytes(4, 0, 64) == 0          # k < 1
+    assert lib.adaflash_workspace_bytes(4, 65, 64) == 0         # k > 64
+    assert lib.adaflash_workspace_bytes(4, 16, 0) == 0          # V < 1
+    assert lib.adaflash_workspace_bytes(-1, 16, 64) == 0
+    assert lib.adaflash_workspace_bytes(4, 16, (1 << 20) + 1) == 0
+    # Grows with the batch and the vocabulary.
+    assert lib.adaflash_workspace_bytes(256, 16, 151936) > lib.adaflash_workspace_bytes(128, 16, 151936)
+    assert lib.adaflash_workspace_bytes(128, 16, 300000) > lib.adaflash_workspace_bytes(128, 16, 151936)
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def _verify(lib, **kw):
+    args = dict(dtype=1, target=FAKE, draft=FAKE, tokens=FAKE, vl=FAKE, uni=FAKE, B=2, k=4, V=64, T=1.0,
+                acc=FAKE, out=FAKE, mg=None, c=10.0, lam=1.0, ro=FAKE, ce=None, rk=None, g=None, st=None,
+                ws=FAKE, wsb=1 << 30, stream=None)
+    args.update(kw)
+    a = args
+    return lib.adaflash_verify(a["dtype"], a["target"], a["draft"], a["tokens"], a["vl"], a["uni"], a["B"],
+                               a["k"], a["V"], a["T"], a["acc"], a["out"], a["mg"], a["c"], a["lam"], a["ro"],
+                               a["ce"], a["rk"], a["g"], a["st"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1.0), -1), (dict(T=float("nan")), -1), (dict(T=float("inf")), -1),
+    (dict(k=0), -1), (dict(k=65), -1), (dict(V=0), -1), (dict(B=-3), -1),
+    (dict(dtype=7), -1), (dict(ro=None), -1), (dict(target=None), -1),
+    (dict(draft=None), -1),                      # T > 0 needs draft logits
+    (dict(uni=None), -1), (dict(tokens=None), -1), (dict(acc=None), -1),
+    (dict(ws=None), -2), (dict(wsb=16), -2),
+    (dict(ce=FAKE, c=0.0), -1), (dict(ce=FAKE, c=-1.0), -1), (dict(g=FAKE, lam=-0.5), -1),
+    (dict(g=FAKE, lam=float("inf")), -1),
+])
+def test_verify_rejects_bad_arguments(lib, kw, code):
+    assert _verify(lib, **kw) == code
+    assert len(lib.adaflash_last_error()) > 0
+
+
+def test_greedy_without_supervision_needs_no_draft_logits(lib):
+    # Validation passes a NULL draft at T == 0; the bad workspace size then fails it.
+    assert _verify(lib, T=0.0, draft=None, uni=None, wsb=16) == -2
+
+
+def test_opd_rejects_bad_arguments(lib):
+    f = lib.adaflash_opd_loss_fwd_bwd
+    ok = dict(dtype=1, t=FAKE, d=FAKE, vl=None, B=2, k=4, V=64, c=10.0, lam=1.0, ro=FAKE, ce=None, rk=None,
+              g=None, st=None, ws=FAKE, wsb=1 << 30, stream=None)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["dtype"], a["t"], a["d"], a["vl"], a["B"], a["k"], a["V"], a["c"], a["lam"], a["ro"],
+                 a["ce"], a["rk"], a["g"], a["st"], a["ws"], a["wsb"], a["stream"])
+
+    assert call(c=0.0) == -1
+    assert call(lam=-1.0) == -1
+    assert call(d=None) == -1
+    assert call(ro=None) == -1
+    assert call(wsb=0) == -2
+    assert call(k=100) == -1
