@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused verify + supervision pass on one MI355X.
+
+Workload (the headline configuration): B=128 requests, k=16 draft tokens,
+V=151936 (Qwen3 vocabulary), bf16 logits, verify lengths ~ U{1..16}, per-request
+draft noise from {0.3, 1.0, 2.0}, T=1, clipped reverse KL with c=10 and
+lambda=1; every call verifies the batch and writes per-row losses and the bf16
+gradient with respect to the draft logits.  Inputs are seeded and synthetic
+and resident in HBM before timing starts.
+
+One JSON line is printed: verified draft positions per second (value), the
+achieved HBM bandwidth of the kernel against the MI355X peak (roofline), and
+the CPU oracle timed on a bounded sample of the same workload (cpu_baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published peak
+METRIC = "verified draft positions/sec + achieved HBM GB/s (B=128, k=16, V=151936)"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--sets", type=int, default=2, help="input sets rotated between calls")
+    ap.add_argument("--clip", type=float, default=10.0)
+    ap.add_argument("--lam", type=float, default=1.0)
+    ap.add_argument("--mode", choices=["fused", "verify", "opd"], default="fused")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run only a 1 GiB device copy (to scale HBM byte counters)")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(verify_len, accept_len, B, k, V, mode):
+    """Compulsory HBM bytes of one call: every verified row pair read once, the
+    bonus row only when it is used, the small per-request arrays, and the
+    supervision outputs."""
+    import numpy as np
+    L = np.clip(verify_len, 1, k).astype(np.int64)
+    e = 2  # bf16
+    N = int(L.sum())
+    if mode == "opd":
+        return N * 3 * V * e + 8 * N + 4 * B
+    bonus = int((accept_len == L).sum())
+    rd = 2 * N * V * e + bonus * V * e
+    small = B * (4 * k + 4 * (k + 1) + 4) + B * (4 + 4 * (k + 1)) + B * 4 * (k + 1)
+    total = rd + small
+    if mode == "fused":
+        total += N * V * e + 8 * N + 4 * (B + 1)
+    return total
+
+
+def copy_probe():
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "calls": 5}))
+
+
+def cpu_baseline(batch, mode, clip, lam, budget_s):
+    """The CPU oracle, as it stands, on the first requests of one input set,
+    repeated until about budget_s seconds have elapsed."""
+    import numpy as np
+    import oracle
+    threads = max(1, min(16, os.cpu_count() or 1))
+    nreq = 8
+    t = batch.target[:nreq]
+    d = batch.draft[:nreq]
+    tok = batch.tokens[:nreq]
+    vl = batch.verify_len[:nreq]
+    uni = batch.uniforms[:nreq]
+    positions = int(np.clip(vl, 1, t.shape[1] - 1).sum())
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        if mode != "opd":
+            oracle.verify(t, d, tok, vl, uni, T=1.0, nthreads=threads)
+        if mode != "verify":
+            oracle.opd(t, d, vl, clip, lam, with_grad=True, nthreads=threads)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": positions * done / el, "unit": "positions/s", "cores": threads, "kind": "oracle",
+            "sample": f"{nreq} requests ({positions} verified positions) of input set 0, "
+                      f"{done} repetitions in {el:.1f} s, {threads} threads"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(every request and row is independent: shard the batch across GPUs)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    if args.copy_probe:
+        copy_probe()
+        return
+
+    import diffusion_drafter_verification_amd as ada
+    import workloads as W
+
+    wl = W.WORKLOADS[4]
+    B, k, V = wl.B, wl.k, wl.V
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+
+    sets = []
+    for s in range(args.sets):
+        bt = W.generate(wl, round=s)
+        sets.append(bt)
+    dsets = []
+    for bt in sets:
+        dsets.append({
+            "t": torch.from_numpy(bt.target.view(np.int16)).view(torch.bfloat16).to(dev),
+            "d": torch.from_numpy(bt.draft.view(np.int16)).view(torch.bfloat16).to(dev),
+            "tok": torch.from_numpy(bt.tokens).to(dev),
+            "vl": torch.from_numpy(bt.verify_len).to(dev),
+            "u": torch.from_numpy(bt.uniforms).to(dev),
+        })
+    ws = ada.workspace(B, k, V, dev)
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    outt = torch.empty(B, k + 1, dtype=torch.int32, device=dev)
+    mg = torch.empty(B, k + 1, dtype=torch.float32, device=dev)
+    ro = torch.empty(B + 1, dtype=torch.int32, device=dev)
+    ce = torch.empty(B * k, dtype=torch.float32, device=dev)
+    rk = torch.empty(B * k, dtype=torch.float32, device=dev)
+    grad = torch.empty(B * k, V, dtype=torch.bfloat16, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def call(ds):
+        if args.mode == "opd":
+            ada.adaflash_opd_loss_fwd_bwd(ds["t"], ds["d"], ds["vl"], args.clip, args.lam, ro, ce, rk, grad,
+                                          status, ws, stream)
+        else:
+            fused = args.mode == "fused"
+            ada.adaflash_verify(ds["t"], ds["d"], ds["tok"], ds["vl"], ds["u"], 1.0, acc, outt, mg, args.clip,
+                                args.lam, ro, ce if fused else None, rk if fused else None,
+                                grad if fused else None, status, ws, stream)
+
+    # accept lengths per set (for the bonus-row byte count)
+    accs = []
+    for ds in dsets:
+        call(ds)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0, f"status flags {int(status.item())}"
+        accs.append(acc.cpu().numpy().copy())
+    bytes_per_set = [algorithmic_bytes(bt.verify_len, a, B, k, V, args.mode) for bt, a in zip(sets, accs)]
+    pos_per_set = [int(np.clip(bt.verify_len, 1, k).sum()) for bt in sets]
+
+    for i in range(args.warmup):
+        call(dsets[i % len(dsets)])
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        call(dsets[i % len(dsets)])
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    st = int(status.item())
+    if st != 0:
+        print(f"status flags {st} after the timed calls", file=sys.stderr)
+        sys.exit(1)
+
+    durs = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)]) * 1e-3  # seconds
+    idx = np.arange(args.steps) % len(dsets)
+    positions = float(sum(pos_per_set[j] for j in idx))
+    bytes_total = float(sum(bytes_per_set[j] for j in idx))
+    avg_dur = float(durs.mean())
+    achieved = bytes_total / args.steps / avg_dur / 1e9
+
+    res = {
+        "metric": METRIC,
+        "value": positions / elapsed,
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": ("c128 fused verify+supervision: B=128, k=16, V=151936, bf16 logits, "
+                         "verify_len~U{1..16}, sigma_b~U{0.3,1,2}, T=1, c=%g, lambda=%g, mode=%s"
+                         % (args.clip, args.lam, args.mode)),
+            "B": B, "k": k, "V": V, "input_sets": args.sets,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None,
+        },
+        "kernel_ms_avg": avg_dur * 1e3,
+        "kernel_ms_p10_p50_p90": [float(np.percentile(durs, q) * 1e3) for q in (10, 50, 90)],
+        "algorithmic_bytes_per_call": bytes_total / args.steps,
+        "verified_positions_per_call": positions / args.steps,
+    }
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(sets[0], args.mode, args.clip, args.lam, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

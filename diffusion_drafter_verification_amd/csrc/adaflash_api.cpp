@@ -44,11 +44,11 @@ size_t workspace_layout(int B, int k, int V, char* base, Workspace* ws) {
   char* Lc = take(sizeof(int32_t) * (size_t)(B > 0 ? B : 1));
   char* roff = take(sizeof(int32_t) * (size_t)(B + 1));
   char* rowlist = take(sizeof(int32_t) * (rows > 0 ? rows : 1));
-  char* rowcnt = take(sizeof(int32_t) * (rows > 0 ? rows : 1));
-  char* reqcnt = take(sizeof(int32_t) * (size_t)(B > 0 ? B : 1));
-  char* part1 = take(sizeof(float4) * 2 * (rows > 0 ? rows : 1) * G);
-  char* part2 = take(sizeof(float4) * (rows > 0 ? rows : 1) * G);
-  char* rowrec = take(sizeof(int4) * (rows > 0 ? rows : 1));
+  char* rowcnt = take(sizeof(int32_t) * kCounterStride * (rows > 0 ? rows : 1));
+  char* reqcnt = take(sizeof(int32_t) * kCounterStride * (size_t)(B > 0 ? B : 1));
+  char* part1 = take(sizeof(float) * kRec1 * (rows > 0 ? rows : 1) * G);
+  char* part2 = take(sizeof(float) * kRec2 * (rows > 0 ? rows : 1) * G);
+  char* rowrec = take(sizeof(float) * kRowRec * (rows > 0 ? rows : 1));
   if (ws) {
     ws->nrows = (int32_t*)nrows;
     ws->Lc = (int32_t*)Lc;
@@ -56,9 +56,9 @@ size_t workspace_layout(int B, int k, int V, char* base, Workspace* ws) {
     ws->rowlist = (int32_t*)rowlist;
     ws->rowcnt = (int32_t*)rowcnt;
     ws->reqcnt = (int32_t*)reqcnt;
-    ws->part1 = (float4*)part1;
-    ws->part2 = (float4*)part2;
-    ws->rowrec = (int4*)rowrec;
+    ws->part1 = (float*)part1;
+    ws->part2 = (float*)part2;
+    ws->rowrec = (float*)rowrec;
   }
   return off;
 }

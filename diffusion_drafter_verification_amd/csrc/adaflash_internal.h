@@ -10,10 +10,15 @@ namespace adaflash {
 
 // Workgroup size and elements of each logit row a thread keeps in registers.
 constexpr int kThreads = 256;
-constexpr int kElems = 16;
+constexpr int kElems = 32;
 constexpr int kChunk = kThreads * kElems;  // elements of one row per workgroup
 
 inline int num_chunks(int V) { return (V + kChunk - 1) / kChunk; }
+
+// Arrival counters sit 256 bytes apart so that no two share a cache line.
+constexpr int kCounterStride = 64;
+// Floats per published chunk record.
+constexpr int kRec1 = 8, kRec2 = 4, kRowRec = 4;
 
 // Device scratch carved out of the caller's workspace.
 struct Workspace {
@@ -21,11 +26,11 @@ struct Workspace {
   int32_t* Lc;       // [B]    clamped verify lengths
   int32_t* roff;     // [B+1]  start of each request in the row list
   int32_t* rowlist;  // [B*(k+1)] target row index b*(k+1)+i of each listed row
-  int32_t* rowcnt;   // [B*(k+1)] per-row arrival counters (zeroed per call)
-  int32_t* reqcnt;   // [B]    per-request arrival counters (zeroed per call)
-  float4* part1;     // [B*(k+1)*G*2] per-chunk row statistics
-  float4* part2;     // [B*(k+1)*G]   per-chunk supervision / residual partials
-  int4* rowrec;      // [B*(k+1)] per-row accept flag and margin
+  int32_t* rowcnt;   // [B*(k+1)*kCounterStride] per-row arrival counters (zeroed per call)
+  int32_t* reqcnt;   // [B*kCounterStride]       per-request arrival counters (zeroed per call)
+  float* part1;      // [B*(k+1)*G*kRec1] per-chunk row statistics
+  float* part2;      // [B*(k+1)*G*kRec2] per-chunk supervision / residual partials
+  float* rowrec;     // [B*(k+1)*kRowRec] per-row accept flag and margin
 };
 
 // Layout of the workspace for (B, k, V); returns the bytes needed.  With

@@ -54,7 +54,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr int kWaves = kThreads / 64;
 constexpr int kIntMax = 0x7fffffff;
-constexpr int kSpinLimit = 1 << 18;  // bound on polls (s_sleep between polls)
+constexpr int kSpinLimit = 1 << 16;  // bound on polls (~0.5 us of s_sleep between polls)
 
 struct KParams {
   const void* target;
@@ -75,9 +75,9 @@ struct KParams {
   const int32_t* rowlist;
   int32_t* rowcnt;
   int32_t* reqcnt;
-  float4* part1;
-  float4* part2;
-  int4* rowrec;
+  float* part1;
+  float* part2;
+  float* rowrec;
   int B, k, V, G;
   float kT;  // log2(e) / T (0 in greedy mode)
   float clip_c, lambda;
@@ -174,18 +174,37 @@ __device__ __forceinline__ float wg_scan_excl(float x, float* red, float* total)
   return wb + ex;
 }
 
-// Arrive at a counter and wait until it reaches `target`.  Thread 0 publishes
-// (release, agent scope) and polls; the rest of the workgroup waits at the
-// barrier.  Returns false if the wait hit its bound.
+// Cross-workgroup records.  Everything one workgroup publishes for another
+// (chunk records, accept flags) is written and read with agent-scope relaxed
+// atomics, which are coherent across the XCDs' L2 caches; a wait on every
+// outstanding memory operation before the counter increment makes those
+// stores complete first, and the readers issue their loads only after they
+// have seen the counter.  Agent-scope release/acquire fences would also write
+// back and invalidate the L2 at every barrier, which measured about 15x slower
+// for this grid.
+__device__ __forceinline__ void pub_store(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float pub_load(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void complete_stores() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Arrive at a counter and wait until it reaches `target`.  Thread 0 arrives
+// and polls; the rest of the workgroup waits at the barrier.  Returns false
+// if the wait hit its bound (or another wait already did).
 __device__ bool arrive_and_wait(int32_t* cnt, int target, int32_t* status, int* sh) {
   if (threadIdx.x == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    complete_stores();
     __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     int ok = 1, spins = 0;
     while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      __builtin_amdgcn_s_sleep(4);
+      __builtin_amdgcn_s_sleep(20);
       ++spins;
-      // Give up at the bound, or at once when another wait has already given up.
       if (spins > kSpinLimit ||
           ((spins & 63) == 0 && status &&
            (__hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & ADAFLASH_FLAG_SYNC_TIMEOUT))) {
@@ -193,7 +212,7 @@ __device__ bool arrive_and_wait(int32_t* cnt, int target, int32_t* status, int* 
         break;
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     if (!ok && status) __hip_atomic_fetch_or(status, ADAFLASH_FLAG_SYNC_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *sh = ok;
   }
@@ -303,8 +322,10 @@ __device__ RowStats combine_part1(const KParams& P, int r, float kT, float* red)
   float4 a = make_float4(neg_inf(), __int_as_float(kIntMax), 0.f, 0.f);
   float4 c = make_float4(neg_inf(), 0.f, 0.f, 0.f);
   if ((int)threadIdx.x < P.G) {
-    a = P.part1[((size_t)r * P.G + threadIdx.x) * 2 + 0];
-    c = P.part1[((size_t)r * P.G + threadIdx.x) * 2 + 1];
+    const float* rec = P.part1 + ((size_t)r * P.G + threadIdx.x) * kRec1;
+    a = make_float4(pub_load(rec + 0), pub_load(rec + 1), NEED_T ? pub_load(rec + 2) : 0.f,
+                    NEED_1 ? pub_load(rec + 3) : 0.f);
+    c = make_float4(pub_load(rec + 4), NEED_T ? pub_load(rec + 5) : 0.f, NEED_1 ? pub_load(rec + 6) : 0.f, 0.f);
   }
   float m[2] = {a.x, c.x};
   const int mops[2] = {OP_MAX, OP_MAX};
@@ -385,7 +406,11 @@ __device__ void finalize_request(const KParams& P, int b, FinShared& fs) {
     for (int i = 0; i <= L; ++i) {
       const int r = r0 + i;
       float4 a = make_float4(neg_inf(), __int_as_float(kIntMax), 0.f, 0.f);
-      if (tid < G) a = P.part1[((size_t)r * G + tid) * 2];
+      if (tid < G) {
+        const float* rec = P.part1 + ((size_t)r * G + tid) * kRec1;
+        a.x = pub_load(rec + 0);
+        a.y = pub_load(rec + 1);
+      }
       float v1[1] = {a.x};
       const int o1[1] = {OP_MAX};
       wg_reduce<1>(v1, o1, fs.red);
@@ -413,7 +438,7 @@ __device__ void finalize_request(const KParams& P, int b, FinShared& fs) {
     // Sampled: first rejected row from the per-row accept flags.
     int first = kIntMax;
     for (int i = tid; i < L; i += kThreads)
-      if (P.rowrec[r0 + i].y == 0) first = min(first, i);
+      if (pub_load(P.rowrec + (size_t)(r0 + i) * kRowRec + 1) == 0.f) first = min(first, i);
     float v1[1] = {__int_as_float(first)};
     const int o1[1] = {OP_MINI};
     wg_reduce<1>(v1, o1, fs.red);
@@ -433,7 +458,7 @@ __device__ void finalize_request(const KParams& P, int b, FinShared& fs) {
     if (A < L) {
       drow = BF16 ? (const void*)((const uint16_t*)P.draft + ((size_t)b * k + A) * V)
                   : (const void*)((const float*)P.draft + ((size_t)b * k + A) * V);
-      const float mj = tid < G ? P.part2[(size_t)rs * G + tid].z : 0.f;
+      const float mj = tid < G ? pub_load(P.part2 + ((size_t)rs * G + tid) * kRec2 + 2) : 0.f;
       locate_chunk(mj, G, us, fs, &jc, &base, &thr, &tot);
       resid = tot > 0.f;
     }
@@ -441,8 +466,9 @@ __device__ void finalize_request(const KParams& P, int b, FinShared& fs) {
       // Draw from p of row rs (bonus row, or the rejected row when Z == 0).
       float mj = 0.f;
       if (tid < G) {
-        const float4 a = P.part1[((size_t)rs * G + tid) * 2];
-        mj = a.x == neg_inf() ? 0.f : a.z * fexp2((a.x - st.Mp) * P.kT) * invSp;
+        const float* rec = P.part1 + ((size_t)rs * G + tid) * kRec1;
+        const float m = pub_load(rec + 0), sT = pub_load(rec + 2);
+        mj = m == neg_inf() ? 0.f : sT * fexp2((m - st.Mp) * P.kT) * invSp;
       }
       locate_chunk(mj, G, us, fs, &jc, &base, &thr, &tot);
     }
@@ -642,8 +668,14 @@ __global__ __launch_bounds__(kThreads) void row_kernel(KParams P) {
     const int sops[5] = {OP_SUM, OP_SUM, OP_SUM, OP_SUM, OP_MINI};
     wg_reduce<5>(s, sops, fs.red);
     if (tid == 0) {
-      P.part1[((size_t)r * G + j) * 2 + 0] = make_float4(Mp, s[4], s[0], s[2]);
-      P.part1[((size_t)r * G + j) * 2 + 1] = make_float4(Mq, s[1], s[3], 0.f);
+      float* rec = P.part1 + ((size_t)r * G + j) * kRec1;
+      pub_store(rec + 0, Mp);
+      pub_store(rec + 1, s[4]);
+      pub_store(rec + 2, s[0]);
+      pub_store(rec + 3, s[2]);
+      pub_store(rec + 4, Mq);
+      pub_store(rec + 5, s[1]);
+      pub_store(rec + 6, s[3]);
     }
   }
 
@@ -651,7 +683,7 @@ __global__ __launch_bounds__(kThreads) void row_kernel(KParams P) {
   bool alive = true;
   if (do_rows) {
     // ---- barrier 1: all chunks of this row have published their statistics.
-    alive = arrive_and_wait(&P.rowcnt[r], G, P.status, &sh_ok);
+    alive = arrive_and_wait(&P.rowcnt[(size_t)r * kCounterStride], G, P.status, &sh_ok);
     if (alive) {
       const RowStats st = combine_part1<SAMPLED, OPD && !(SAMPLED && T1)>(P, r, P.kT, fs.red);
       float Sp1 = st.Sp1, Sq1 = st.Sq1;
@@ -677,7 +709,8 @@ __global__ __launch_bounds__(kThreads) void row_kernel(KParams P) {
         const float u = P.uniforms[(size_t)b * (k + 1) + i];
         accept = u * qx < px;
         if (tid == 0 && j == 0) {
-          P.rowrec[r] = make_int4(0, accept ? 1 : 0, __float_as_int(px - u * qx), 0);
+          pub_store(P.rowrec + (size_t)r * kRowRec + 1, accept ? 1.f : 0.f);
+          pub_store(P.rowrec + (size_t)r * kRowRec + 2, px - u * qx);
           if (P.margins) P.margins[(size_t)b * (k + 1) + i] = px - u * qx;
         }
       }
@@ -722,18 +755,23 @@ __global__ __launch_bounds__(kThreads) void row_kernel(KParams P) {
         float s[3] = {Spart, Rpart, Zpart};
         const int ops[3] = {OP_SUM, OP_SUM, OP_SUM};
         wg_reduce<3>(s, ops, fs.red);
-        if (tid == 0) P.part2[(size_t)r * G + j] = make_float4(s[0], s[1], s[2], 0.f);
+        if (tid == 0) {
+          float* rec = P.part2 + ((size_t)r * G + j) * kRec2;
+          pub_store(rec + 0, s[0]);
+          pub_store(rec + 1, s[1]);
+          pub_store(rec + 2, s[2]);
+        }
       }
 
       if constexpr (OPD) {
         // ---- barrier 2: supervision sums of every chunk are published.
-        alive = arrive_and_wait(&P.rowcnt[r], 2 * G, P.status, &sh_ok);
+        alive = arrive_and_wait(&P.rowcnt[(size_t)r * kCounterStride], 2 * G, P.status, &sh_ok);
         if (alive) {
           float sr[2] = {0.f, 0.f};
           if (tid < G) {
-            const float4 a = P.part2[(size_t)r * G + tid];
-            sr[0] = a.x;
-            sr[1] = a.y;
+            const float* rec = P.part2 + ((size_t)r * G + tid) * kRec2;
+            sr[0] = pub_load(rec + 0);
+            sr[1] = pub_load(rec + 1);
           }
           const int srops[2] = {OP_SUM, OP_SUM};
           wg_reduce<2>(sr, srops, fs.red);
@@ -800,12 +838,12 @@ __global__ __launch_bounds__(kThreads) void row_kernel(KParams P) {
   if constexpr (VERIFY) {
     // ---- request arrival: the last workgroup of the request finalises it.
     if (tid == 0) {
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      complete_stores();
       const int total = G * (L + 1);
-      const int old = __hip_atomic_fetch_add(&P.reqcnt[b], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const int last = (old == total - 1) ? 1 : 0;
-      if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      sh_ok = last;
+      const int old = __hip_atomic_fetch_add(&P.reqcnt[(size_t)b * kCounterStride], 1, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      sh_ok = (old == total - 1) ? 1 : 0;
     }
     __syncthreads();
     const int last = sh_ok;
@@ -860,9 +898,9 @@ __global__ __launch_bounds__(1024) void pack_kernel(const int32_t* verify_len, i
       ws.roff[b] = start;
       for (int ii = 0; ii < n2; ++ii) {
         ws.rowlist[start + ii] = b * (k + 1) + ii;
-        ws.rowcnt[start + ii] = 0;
+        ws.rowcnt[(size_t)(start + ii) * kCounterStride] = 0;
       }
-      ws.reqcnt[b] = 0;
+      ws.reqcnt[(size_t)b * kCounterStride] = 0;
     }
     carry += s_scan[1023];
     carry2 += s_scan2[1023];

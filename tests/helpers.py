@@ -116,11 +116,19 @@ def bf16_ulp(x: np.ndarray) -> np.ndarray:
     return 2.0 ** (e - 7)
 
 
+def _loss_excess(g, r):
+    """Error beyond 1e-3 relative + 1e-6 absolute; equal infinities match."""
+    g = g.astype(np.float64)
+    same_inf = np.isinf(r) & (g == r)
+    with np.errstate(invalid="ignore"):
+        e = np.abs(g - r) - (1e-3 * np.abs(r) + 1e-6)
+    e = np.where(same_inf, -1.0, e)
+    return np.where(np.isnan(e), np.inf, e)
+
+
 def compare_losses(ce_g, rk_g, ce_r, rk_r):
-    ce_g = ce_g.astype(np.float64)
-    rk_g = rk_g.astype(np.float64)
-    e1 = np.abs(ce_g - ce_r) - (1e-3 * np.abs(ce_r) + 1e-6)
-    e2 = np.abs(rk_g - rk_r) - (1e-3 * np.abs(rk_r) + 1e-6)
+    e1 = _loss_excess(ce_g, ce_r)
+    e2 = _loss_excess(rk_g, rk_r)
     assert (e1 <= 0).all(), (np.argmax(e1), ce_g[np.argmax(e1)], ce_r[np.argmax(e1)])
     assert (e2 <= 0).all(), (np.argmax(e2), rk_g[np.argmax(e2)], rk_r[np.argmax(e2)])
 

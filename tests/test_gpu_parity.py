@@ -198,9 +198,9 @@ def test_ties_take_the_lowest_index():
 def test_deterministic():
     say("determinism")
     bt = W.generate(small("d", B=12, k=8, V=20000, seed=12), T=1.0)
-    first = gpu_verify(bt, 1.0, opd=True, c=0.01)
+    first = gpu_verify(bt, 1.0, opd=True, clip_c=0.01)
     for _ in range(10):
-        again = gpu_verify(bt, 1.0, opd=True, c=0.01)
+        again = gpu_verify(bt, 1.0, opd=True, clip_c=0.01)
         for key in ("accept_len", "out_tokens", "row_offsets", "loss_ce", "loss_rkl", "grad"):
             assert np.array_equal(first[key], again[key]), key
         assert np.array_equal(first["margins"], again["margins"], equal_nan=True)
