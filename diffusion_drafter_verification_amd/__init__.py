@@ -21,7 +21,9 @@ from typing import Optional
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libadaflash.so")
+# ADAFLASH_LIB may name another build of the same library (for example an
+# instrumented one); by default the in-tree build next to this file is used.
+LIB_PATH = os.environ.get("ADAFLASH_LIB") or os.path.join(_PKG, "libadaflash.so")
 
 ADAFLASH_F32 = 0
 ADAFLASH_BF16 = 1

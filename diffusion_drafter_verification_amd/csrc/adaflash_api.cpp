@@ -40,22 +40,14 @@ size_t workspace_layout(int B, int k, int V, char* base, Workspace* ws) {
     off = align_up(off + bytes);
     return base ? base + at : nullptr;
   };
-  char* nrows = take(sizeof(int32_t));
   char* Lc = take(sizeof(int32_t) * (size_t)(B > 0 ? B : 1));
-  char* roff = take(sizeof(int32_t) * (size_t)(B + 1));
-  char* rowlist = take(sizeof(int32_t) * (rows > 0 ? rows : 1));
   char* rowcnt = take(sizeof(int32_t) * kCounterStride * (rows > 0 ? rows : 1));
-  char* reqcnt = take(sizeof(int32_t) * kCounterStride * (size_t)(B > 0 ? B : 1));
   char* part1 = take(sizeof(float) * kRec1 * (rows > 0 ? rows : 1) * G);
   char* part2 = take(sizeof(float) * kRec2 * (rows > 0 ? rows : 1) * G);
   char* rowrec = take(sizeof(float) * kRowRec * (rows > 0 ? rows : 1));
   if (ws) {
-    ws->nrows = (int32_t*)nrows;
     ws->Lc = (int32_t*)Lc;
-    ws->roff = (int32_t*)roff;
-    ws->rowlist = (int32_t*)rowlist;
     ws->rowcnt = (int32_t*)rowcnt;
-    ws->reqcnt = (int32_t*)reqcnt;
     ws->part1 = (float*)part1;
     ws->part2 = (float*)part2;
     ws->rowrec = (float*)rowrec;

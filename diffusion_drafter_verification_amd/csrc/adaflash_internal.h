@@ -22,12 +22,8 @@ constexpr int kRec1 = 8, kRec2 = 4, kRowRec = 4;
 
 // Device scratch carved out of the caller's workspace.
 struct Workspace {
-  int32_t* nrows;    // [1]    rows in the row list
   int32_t* Lc;       // [B]    clamped verify lengths
-  int32_t* roff;     // [B+1]  start of each request in the row list
-  int32_t* rowlist;  // [B*(k+1)] target row index b*(k+1)+i of each listed row
   int32_t* rowcnt;   // [B*(k+1)*kCounterStride] per-row arrival counters (zeroed per call)
-  int32_t* reqcnt;   // [B*kCounterStride]       per-request arrival counters (zeroed per call)
   float* part1;      // [B*(k+1)*G*kRec1] per-chunk row statistics
   float* part2;      // [B*(k+1)*G*kRec2] per-chunk supervision / residual partials
   float* rowrec;     // [B*(k+1)*kRowRec] per-row accept flag and margin

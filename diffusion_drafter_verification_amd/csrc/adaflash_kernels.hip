@@ -1,9 +1,10 @@
 // gfx950 (CDNA4) kernels for the ragged verify-and-supervise pass.
 //
 // Work decomposition
-//   The pack kernel clamps the verify lengths, builds the list of rows that
-//   must be read -- request b contributes its L_b verified rows plus, when
-//   verifying, its bonus row L_b -- and clears the arrival counters.
+//   The pack kernel clamps the verify lengths, writes the packed row offsets
+//   and clears the arrival counters.  Request b contributes its L_b verified
+//   rows plus, when verifying, its bonus row L_b; workgroups of the padded
+//   positions beyond that exit at once.
 //
 //   The row kernel gives each (row, chunk) pair one 256-thread workgroup.  A
 //   chunk is kChunk = 4096 consecutive vocabulary entries; each thread keeps
@@ -54,7 +55,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr int kWaves = kThreads / 64;
 constexpr int kIntMax = 0x7fffffff;
-constexpr int kSpinLimit = 1 << 16;  // bound on polls (~0.5 us of s_sleep between polls)
+constexpr int kSpinLimit = 1 << 18;  // bound on polls (~0.2 us of s_sleep between polls)
 
 struct KParams {
   const void* target;
@@ -69,12 +70,8 @@ struct KParams {
   float* loss_rkl;
   void* grad;
   int32_t* status;
-  const int32_t* nrows;
   const int32_t* Lc;
-  const int32_t* roff;
-  const int32_t* rowlist;
   int32_t* rowcnt;
-  int32_t* reqcnt;
   float* part1;
   float* part2;
   float* rowrec;
@@ -203,7 +200,7 @@ __device__ bool arrive_and_wait(int32_t* cnt, int target, int32_t* status, int* 
     __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     int ok = 1, spins = 0;
     while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      __builtin_amdgcn_s_sleep(20);
+      __builtin_amdgcn_s_sleep(6);
       ++spins;
       if (spins > kSpinLimit ||
           ((spins & 63) == 0 && status &&
@@ -228,15 +225,24 @@ __device__ __forceinline__ void flag(int32_t* status, int bits) {
 
 // ------------------------------------------------------------ chunk storage
 
-// 16 consecutive-slot entries of one row held by one thread.  Entry e sits at
-// vocabulary index v0 + (e / VEC) * kThreads * VEC + tid * VEC + e % VEC, so
-// each slot is one coalesced 16-byte load across the workgroup.  Entries past
-// V read as -inf.
+// kElems entries of one row held by one thread.  Entry e sits at vocabulary
+// index v0 + (e / VEC) * kThreads * VEC + tid * VEC + e % VEC, so each slot is
+// one coalesced 16-byte load across the workgroup.  Entries past V read as the
+// most negative finite value in both rows: they add nothing to maxima or sums
+// of exponentials, and unlike -inf their difference z_q - z_p is 0, not NaN.
 template <bool BF16>
 struct Chunk {
   static constexpr int VEC = BF16 ? 8 : 4;
   static constexpr int NW = BF16 ? kElems / 2 : kElems;
   uint32_t w[NW];
+
+  // Makes the packed words opaque to the optimiser so that values unpacked
+  // before this point are recomputed (one shift or mask each) rather than
+  // kept live across the workgroup reductions.
+  __device__ __forceinline__ void opaque() {
+#pragma unroll
+    for (int q = 0; q < NW; ++q) asm volatile("" : "+v"(w[q]));
+  }
 
   __device__ __forceinline__ float get(int e) const {
     if constexpr (BF16) {
@@ -258,7 +264,7 @@ template <bool BF16, bool ALIGNED>
 __device__ __forceinline__ void load_chunk(Chunk<BF16>& c, const void* row, int v0, int V) {
   constexpr int VEC = Chunk<BF16>::VEC;
   constexpr int NV = kElems / VEC;
-  const uint32_t ninf = BF16 ? 0xff80ff80u : 0xff800000u;
+  const uint32_t ninf = BF16 ? 0xff7fff7fu : 0xff7fffffu;  // -max finite
 #pragma unroll
   for (int s = 0; s < NV; ++s) {
     const int idx0 = v0 + s * (kThreads * VEC) + (int)threadIdx.x * VEC;
@@ -281,7 +287,7 @@ __device__ __forceinline__ void load_chunk(Chunk<BF16>& c, const void* row, int 
       for (int u = 0; u < VEC; ++u) {
         const int idx = idx0 + u;
         if constexpr (BF16) {
-          uint32_t h = idx < V ? (uint32_t)((const uint16_t*)row)[idx] : 0xff80u;
+          uint32_t h = idx < V ? (uint32_t)((const uint16_t*)row)[idx] : 0xff7fu;
           const int wi = s * 4 + (u >> 1);
           if (u & 1) c.w[wi] |= h << 16;
           else c.w[wi] = h;
@@ -299,10 +305,12 @@ __device__ __forceinline__ float load_logit(const void* row, int v) {
   else return ((const float*)row)[v];
 }
 
-// Two rounded values packed for a bf16 store (round to nearest even).
+// Two values rounded to bf16 (nearest even) and packed: one v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const __bf16 a = (__bf16)lo, b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  const f32x2_t f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
 
 // ------------------------------------------------------------ row statistics
@@ -397,7 +405,7 @@ __device__ void finalize_request(const KParams& P, int b, FinShared& fs) {
   const int k = P.k, V = P.V, G = P.G;
   const int tid = threadIdx.x;
   const int L = P.Lc[b];
-  const int r0 = P.roff[b];
+  const int r0 = b * (k + 1);  // row slot of position 0
   int A = L, token = 0;
   float sample_margin = __int_as_float(0x7fc00000);
 
@@ -592,13 +600,15 @@ __global__ __launch_bounds__(kThreads) void row_kernel(KParams P) {
 
   const int tid = threadIdx.x;
   const int G = P.G;
-  const int r = (int)blockIdx.x / G;
-  const int j = (int)blockIdx.x - r * G;
-  if (r >= *P.nrows) return;
   const int k = P.k, V = P.V;
-  const int rid = P.rowlist[r];
-  const int b = rid / (k + 1), i = rid - b * (k + 1);
+  // Workgroup -> (request b, position i, chunk j); row slot r = b*(k+1) + i.
+  const int s_ = (int)blockIdx.x / G;
+  const int j = (int)blockIdx.x - s_ * G;
+  const int b = s_ / (k + 1), i = s_ - b * (k + 1);
   const int L = P.Lc[b];
+  if (i > L || (!VERIFY && i == L)) return;
+  const int r = s_;
+  const int rid = r;
   const bool draft_row = i < L;
   const bool need_q = draft_row && (OPD || SAMPLED);
   const int v0 = j * kChunk;
@@ -622,6 +632,8 @@ __global__ __launch_bounds__(kThreads) void row_kernel(KParams P) {
 #pragma unroll
     for (int e = 0; e < kElems; ++e) mq = fmaxf(mq, cq.get(e));
   }
+  cp.opaque();
+  cq.opaque();
   {
     float v[2] = {mp, mq};
     const int ops[2] = {OP_MAX, OP_MAX};
@@ -716,6 +728,8 @@ __global__ __launch_bounds__(kThreads) void row_kernel(KParams P) {
       }
 
       // ---- phase 2: supervision sums and/or the residual mass of this chunk.
+      cp.opaque();
+      cq.opaque();
       float Spart = 0.f, Rpart = 0.f, Zpart = 0.f;
       float gc[kElems];
       float qv[kElems];
@@ -835,38 +849,378 @@ __global__ __launch_bounds__(kThreads) void row_kernel(KParams P) {
     }
   }
 
-  if constexpr (VERIFY) {
-    // ---- request arrival: the last workgroup of the request finalises it.
-    if (tid == 0) {
-      complete_stores();
-      const int total = G * (L + 1);
-      const int old = __hip_atomic_fetch_add(&P.reqcnt[(size_t)b * kCounterStride], 1, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT);
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      sh_ok = (old == total - 1) ? 1 : 0;
-    }
-    __syncthreads();
-    const int last = sh_ok;
-    __syncthreads();
-    if (last) finalize_request<BF16, ALIGNED, VMODE>(P, b, fs);
-  }
   (void)alive;
   (void)GREEDY;
 }
 
+// ----------------------------------------------- supervision kernel (T = 1)
+//
+// Supervision at temperature 1, alone or fused with greedy verification or
+// with sampled verification at T = 1.  Pass 1 publishes per chunk the maxima,
+// the sums of exponentials, W = sum e dz and A = max e dz, where
+// e = exp(z_q - m) (m: this chunk's maximum of z_q) and dz = z_q - z_p.  After
+// the row barrier every chunk derives lse_q, lse_p, D = lse_q - lse_p, the
+// unclipped KL = sum_v q_v dz_v - D, and a bound on every entry's term
+// f_v = q_v (dz_v - D):
+//   f_v <= exp(m_j - lse_q) (A_j + max(0, -D)) <= (max_j e^{m_j - M} A_j + max(0, -D)) / S_q,
+// using e_v <= 1 (M: row maximum of z_q, S_q = sum_v exp(z_q - M)).
+// When the bound is below c no entry is clipped, so R = KL and S = KL + 1,
+// and each chunk writes its gradient at once:
+//   g_v = q_v (1 + lambda (d_v - KL)) - [v == x*],  d_v = dz_v - D.
+// Otherwise (or when a row holds -inf or non-finite logits) the exact path
+// accumulates R and S per chunk and meets the row at a second barrier.
+// Only the packed logits stay in registers between passes; q and dz are
+// recomputed (the kernel is bound by bytes in flight, so registers are worth
+// more than the extra arithmetic).
+
+struct SupStats {
+  float Mp, Mq, Sp, Sq, Wsum, BA;
+  int xstar, nonfinite;
+};
+
+__device__ SupStats combine_sup(const KParams& P, int r, float* red) {
+  float mp = neg_inf(), mq = neg_inf(), sp = 0.f, sq = 0.f, w = 0.f, a = neg_inf();
+  int idx = kIntMax;
+  if ((int)threadIdx.x < P.G) {
+    const float* rec = P.part1 + ((size_t)r * P.G + threadIdx.x) * kRec1;
+    mp = pub_load(rec + 0);
+    idx = __float_as_int(pub_load(rec + 1));
+    sp = pub_load(rec + 2);
+    w = pub_load(rec + 3);
+    mq = pub_load(rec + 4);
+    sq = pub_load(rec + 5);
+    a = pub_load(rec + 6);
+  }
+  float m[2] = {mp, mq};
+  const int mops[2] = {OP_MAX, OP_MAX};
+  wg_reduce<2>(m, mops, red);
+  const float fp = mp == neg_inf() ? 0.f : fexp2((mp - m[0]) * kLog2e);
+  const float fq = mq == neg_inf() ? 0.f : fexp2((mq - m[1]) * kLog2e);
+  const bool fin = (int)threadIdx.x >= P.G || (__builtin_isfinite(w) && !__builtin_isnan(a) && a < __builtin_inff());
+  float v[6] = {sp * fp, sq * fq, fq > 0.f ? w * fq : 0.f, fq > 0.f ? fq * a : neg_inf(),
+                __int_as_float(mp == m[0] ? idx : kIntMax), __int_as_float(fin ? 0 : 1)};
+  const int ops[6] = {OP_SUM, OP_SUM, OP_SUM, OP_MAX, OP_MINI, OP_MAX};
+  // OP_MAX on the flag's bit pattern is an integer max for these two values.
+  wg_reduce<6>(v, ops, red);
+  SupStats s;
+  s.Mp = m[0];
+  s.Mq = m[1];
+  s.Sp = v[0];
+  s.Sq = v[1];
+  s.Wsum = v[2];
+  s.BA = v[3];
+  s.xstar = __float_as_int(v[4]);
+  s.nonfinite = __float_as_int(v[5]) != 0;
+  return s;
+}
+
+template <bool BF16, bool ALIGNED, int VMODE>
+__global__ __launch_bounds__(kThreads) void sup_kernel(KParams P) {
+  constexpr bool SAMPLED = VMODE == 2, VERIFY = VMODE != 0;
+  constexpr int VEC = Chunk<BF16>::VEC;
+  constexpr int NV = kElems / VEC;
+  __shared__ FinShared fs;
+  __shared__ int sh_ok;
+
+  const int tid = threadIdx.x;
+  const int G = P.G;
+  const int k = P.k, V = P.V;
+  // Workgroup -> (request b, position i, chunk j); row slot r = b*(k+1) + i.
+  // Supervision alone uses positions i < k, verification also the bonus slot.
+  const int per_req = VERIFY ? k + 1 : k;
+  const int s_ = (int)blockIdx.x / G;
+  const int j = (int)blockIdx.x - s_ * G;
+  const int b = s_ / per_req, i = s_ - b * per_req;
+  const int L = P.Lc[b];
+  if (i > L || (!VERIFY && i == L)) return;
+  const int r = b * (k + 1) + i;
+  const bool draft_row = i < L;
+  const int v0 = j * kChunk;
+
+  const void* trow = BF16 ? (const void*)((const uint16_t*)P.target + (size_t)r * V)
+                          : (const void*)((const float*)P.target + (size_t)r * V);
+  const void* drow = nullptr;
+  if (draft_row)
+    drow = BF16 ? (const void*)((const uint16_t*)P.draft + ((size_t)b * k + i) * V)
+                : (const void*)((const float*)P.draft + ((size_t)b * k + i) * V);
+
+  // ---- pass 1
+  Chunk<BF16> cp, cq;
+  load_chunk<BF16, ALIGNED>(cp, trow, v0, V);
+  if (draft_row) load_chunk<BF16, ALIGNED>(cq, drow, v0, V);
+  // Per-row scalars needed after the barrier, fetched now so that their
+  // latency overlaps the chunk loads.
+  int xtok = 0, n = 0;
+  float u_acc = 0.f, zpx = 0.f, zqx = 0.f;
+  if (draft_row) {
+    n = P.row_offsets[b] + i;  // packed row
+    if constexpr (SAMPLED) {
+      xtok = P.tokens[(size_t)b * k + i];
+      if (xtok < 0 || xtok >= V) {
+        if (tid == 0 && j == 0) flag(P.status, ADAFLASH_FLAG_BAD_TOKEN);
+        xtok = xtok < 0 ? 0 : V - 1;
+      }
+      u_acc = P.uniforms[(size_t)b * (k + 1) + i];
+      zpx = load_logit<BF16>(trow, xtok);
+      zqx = load_logit<BF16>(drow, xtok);
+    }
+  }
+  float mp = neg_inf(), mq = neg_inf();
+#pragma unroll
+  for (int e = 0; e < kElems; ++e) mp = fmaxf(mp, cp.get(e));
+  if (draft_row) {
+#pragma unroll
+    for (int e = 0; e < kElems; ++e) mq = fmaxf(mq, cq.get(e));
+  }
+  cp.opaque();
+  cq.opaque();
+  float Mw[2] = {mp, mq};
+  {
+    const int ops[2] = {OP_MAX, OP_MAX};
+    wg_reduce<2>(Mw, ops, fs.red);
+  }
+  int cand = kIntMax;
+  if (mp == Mw[0]) {
+#pragma unroll
+    for (int e = kElems - 1; e >= 0; --e)
+      if (cp.get(e) == Mw[0]) cand = entry_index<BF16>(v0, e);
+  }
+  float sp = 0.f, sq = 0.f, W = 0.f, Amax = neg_inf();
+  const float ap = Mw[0] == neg_inf() ? 0.f : -Mw[0] * kLog2e;
+  const float aq = Mw[1] == neg_inf() ? 0.f : -Mw[1] * kLog2e;
+  if (draft_row) {
+#pragma unroll
+    for (int e = 0; e < kElems; ++e) {
+      const float zq = cq.get(e), zp = cp.get(e);
+      const float ee = fexp2(fmaf(zq, kLog2e, aq));
+      sp += fexp2(fmaf(zp, kLog2e, ap));
+      sq += ee;
+      const float pr = ee * (zq - zp);
+      W += pr;
+      Amax = fmaxf(Amax, pr);
+    }
+  } else if (SAMPLED) {
+#pragma unroll
+    for (int e = 0; e < kElems; ++e) sp += fexp2(fmaf(cp.get(e), kLog2e, ap));
+  }
+  {
+    float v[5] = {sp, sq, W, Amax, __int_as_float(cand)};
+    const int ops[5] = {OP_SUM, OP_SUM, OP_SUM, OP_MAX, OP_MINI};
+    wg_reduce<5>(v, ops, fs.red);
+    if (tid == 0) {
+      float* rec = P.part1 + ((size_t)r * G + j) * kRec1;
+      pub_store(rec + 0, Mw[0]);
+      pub_store(rec + 1, v[4]);
+      pub_store(rec + 2, v[0]);
+      pub_store(rec + 3, v[2]);
+      pub_store(rec + 4, Mw[1]);
+      pub_store(rec + 5, v[1]);
+      pub_store(rec + 6, v[3]);
+    }
+  }
+
+  if (draft_row) {
+    bool alive = arrive_and_wait(&P.rowcnt[(size_t)r * kCounterStride], G, P.status, &sh_ok);
+    if (alive) {
+      const SupStats st = combine_sup(P, r, fs.red);
+      const float lse_q2 = st.Mq * kLog2e + flog2(st.Sq);
+      const float lse_p2 = st.Mp * kLog2e + flog2(st.Sp);
+      const float D = (lse_q2 - lse_p2) * kLn2;
+      const float KL = st.Wsum / st.Sq - D;
+      const float bound = (st.BA + fmaxf(0.f, -D)) / st.Sq;
+      const float c = P.clip_c, lam = P.lambda;
+      const bool fast = !st.nonfinite && bound <= 0.999f * c;
+      if (tid == 0 && j == 0 && !(st.Mp < __builtin_inff() && st.Sp > 0.f && st.Sq > 0.f))
+        flag(P.status, ADAFLASH_FLAG_NONFINITE);
+
+      bool accept = true;
+      if constexpr (SAMPLED) {
+        const float px = fexp2((zpx - st.Mp) * kLog2e) / st.Sp;
+        const float qx = fexp2((zqx - st.Mq) * kLog2e) / st.Sq;
+        const float u = u_acc;
+        accept = u * qx < px;
+        if (tid == 0 && j == 0) {
+          pub_store(P.rowrec + (size_t)r * kRowRec + 1, accept ? 1.f : 0.f);
+          pub_store(P.rowrec + (size_t)r * kRowRec + 2, px - u * qx);
+          if (P.margins) P.margins[(size_t)b * (k + 1) + i] = px - u * qx;
+        }
+      }
+
+      cp.opaque();
+      cq.opaque();
+      const int xs = st.xstar;
+      const int xo = xs - v0;
+      const bool xs_here = xo >= 0 && xo < kChunk && ((xo % (kThreads * VEC)) / VEC) == tid;
+      const int xs_slot = xo >= 0 ? xo / (kThreads * VEC) : -1;
+      const int xs_u = xo >= 0 ? xo % VEC : -1;
+
+      // Residual mass max(0, p - q) of a rejected row (the finaliser draws from
+      // the first rejected row), accumulated inside the gradient loops.
+      const bool need_res = SAMPLED && !accept;
+      float Zpart = 0.f;
+
+      auto store_slot = [&](int s2, float (&g)[VEC]) {
+        if (xs_here && xs_slot == s2) {
+#pragma unroll
+          for (int u = 0; u < VEC; ++u)
+            if (u == xs_u) g[u] -= 1.f;
+        }
+        const int idx0 = v0 + s2 * (kThreads * VEC) + tid * VEC;
+        if constexpr (BF16) {
+          uint16_t* gr = (uint16_t*)P.grad + (size_t)n * V;
+          if constexpr (ALIGNED) {
+            if (idx0 < V) {
+              uint4 o;
+              o.x = pack_bf16x2(g[0], g[1]);
+              o.y = pack_bf16x2(g[2], g[3]);
+              o.z = pack_bf16x2(g[4], g[5]);
+              o.w = pack_bf16x2(g[6], g[7]);
+              *(uint4*)(gr + idx0) = o;
+            }
+          } else {
+#pragma unroll
+            for (int u = 0; u < VEC; ++u)
+              if (idx0 + u < V) gr[idx0 + u] = __builtin_bit_cast(uint16_t, (__bf16)g[u]);
+          }
+        } else {
+          float* gr = (float*)P.grad + (size_t)n * V;
+          if constexpr (ALIGNED) {
+            if (idx0 < V) *(float4*)(gr + idx0) = make_float4(g[0], g[1], g[2], g[3]);
+          } else {
+#pragma unroll
+            for (int u = 0; u < VEC; ++u)
+              if (idx0 + u < V) gr[idx0 + u] = g[u];
+          }
+        }
+      };
+
+      float Rrow = KL;
+      if (fast) {
+        if (SAMPLED && tid == 0) pub_store(P.part2 + ((size_t)r * G + j) * kRec2 + 2, 0.f);
+        const float c1 = 1.f - lam * KL;
+#pragma unroll
+        for (int s2 = 0; s2 < NV; ++s2) {
+          float g[VEC];
+#pragma unroll
+          for (int u = 0; u < VEC; ++u) {
+            const int e = s2 * VEC + u;
+            const float zq = cq.get(e), zp = cp.get(e);
+            const float q = fexp2(fmaf(zq, kLog2e, -lse_q2));
+            g[u] = q * fmaf(lam, (zq - zp) - D, c1);
+          }
+          if (P.grad) store_slot(s2, g);
+        }
+        if (need_res) {
+          // Separate sweep: folding it into the loop above doubles the live set.
+          cp.opaque();
+          cq.opaque();
+#pragma unroll
+          for (int e = 0; e < kElems; ++e) {
+            const float q = fexp2(fmaf(cq.get(e), kLog2e, -lse_q2));
+            Zpart += fmaxf(0.f, fexp2(fmaf(cp.get(e), kLog2e, -lse_p2)) - q);
+          }
+        }
+      } else {
+        // Exact path: clipped sums, second barrier, then the gradient (the
+        // per-entry terms are recomputed from the cached e and dz).
+        float Spart = 0.f, Rpart = 0.f;
+#pragma unroll
+        for (int e = 0; e < kElems; ++e) {
+          const float zq = cq.get(e), zp = cp.get(e);
+          const float q = fexp2(fmaf(zq, kLog2e, -lse_q2));
+          if (need_res) Zpart += fmaxf(0.f, fexp2(fmaf(zp, kLog2e, -lse_p2)) - q);
+          const float d = (zq - zp) - D;
+          const float f = q > 0.f ? q * d : 0.f;
+          const bool inU = f <= c;
+          Rpart += inU ? f : c;
+          Spart += inU ? f + q : 0.f;
+        }
+        float s3[3] = {Spart, Rpart, Zpart};
+        const int ops3[3] = {OP_SUM, OP_SUM, OP_SUM};
+        wg_reduce<3>(s3, ops3, fs.red);
+        if (tid == 0) {
+          float* rec = P.part2 + ((size_t)r * G + j) * kRec2;
+          pub_store(rec + 0, s3[0]);
+          pub_store(rec + 1, s3[1]);
+          if (SAMPLED) pub_store(rec + 2, s3[2]);
+        }
+        alive = arrive_and_wait(&P.rowcnt[(size_t)r * kCounterStride], 2 * G, P.status, &sh_ok);
+        if (alive) {
+          float sr[2] = {0.f, 0.f};
+          if (tid < G) {
+            const float* rec = P.part2 + ((size_t)r * G + tid) * kRec2;
+            sr[0] = pub_load(rec + 0);
+            sr[1] = pub_load(rec + 1);
+          }
+          const int srops[2] = {OP_SUM, OP_SUM};
+          wg_reduce<2>(sr, srops, fs.red);
+          Rrow = sr[1];
+          const float lamS = lam * sr[0];
+          cp.opaque();
+          cq.opaque();
+          if (P.grad) {
+#pragma unroll
+            for (int s2 = 0; s2 < NV; ++s2) {
+              float g[VEC];
+#pragma unroll
+              for (int u = 0; u < VEC; ++u) {
+                const int e = s2 * VEC + u;
+                const float zq = cq.get(e);
+                const float q = fexp2(fmaf(zq, kLog2e, -lse_q2));
+                const float d = (zq - cp.get(e)) - D;
+                const float f = q > 0.f ? q * d : 0.f;
+                const float sterm = f <= c ? f + q : 0.f;
+                g[u] = fmaf(-lamS, q, fmaf(lam, sterm, q));
+              }
+              store_slot(s2, g);
+            }
+          }
+        }
+      }
+      if (fast && SAMPLED) {
+        // The residual mass still has to reach the finaliser.
+        float z1[1] = {Zpart};
+        const int o1[1] = {OP_SUM};
+        wg_reduce<1>(z1, o1, fs.red);
+        if (tid == 0) pub_store(P.part2 + ((size_t)r * G + j) * kRec2 + 2, z1[0]);
+      }
+      if (alive && xs_here) {
+        // Losses, written by the thread that holds z_q[x*].
+        float zqs = 0.f;
+        const int es = xs_slot * VEC + xs_u;
+#pragma unroll
+        for (int e = 0; e < kElems; ++e)
+          if (e == es) zqs = cq.get(e);
+        if (P.loss_ce) P.loss_ce[n] = lse_q2 * kLn2 - zqs;
+        if (P.loss_rkl) P.loss_rkl[n] = Rrow;
+      }
+    }
+  }
+
+}
+
+// ----------------------------------------------------------- finalise kernel
+
+// One workgroup per request, after the row kernel: first rejection, then the
+// correction or bonus draw.
+template <bool BF16, bool ALIGNED, int VMODE>
+__global__ __launch_bounds__(kThreads) void final_kernel(KParams P) {
+  __shared__ FinShared fs;
+  finalize_request<BF16, ALIGNED, VMODE>(P, (int)blockIdx.x, fs);
+}
+
 // --------------------------------------------------------------- pack kernel
 
-// One workgroup of 1024 threads: clamp verify lengths, prefix sums, row list,
-// counter reset, status initialisation.
-__global__ __launch_bounds__(1024) void pack_kernel(const int32_t* verify_len, int B, int k, int bonus,
+// One workgroup of 1024 threads: clamp verify lengths, prefix sum of the
+// verified rows (packed row offsets), counter reset, status initialisation.
+__global__ __launch_bounds__(1024) void pack_kernel(const int32_t* verify_len, int B, int k,
                                                      int32_t* row_offsets, Workspace ws, int32_t* status) {
   __shared__ int s_scan[1024];
-  __shared__ int s_scan2[1024];
   __shared__ int s_flags;
   const int tid = threadIdx.x;
   if (tid == 0) s_flags = 0;
   __syncthreads();
-  int carry = 0, carry2 = 0;
+  int carry = 0;
   for (int base = 0; base < B; base += 1024) {
     const int b = base + tid;
     int L = 0;
@@ -878,38 +1232,24 @@ __global__ __launch_bounds__(1024) void pack_kernel(const int32_t* verify_len, i
       }
       ws.Lc[b] = L;
     }
-    const int n2 = b < B ? L + bonus : 0;
     s_scan[tid] = L;
-    s_scan2[tid] = n2;
     __syncthreads();
     // Hillis-Steele inclusive scan.
     for (int off = 1; off < 1024; off <<= 1) {
       const int a = tid >= off ? s_scan[tid - off] : 0;
-      const int a2 = tid >= off ? s_scan2[tid - off] : 0;
       __syncthreads();
       s_scan[tid] += a;
-      s_scan2[tid] += a2;
       __syncthreads();
     }
-    const int incl = s_scan[tid], incl2 = s_scan2[tid];
     if (b < B) {
-      row_offsets[b] = carry + incl - L;
-      const int start = carry2 + incl2 - n2;
-      ws.roff[b] = start;
-      for (int ii = 0; ii < n2; ++ii) {
-        ws.rowlist[start + ii] = b * (k + 1) + ii;
-        ws.rowcnt[(size_t)(start + ii) * kCounterStride] = 0;
-      }
-      ws.reqcnt[(size_t)b * kCounterStride] = 0;
+      row_offsets[b] = carry + s_scan[tid] - L;
+      for (int ii = 0; ii <= k; ++ii) ws.rowcnt[((size_t)b * (k + 1) + ii) * kCounterStride] = 0;
     }
     carry += s_scan[1023];
-    carry2 += s_scan2[1023];
     __syncthreads();
   }
   if (tid == 0) {
     row_offsets[B] = carry;
-    ws.roff[B] = carry2;
-    *ws.nrows = carry2;
     if (status) *status = s_flags;
   }
 }
@@ -920,24 +1260,39 @@ hipError_t launch_rows(const KParams& p, int grid, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <bool BF16, bool ALIGNED, int VMODE>
+hipError_t launch_sup(const KParams& p, int grid, hipStream_t st) {
+  hipLaunchKernelGGL((sup_kernel<BF16, ALIGNED, VMODE>), dim3(grid), dim3(kThreads), 0, st, p);
+  return hipGetLastError();
+}
+
+template <bool BF16, bool ALIGNED, int VMODE>
+hipError_t launch_final(const KParams& p, hipStream_t st) {
+  hipLaunchKernelGGL((final_kernel<BF16, ALIGNED, VMODE>), dim3(p.B), dim3(kThreads), 0, st, p);
+  return hipGetLastError();
+}
+
 template <bool BF16, bool ALIGNED>
 hipError_t dispatch_mode(const KParams& p, int grid, int opd, int vmode, bool t1, hipStream_t st) {
-  if (!opd) {
-    if (vmode == 1) return launch_rows<BF16, ALIGNED, false, 1, false>(p, grid, st);
-    if (vmode == 2) return launch_rows<BF16, ALIGNED, false, 2, false>(p, grid, st);
-    return hipErrorInvalidValue;
-  }
-  if (vmode == 0) return launch_rows<BF16, ALIGNED, true, 0, false>(p, grid, st);
-  if (vmode == 1) return launch_rows<BF16, ALIGNED, true, 1, false>(p, grid, st);
-  if (t1) return launch_rows<BF16, ALIGNED, true, 2, true>(p, grid, st);
-  return launch_rows<BF16, ALIGNED, true, 2, false>(p, grid, st);
+  hipError_t e;
+  if (opd && vmode == 0) e = launch_sup<BF16, ALIGNED, 0>(p, grid, st);
+  else if (opd && vmode == 1) e = launch_sup<BF16, ALIGNED, 1>(p, grid, st);
+  else if (opd && vmode == 2 && t1) e = launch_sup<BF16, ALIGNED, 2>(p, grid, st);
+  else if (opd) e = launch_rows<BF16, ALIGNED, true, 2, false>(p, grid, st);
+  else if (vmode == 1) e = launch_rows<BF16, ALIGNED, false, 1, false>(p, grid, st);
+  else if (vmode == 2) e = launch_rows<BF16, ALIGNED, false, 2, false>(p, grid, st);
+  else return hipErrorInvalidValue;
+  if (e != hipSuccess) return e;
+  if (vmode == 1) return launch_final<BF16, ALIGNED, 1>(p, st);
+  if (vmode == 2) return launch_final<BF16, ALIGNED, 2>(p, st);
+  return hipSuccess;
 }
 
 }  // namespace
 
 hipError_t launch(const LaunchArgs& a) {
   const int bonus = a.verify ? 1 : 0;
-  hipLaunchKernelGGL(pack_kernel, dim3(1), dim3(1024), 0, a.stream, a.verify_len, a.B, a.k, bonus,
+  hipLaunchKernelGGL(pack_kernel, dim3(1), dim3(1024), 0, a.stream, a.verify_len, a.B, a.k,
                      a.row_offsets, a.ws, a.status);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.B == 0) return e;
@@ -955,12 +1310,8 @@ hipError_t launch(const LaunchArgs& a) {
   p.loss_rkl = a.loss_rkl;
   p.grad = a.grad;
   p.status = a.status;
-  p.nrows = a.ws.nrows;
   p.Lc = a.ws.Lc;
-  p.roff = a.ws.roff;
-  p.rowlist = a.ws.rowlist;
   p.rowcnt = a.ws.rowcnt;
-  p.reqcnt = a.ws.reqcnt;
   p.part1 = a.ws.part1;
   p.part2 = a.ws.part2;
   p.rowrec = a.ws.rowrec;
