@@ -25,6 +25,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published peak
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "sup_kernel_c128_fused_hbm_bytes.md")
+KERNEL_SOURCE = os.path.join(ROOT, "diffusion_drafter_verification_amd", "csrc", "adaflash_kernels.hip")
 METRIC = "verified draft positions/sec + achieved HBM GB/s (B=128, k=16, V=151936)"
 
 
@@ -74,6 +76,21 @@ def copy_probe():
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes": n, "calls": 5}))
+
+
+def measured_traffic(mode):
+    """HBM bytes per launch of the fused kernel from the committed rocprofv3
+    counter summary, or None when the kernel source changed since then."""
+    import hashlib
+    import re
+    if mode != "fused" or not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    m = re.search(r"```json\n(.*?)\n```", open(TRAFFIC_PROFILE).read(), re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    return rec["traffic_bytes_per_launch"] if rec.get("kernel_source_sha256") == sha else None
 
 
 def cpu_baseline(batch, mode, clip, lam, budget_s):
@@ -220,7 +237,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": measured_traffic(args.mode),
         },
         "kernel_ms_avg": avg_dur * 1e3,
         "kernel_ms_p10_p50_p90": [float(np.percentile(durs, q) * 1e3) for q in (10, 50, 90)],
