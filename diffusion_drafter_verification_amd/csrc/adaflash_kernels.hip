@@ -41,6 +41,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "adaflash_internal.h"
 
 #define ADAFLASH_FLAG_BAD_VERIFY_LEN 1
@@ -95,9 +97,12 @@ __device__ __forceinline__ float dpp_f(float v) {
   return __int_as_float(dpp_i<CTRL>(__float_as_int(v)));
 }
 
-// Butterfly inside each 16-lane row (xor 1, xor 2, mirror 8, mirror 16): every
-// lane of a row ends with the bit-identical row result; the four row results
-// are then combined in a fixed order.  Must be called with all lanes active.
+// Wave reduction: a butterfly inside each 16-lane row (xor 1, xor 2, mirror 8,
+// mirror 16) leaves every lane of a row with the row result; two row
+// broadcasts (lane 15 into rows 1 and 3, then lane 31 into rows 2 and 3)
+// accumulate the four rows into lane 63, which is read as a uniform value.
+// The combination order is fixed, so the result is deterministic.  Must be
+// called with all lanes active.
 enum { OP_SUM = 0, OP_MAX = 1, OP_MINI = 2 };
 
 template <int OP>
@@ -108,16 +113,27 @@ __device__ __forceinline__ float op2(float a, float b) {
 }
 
 template <int OP>
+__device__ __forceinline__ float op_identity() {
+  if constexpr (OP == OP_SUM) return 0.f;
+  if constexpr (OP == OP_MAX) return -__builtin_inff();
+  return __int_as_float(0x7fffffff);
+}
+
+// DPP move restricted to the rows in ROWMASK; other rows receive `old`.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ float dpp_rows(float v, float old) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL, ROWMASK, 0xF, false));
+}
+
+template <int OP>
 __device__ __forceinline__ float wave_reduce(float v) {
   v = op2<OP>(v, dpp_f<0xB1>(v));   // quad_perm [1,0,3,2]
   v = op2<OP>(v, dpp_f<0x4E>(v));   // quad_perm [2,3,0,1]
   v = op2<OP>(v, dpp_f<0x141>(v));  // row_half_mirror
   v = op2<OP>(v, dpp_f<0x140>(v));  // row_mirror
-  float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-  float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-  float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-  float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-  return op2<OP>(op2<OP>(r0, r1), op2<OP>(r2, r3));
+  v = op2<OP>(v, dpp_rows<0x142, 0xA>(v, op_identity<OP>()));  // row_bcast:15
+  v = op2<OP>(v, dpp_rows<0x143, 0xC>(v, op_identity<OP>()));  // row_bcast:31
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 // Workgroup reduction of N values with per-value operators; every thread gets
@@ -265,6 +281,21 @@ __device__ __forceinline__ void load_chunk(Chunk<BF16>& c, const void* row, int 
   constexpr int VEC = Chunk<BF16>::VEC;
   constexpr int NV = kElems / VEC;
   const uint32_t ninf = BF16 ? 0xff7fff7fu : 0xff7fffffu;  // -max finite
+  if constexpr (ALIGNED) {
+    if (v0 + kChunk <= V) {  // whole chunk inside the row: no per-slot guards
+#pragma unroll
+      for (int s = 0; s < NV; ++s) {
+        const int idx0 = v0 + s * (kThreads * VEC) + (int)threadIdx.x * VEC;
+        const uint4 q = BF16 ? *(const uint4*)((const uint16_t*)row + idx0)
+                             : *(const uint4*)((const float*)row + idx0);
+        c.w[s * 4 + 0] = q.x;
+        c.w[s * 4 + 1] = q.y;
+        c.w[s * 4 + 2] = q.z;
+        c.w[s * 4 + 3] = q.w;
+      }
+      return;
+    }
+  }
 #pragma unroll
   for (int s = 0; s < NV; ++s) {
     const int idx0 = v0 + s * (kThreads * VEC) + (int)threadIdx.x * VEC;
@@ -878,11 +909,47 @@ struct SupStats {
   int xstar, nonfinite;
 };
 
-__device__ SupStats combine_sup(const KParams& P, int r, float* red) {
-  float mp = neg_inf(), mq = neg_inf(), sp = 0.f, sq = 0.f, w = 0.f, a = neg_inf();
-  int idx = kIntMax;
-  if ((int)threadIdx.x < P.G) {
-    const float* rec = P.part1 + ((size_t)r * P.G + threadIdx.x) * kRec1;
+// Combines the G chunk records of row r (identical in every workgroup of the
+// row).  With G <= 64 wave 0 alone reduces them (lane j holds chunk j) and
+// hands the results to the other waves through fs.f; otherwise every wave
+// takes part.
+__device__ SupStats combine_sup(const KParams& P, int r, FinShared& fs) {
+  const int tid = threadIdx.x;
+  const int G = P.G;
+  auto reduce = [&](float mp, float mq, float sp, float sq, float w, float a, int idx, bool valid,
+                    float (&m)[2], float (&v)[6], bool whole_group) {
+    if (whole_group) {
+      m[0] = mp;
+      m[1] = mq;
+      const int mops[2] = {OP_MAX, OP_MAX};
+      wg_reduce<2>(m, mops, fs.red);
+    } else {
+      m[0] = wave_reduce<OP_MAX>(mp);
+      m[1] = wave_reduce<OP_MAX>(mq);
+    }
+    const float fp = mp == neg_inf() ? 0.f : fexp2((mp - m[0]) * kLog2e);
+    const float fq = mq == neg_inf() ? 0.f : fexp2((mq - m[1]) * kLog2e);
+    const bool fin = !valid || (__builtin_isfinite(w) && !__builtin_isnan(a) && a < __builtin_inff());
+    v[0] = sp * fp;
+    v[1] = sq * fq;
+    v[2] = fq > 0.f ? w * fq : 0.f;
+    v[3] = fq > 0.f ? fq * a : neg_inf();
+    v[4] = __int_as_float(mp == m[0] ? idx : kIntMax);
+    v[5] = __int_as_float(fin ? 0 : 1);  // OP_MAX on these two bit patterns is an integer max
+    if (whole_group) {
+      const int ops[6] = {OP_SUM, OP_SUM, OP_SUM, OP_MAX, OP_MINI, OP_MAX};
+      wg_reduce<6>(v, ops, fs.red);
+    } else {
+      v[0] = wave_reduce<OP_SUM>(v[0]);
+      v[1] = wave_reduce<OP_SUM>(v[1]);
+      v[2] = wave_reduce<OP_SUM>(v[2]);
+      v[3] = wave_reduce<OP_MAX>(v[3]);
+      v[4] = wave_reduce<OP_MINI>(v[4]);
+      v[5] = wave_reduce<OP_MAX>(v[5]);
+    }
+  };
+  auto load = [&](int c, float& mp, float& mq, float& sp, float& sq, float& w, float& a, int& idx) {
+    const float* rec = P.part1 + ((size_t)r * G + c) * kRec1;
     mp = pub_load(rec + 0);
     idx = __float_as_int(pub_load(rec + 1));
     sp = pub_load(rec + 2);
@@ -890,18 +957,32 @@ __device__ SupStats combine_sup(const KParams& P, int r, float* red) {
     mq = pub_load(rec + 4);
     sq = pub_load(rec + 5);
     a = pub_load(rec + 6);
+  };
+  float m[2], v[6];
+  if (G <= 64) {
+    if (tid < 64) {
+      float mp = neg_inf(), mq = neg_inf(), sp = 0.f, sq = 0.f, w = 0.f, a = neg_inf();
+      int idx = kIntMax;
+      if (tid < G) load(tid, mp, mq, sp, sq, w, a, idx);
+      reduce(mp, mq, sp, sq, w, a, idx, tid < G, m, v, false);
+      if (tid == 0) {
+        fs.f[0] = m[0];
+        fs.f[1] = m[1];
+#pragma unroll
+        for (int q = 0; q < 6; ++q) fs.f[2 + q] = v[q];
+      }
+    }
+    __syncthreads();
+    m[0] = fs.f[0];
+    m[1] = fs.f[1];
+#pragma unroll
+    for (int q = 0; q < 6; ++q) v[q] = fs.f[2 + q];
+  } else {
+    float mp = neg_inf(), mq = neg_inf(), sp = 0.f, sq = 0.f, w = 0.f, a = neg_inf();
+    int idx = kIntMax;
+    if (tid < G) load(tid, mp, mq, sp, sq, w, a, idx);
+    reduce(mp, mq, sp, sq, w, a, idx, tid < G, m, v, true);
   }
-  float m[2] = {mp, mq};
-  const int mops[2] = {OP_MAX, OP_MAX};
-  wg_reduce<2>(m, mops, red);
-  const float fp = mp == neg_inf() ? 0.f : fexp2((mp - m[0]) * kLog2e);
-  const float fq = mq == neg_inf() ? 0.f : fexp2((mq - m[1]) * kLog2e);
-  const bool fin = (int)threadIdx.x >= P.G || (__builtin_isfinite(w) && !__builtin_isnan(a) && a < __builtin_inff());
-  float v[6] = {sp * fp, sq * fq, fq > 0.f ? w * fq : 0.f, fq > 0.f ? fq * a : neg_inf(),
-                __int_as_float(mp == m[0] ? idx : kIntMax), __int_as_float(fin ? 0 : 1)};
-  const int ops[6] = {OP_SUM, OP_SUM, OP_SUM, OP_MAX, OP_MINI, OP_MAX};
-  // OP_MAX on the flag's bit pattern is an integer max for these two values.
-  wg_reduce<6>(v, ops, red);
   SupStats s;
   s.Mp = m[0];
   s.Mq = m[1];
@@ -914,6 +995,20 @@ __device__ SupStats combine_sup(const KParams& P, int r, float* red) {
   return s;
 }
 
+// Gradient value of the fast path (no entry clipped) and of the exact path.
+__device__ __forceinline__ float grad_fast(float zq, float zp, float lse_q2, float D, float lam, float c1) {
+  const float q = fexp2(fmaf(zq, kLog2e, -lse_q2));
+  return q * fmaf(lam, (zq - zp) - D, c1);
+}
+__device__ __forceinline__ float grad_exact(float zq, float zp, float lse_q2, float D, float lam, float lamS,
+                                            float c) {
+  const float q = fexp2(fmaf(zq, kLog2e, -lse_q2));
+  const float dd = (zq - zp) - D;
+  const float f = q > 0.f ? q * dd : 0.f;
+  const float sterm = f <= c ? f + q : 0.f;
+  return fmaf(-lamS, q, fmaf(lam, sterm, q));
+}
+
 template <bool BF16, bool ALIGNED, int VMODE>
 __global__ __launch_bounds__(kThreads) void sup_kernel(KParams P) {
   constexpr bool SAMPLED = VMODE == 2, VERIFY = VMODE != 0;
@@ -923,6 +1018,7 @@ __global__ __launch_bounds__(kThreads) void sup_kernel(KParams P) {
   __shared__ int sh_ok;
 
   const int tid = threadIdx.x;
+  const int wave = tid >> 6;
   const int G = P.G;
   const int k = P.k, V = P.V;
   // Workgroup -> (request b, position i, chunk j); row slot r = b*(k+1) + i.
@@ -979,11 +1075,15 @@ __global__ __launch_bounds__(kThreads) void sup_kernel(KParams P) {
     const int ops[2] = {OP_MAX, OP_MAX};
     wg_reduce<2>(Mw, ops, fs.red);
   }
+  // Lowest index of this chunk holding the maximum of z_p (only threads that
+  // hold it search; the entry number is tracked and converted once).
   int cand = kIntMax;
   if (mp == Mw[0]) {
+    int ce = 0;
 #pragma unroll
     for (int e = kElems - 1; e >= 0; --e)
-      if (cp.get(e) == Mw[0]) cand = entry_index<BF16>(v0, e);
+      if (cp.get(e) == Mw[0]) ce = e;
+    cand = v0 + (ce / VEC) * (kThreads * VEC) + tid * VEC + (ce % VEC);
   }
   float sp = 0.f, sq = 0.f, W = 0.f, Amax = neg_inf();
   const float ap = Mw[0] == neg_inf() ? 0.f : -Mw[0] * kLog2e;
@@ -1018,185 +1118,183 @@ __global__ __launch_bounds__(kThreads) void sup_kernel(KParams P) {
       pub_store(rec + 6, v[3]);
     }
   }
+  if (!draft_row) return;
 
-  if (draft_row) {
-    bool alive = arrive_and_wait(&P.rowcnt[(size_t)r * kCounterStride], G, P.status, &sh_ok);
-    if (alive) {
-      const SupStats st = combine_sup(P, r, fs.red);
-      const float lse_q2 = st.Mq * kLog2e + flog2(st.Sq);
-      const float lse_p2 = st.Mp * kLog2e + flog2(st.Sp);
-      const float D = (lse_q2 - lse_p2) * kLn2;
-      const float KL = st.Wsum / st.Sq - D;
-      const float bound = (st.BA + fmaxf(0.f, -D)) / st.Sq;
-      const float c = P.clip_c, lam = P.lambda;
-      const bool fast = !st.nonfinite && bound <= 0.999f * c;
-      if (tid == 0 && j == 0 && !(st.Mp < __builtin_inff() && st.Sp > 0.f && st.Sq > 0.f))
-        flag(P.status, ADAFLASH_FLAG_NONFINITE);
+  bool alive = arrive_and_wait(&P.rowcnt[(size_t)r * kCounterStride], G, P.status, &sh_ok);
+  if (!alive) return;
+  // Sampled verification: the finaliser draws from the residual of the first
+  // rejected row only, so a row behind a row already known to be rejected
+  // skips the residual.  Wave 1 reads the earlier rows' accept flags (reset
+  // to "unknown" by the pack kernel) while wave 0 combines the records.
+  if (SAMPLED && wave == 1) {
+    const int l = tid - 64;
+    const bool rej = l < i && pub_load(P.rowrec + (size_t)(r - i + l) * kRowRec + 1) == 0.f;
+    const unsigned long long any = __ballot(rej);
+    if (l == 0) fs.i[0] = any != 0ull;
+  }
+  const SupStats st = combine_sup(P, r, fs);
+  const bool earlier_rejected = SAMPLED && fs.i[0] != 0;
+  const float lse_q2 = st.Mq * kLog2e + flog2(st.Sq);
+  const float lse_p2 = st.Mp * kLog2e + flog2(st.Sp);
+  const float D = (lse_q2 - lse_p2) * kLn2;
+  const float KL = st.Wsum / st.Sq - D;
+  const float bound = (st.BA + fmaxf(0.f, -D)) / st.Sq;
+  const float c = P.clip_c, lam = P.lambda;
+  const bool fast = !st.nonfinite && bound <= 0.999f * c;
+  if (tid == 0 && j == 0 && !(st.Mp < __builtin_inff() && st.Sp > 0.f && st.Sq > 0.f))
+    flag(P.status, ADAFLASH_FLAG_NONFINITE);
 
-      bool accept = true;
-      if constexpr (SAMPLED) {
-        const float px = fexp2((zpx - st.Mp) * kLog2e) / st.Sp;
-        const float qx = fexp2((zqx - st.Mq) * kLog2e) / st.Sq;
-        const float u = u_acc;
-        accept = u * qx < px;
-        if (tid == 0 && j == 0) {
-          pub_store(P.rowrec + (size_t)r * kRowRec + 1, accept ? 1.f : 0.f);
-          pub_store(P.rowrec + (size_t)r * kRowRec + 2, px - u * qx);
-          if (P.margins) P.margins[(size_t)b * (k + 1) + i] = px - u * qx;
-        }
-      }
-
-      cp.opaque();
-      cq.opaque();
-      const int xs = st.xstar;
-      const int xo = xs - v0;
-      const bool xs_here = xo >= 0 && xo < kChunk && ((xo % (kThreads * VEC)) / VEC) == tid;
-      const int xs_slot = xo >= 0 ? xo / (kThreads * VEC) : -1;
-      const int xs_u = xo >= 0 ? xo % VEC : -1;
-
-      // Residual mass max(0, p - q) of a rejected row (the finaliser draws from
-      // the first rejected row), accumulated inside the gradient loops.
-      const bool need_res = SAMPLED && !accept;
-      float Zpart = 0.f;
-
-      auto store_slot = [&](int s2, float (&g)[VEC]) {
-        if (xs_here && xs_slot == s2) {
-#pragma unroll
-          for (int u = 0; u < VEC; ++u)
-            if (u == xs_u) g[u] -= 1.f;
-        }
-        const int idx0 = v0 + s2 * (kThreads * VEC) + tid * VEC;
-        if constexpr (BF16) {
-          uint16_t* gr = (uint16_t*)P.grad + (size_t)n * V;
-          if constexpr (ALIGNED) {
-            if (idx0 < V) {
-              uint4 o;
-              o.x = pack_bf16x2(g[0], g[1]);
-              o.y = pack_bf16x2(g[2], g[3]);
-              o.z = pack_bf16x2(g[4], g[5]);
-              o.w = pack_bf16x2(g[6], g[7]);
-              *(uint4*)(gr + idx0) = o;
-            }
-          } else {
-#pragma unroll
-            for (int u = 0; u < VEC; ++u)
-              if (idx0 + u < V) gr[idx0 + u] = __builtin_bit_cast(uint16_t, (__bf16)g[u]);
-          }
-        } else {
-          float* gr = (float*)P.grad + (size_t)n * V;
-          if constexpr (ALIGNED) {
-            if (idx0 < V) *(float4*)(gr + idx0) = make_float4(g[0], g[1], g[2], g[3]);
-          } else {
-#pragma unroll
-            for (int u = 0; u < VEC; ++u)
-              if (idx0 + u < V) gr[idx0 + u] = g[u];
-          }
-        }
-      };
-
-      float Rrow = KL;
-      if (fast) {
-        if (SAMPLED && tid == 0) pub_store(P.part2 + ((size_t)r * G + j) * kRec2 + 2, 0.f);
-        const float c1 = 1.f - lam * KL;
-#pragma unroll
-        for (int s2 = 0; s2 < NV; ++s2) {
-          float g[VEC];
-#pragma unroll
-          for (int u = 0; u < VEC; ++u) {
-            const int e = s2 * VEC + u;
-            const float zq = cq.get(e), zp = cp.get(e);
-            const float q = fexp2(fmaf(zq, kLog2e, -lse_q2));
-            g[u] = q * fmaf(lam, (zq - zp) - D, c1);
-          }
-          if (P.grad) store_slot(s2, g);
-        }
-        if (need_res) {
-          // Separate sweep: folding it into the loop above doubles the live set.
-          cp.opaque();
-          cq.opaque();
-#pragma unroll
-          for (int e = 0; e < kElems; ++e) {
-            const float q = fexp2(fmaf(cq.get(e), kLog2e, -lse_q2));
-            Zpart += fmaxf(0.f, fexp2(fmaf(cp.get(e), kLog2e, -lse_p2)) - q);
-          }
-        }
-      } else {
-        // Exact path: clipped sums, second barrier, then the gradient (the
-        // per-entry terms are recomputed from the cached e and dz).
-        float Spart = 0.f, Rpart = 0.f;
-#pragma unroll
-        for (int e = 0; e < kElems; ++e) {
-          const float zq = cq.get(e), zp = cp.get(e);
-          const float q = fexp2(fmaf(zq, kLog2e, -lse_q2));
-          if (need_res) Zpart += fmaxf(0.f, fexp2(fmaf(zp, kLog2e, -lse_p2)) - q);
-          const float d = (zq - zp) - D;
-          const float f = q > 0.f ? q * d : 0.f;
-          const bool inU = f <= c;
-          Rpart += inU ? f : c;
-          Spart += inU ? f + q : 0.f;
-        }
-        float s3[3] = {Spart, Rpart, Zpart};
-        const int ops3[3] = {OP_SUM, OP_SUM, OP_SUM};
-        wg_reduce<3>(s3, ops3, fs.red);
-        if (tid == 0) {
-          float* rec = P.part2 + ((size_t)r * G + j) * kRec2;
-          pub_store(rec + 0, s3[0]);
-          pub_store(rec + 1, s3[1]);
-          if (SAMPLED) pub_store(rec + 2, s3[2]);
-        }
-        alive = arrive_and_wait(&P.rowcnt[(size_t)r * kCounterStride], 2 * G, P.status, &sh_ok);
-        if (alive) {
-          float sr[2] = {0.f, 0.f};
-          if (tid < G) {
-            const float* rec = P.part2 + ((size_t)r * G + tid) * kRec2;
-            sr[0] = pub_load(rec + 0);
-            sr[1] = pub_load(rec + 1);
-          }
-          const int srops[2] = {OP_SUM, OP_SUM};
-          wg_reduce<2>(sr, srops, fs.red);
-          Rrow = sr[1];
-          const float lamS = lam * sr[0];
-          cp.opaque();
-          cq.opaque();
-          if (P.grad) {
-#pragma unroll
-            for (int s2 = 0; s2 < NV; ++s2) {
-              float g[VEC];
-#pragma unroll
-              for (int u = 0; u < VEC; ++u) {
-                const int e = s2 * VEC + u;
-                const float zq = cq.get(e);
-                const float q = fexp2(fmaf(zq, kLog2e, -lse_q2));
-                const float d = (zq - cp.get(e)) - D;
-                const float f = q > 0.f ? q * d : 0.f;
-                const float sterm = f <= c ? f + q : 0.f;
-                g[u] = fmaf(-lamS, q, fmaf(lam, sterm, q));
-              }
-              store_slot(s2, g);
-            }
-          }
-        }
-      }
-      if (fast && SAMPLED) {
-        // The residual mass still has to reach the finaliser.
-        float z1[1] = {Zpart};
-        const int o1[1] = {OP_SUM};
-        wg_reduce<1>(z1, o1, fs.red);
-        if (tid == 0) pub_store(P.part2 + ((size_t)r * G + j) * kRec2 + 2, z1[0]);
-      }
-      if (alive && xs_here) {
-        // Losses, written by the thread that holds z_q[x*].
-        float zqs = 0.f;
-        const int es = xs_slot * VEC + xs_u;
-#pragma unroll
-        for (int e = 0; e < kElems; ++e)
-          if (e == es) zqs = cq.get(e);
-        if (P.loss_ce) P.loss_ce[n] = lse_q2 * kLn2 - zqs;
-        if (P.loss_rkl) P.loss_rkl[n] = Rrow;
-      }
+  bool accept = true;
+  if constexpr (SAMPLED) {
+    const float px = fexp2((zpx - st.Mp) * kLog2e) * __builtin_amdgcn_rcpf(st.Sp);
+    const float qx = fexp2((zqx - st.Mq) * kLog2e) * __builtin_amdgcn_rcpf(st.Sq);
+    const float u = u_acc;
+    accept = u * qx < px;
+    if (tid == 0 && j == 0) {
+      pub_store(P.rowrec + (size_t)r * kRowRec + 1, accept ? 1.f : 0.f);
+      pub_store(P.rowrec + (size_t)r * kRowRec + 2, px - u * qx);
+      if (P.margins) P.margins[(size_t)b * (k + 1) + i] = px - u * qx;
     }
   }
 
+  cp.opaque();
+  cq.opaque();
+  const int xs = st.xstar;
+  const int xo = xs - v0;
+  const bool xs_here = xo >= 0 && xo < kChunk && ((xo % (kThreads * VEC)) / VEC) == tid;
+  // The thread holding x* reads z_q[x*] now (z_p[x*] is the row maximum); its
+  // gradient entry is rewritten after the sweep with the one-hot term.
+  float zqs = 0.f;
+  if (xs_here) zqs = load_logit<BF16>(drow, xs);
+
+  // Residual mass max(0, p - q) of a rejected row.
+  const bool need_res = SAMPLED && !accept && !earlier_rejected;
+  float Zpart = 0.f;
+
+  auto store_slot = [&](int s2, const float (&g)[VEC]) {
+    const int idx0 = v0 + s2 * (kThreads * VEC) + tid * VEC;
+    if constexpr (BF16) {
+      uint16_t* gr = (uint16_t*)P.grad + (size_t)n * V;
+      if constexpr (ALIGNED) {
+        if (idx0 < V) {
+          uint4 o;
+          o.x = pack_bf16x2(g[0], g[1]);
+          o.y = pack_bf16x2(g[2], g[3]);
+          o.z = pack_bf16x2(g[4], g[5]);
+          o.w = pack_bf16x2(g[6], g[7]);
+          *(uint4*)(gr + idx0) = o;
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < VEC; ++u)
+          if (idx0 + u < V) gr[idx0 + u] = __builtin_bit_cast(uint16_t, (__bf16)g[u]);
+      }
+    } else {
+      float* gr = (float*)P.grad + (size_t)n * V;
+      if constexpr (ALIGNED) {
+        if (idx0 < V) *(float4*)(gr + idx0) = make_float4(g[0], g[1], g[2], g[3]);
+      } else {
+#pragma unroll
+        for (int u = 0; u < VEC; ++u)
+          if (idx0 + u < V) gr[idx0 + u] = g[u];
+      }
+    }
+  };
+  auto store_one = [&](int v, float g) {
+    if constexpr (BF16) ((uint16_t*)P.grad)[(size_t)n * V + v] = __builtin_bit_cast(uint16_t, (__bf16)g);
+    else ((float*)P.grad)[(size_t)n * V + v] = g;
+  };
+
+  float Rrow = KL;
+  float gstar = 0.f;
+  if (fast) {
+    const float c1 = 1.f - lam * KL;
+    // The residual sweep shares the gradient's unpacked logits and q.
+    auto sweep = [&](auto with_res) {
+#pragma unroll
+      for (int s2 = 0; s2 < NV; ++s2) {
+        float g[VEC];
+#pragma unroll
+        for (int u = 0; u < VEC; ++u) {
+          const int e = s2 * VEC + u;
+          const float zq = cq.get(e), zp = cp.get(e);
+          const float q = fexp2(fmaf(zq, kLog2e, -lse_q2));
+          g[u] = q * fmaf(lam, (zq - zp) - D, c1);
+          if constexpr (decltype(with_res)::value)
+            Zpart += fmaxf(0.f, fexp2(fmaf(zp, kLog2e, -lse_p2)) - q);
+        }
+        if (P.grad) store_slot(s2, g);
+      }
+    };
+    if (need_res) sweep(std::true_type{});
+    else if (P.grad) sweep(std::false_type{});
+    gstar = grad_fast(zqs, st.Mp, lse_q2, D, lam, c1) - 1.f;
+  } else {
+    // Exact path: clipped sums, second barrier, then the gradient (the
+    // per-entry terms are recomputed from the packed logits).
+    float Spart = 0.f, Rpart = 0.f;
+#pragma unroll
+    for (int e = 0; e < kElems; ++e) {
+      const float zq = cq.get(e), zp = cp.get(e);
+      const float q = fexp2(fmaf(zq, kLog2e, -lse_q2));
+      if (need_res) Zpart += fmaxf(0.f, fexp2(fmaf(zp, kLog2e, -lse_p2)) - q);
+      const float dd = (zq - zp) - D;
+      const float f = q > 0.f ? q * dd : 0.f;
+      const bool inU = f <= c;
+      Rpart += inU ? f : c;
+      Spart += inU ? f + q : 0.f;
+    }
+    float s3[3] = {Spart, Rpart, Zpart};
+    const int ops3[3] = {OP_SUM, OP_SUM, OP_SUM};
+    wg_reduce<3>(s3, ops3, fs.red);
+    if (tid == 0) {
+      float* rec = P.part2 + ((size_t)r * G + j) * kRec2;
+      pub_store(rec + 0, s3[0]);
+      pub_store(rec + 1, s3[1]);
+      if (SAMPLED) pub_store(rec + 2, s3[2]);
+    }
+    alive = arrive_and_wait(&P.rowcnt[(size_t)r * kCounterStride], 2 * G, P.status, &sh_ok);
+    if (!alive) return;
+    float sr[2] = {0.f, 0.f};
+    if (tid < G) {
+      const float* rec = P.part2 + ((size_t)r * G + tid) * kRec2;
+      sr[0] = pub_load(rec + 0);
+      sr[1] = pub_load(rec + 1);
+    }
+    const int srops[2] = {OP_SUM, OP_SUM};
+    wg_reduce<2>(sr, srops, fs.red);
+    Rrow = sr[1];
+    const float lamS = lam * sr[0];
+    cp.opaque();
+    cq.opaque();
+    if (P.grad) {
+#pragma unroll
+      for (int s2 = 0; s2 < NV; ++s2) {
+        float g[VEC];
+#pragma unroll
+        for (int u = 0; u < VEC; ++u) {
+          const int e = s2 * VEC + u;
+          g[u] = grad_exact(cq.get(e), cp.get(e), lse_q2, D, lam, lamS, c);
+        }
+        store_slot(s2, g);
+      }
+    }
+    gstar = grad_exact(zqs, st.Mp, lse_q2, D, lam, lamS, c) - 1.f;
+  }
+  if (fast && need_res) {
+    // The residual mass of this chunk goes to the finaliser.
+    float z1[1] = {Zpart};
+    const int o1[1] = {OP_SUM};
+    wg_reduce<1>(z1, o1, fs.red);
+    if (tid == 0) pub_store(P.part2 + ((size_t)r * G + j) * kRec2 + 2, z1[0]);
+  }
+  if (xs_here) {
+    // One-hot term of the hard-label cross entropy and the losses, by the
+    // thread that holds x* (its slot store above is overwritten).
+    if (P.grad) store_one(xs, gstar);
+    if (P.loss_ce) P.loss_ce[n] = lse_q2 * kLn2 - zqs;
+    if (P.loss_rkl) P.loss_rkl[n] = Rrow;
+  }
 }
 
 // ----------------------------------------------------------- finalise kernel
@@ -1243,7 +1341,10 @@ __global__ __launch_bounds__(1024) void pack_kernel(const int32_t* verify_len, i
     }
     if (b < B) {
       row_offsets[b] = carry + s_scan[tid] - L;
-      for (int ii = 0; ii <= k; ++ii) ws.rowcnt[((size_t)b * (k + 1) + ii) * kCounterStride] = 0;
+      for (int ii = 0; ii <= k; ++ii) {
+        ws.rowcnt[((size_t)b * (k + 1) + ii) * kCounterStride] = 0;
+        ws.rowrec[((size_t)b * (k + 1) + ii) * kRowRec + 1] = 2.f;  // accept flag: not yet known
+      }
     }
     carry += s_scan[1023];
     __syncthreads();
