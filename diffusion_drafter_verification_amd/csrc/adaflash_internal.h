@@ -10,7 +10,10 @@ namespace adaflash {
 
 // Workgroup size and elements of each logit row a thread keeps in registers.
 constexpr int kThreads = 256;
-constexpr int kElems = 32;
+#ifndef ADAFLASH_ELEMS
+#define ADAFLASH_ELEMS 32  // entries of a row per thread (tuning: 32 or 64)
+#endif
+constexpr int kElems = ADAFLASH_ELEMS;
 constexpr int kChunk = kThreads * kElems;  // elements of one row per workgroup
 
 inline int num_chunks(int V) { return (V + kChunk - 1) / kChunk; }

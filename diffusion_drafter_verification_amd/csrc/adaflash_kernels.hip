@@ -103,21 +103,28 @@ __device__ __forceinline__ float dpp_f(float v) {
 // accumulate the four rows into lane 63, which is read as a uniform value.
 // The combination order is fixed, so the result is deterministic.  Must be
 // called with all lanes active.
-enum { OP_SUM = 0, OP_MAX = 1, OP_MINI = 2 };
+enum { OP_SUM = 0, OP_MAX = 1, OP_MINI = 2, OP_MAXI = 3 };
 
 template <int OP>
 __device__ __forceinline__ float op2(float a, float b) {
   if constexpr (OP == OP_SUM) return a + b;
   if constexpr (OP == OP_MAX) return fmaxf(a, b);
+  if constexpr (OP == OP_MAXI) return __int_as_float(max(__float_as_int(a), __float_as_int(b)));
   return __int_as_float(min(__float_as_int(a), __float_as_int(b)));
 }
 
 template <int OP>
 __device__ __forceinline__ float op_identity() {
-  if constexpr (OP == OP_SUM) return 0.f;
+  if constexpr (OP == OP_SUM) return -0.f;  // exact identity of addition, also for -0
   if constexpr (OP == OP_MAX) return -__builtin_inff();
+  if constexpr (OP == OP_MAXI) return __int_as_float((int)0x80000000);
   return __int_as_float(0x7fffffff);
 }
+
+// Order-preserving map of float bit patterns to signed integers (and back:
+// the map is its own inverse).  A float maximum becomes an integer maximum,
+// which needs no NaN canonicalisation.  Only used where no operand is NaN.
+__device__ __forceinline__ int max_key(int x) { return x ^ ((x >> 31) & 0x7fffffff); }
 
 // DPP move restricted to the rows in ROWMASK; other rows receive `old`.
 template <int CTRL, int ROWMASK>
@@ -127,6 +134,11 @@ __device__ __forceinline__ float dpp_rows(float v, float old) {
 
 template <int OP>
 __device__ __forceinline__ float wave_reduce(float v) {
+  if constexpr (OP == OP_MAX) {
+    // Maxima of finite values or -inf: reduced as integer keys.
+    const float k = __int_as_float(max_key(__float_as_int(v)));
+    return __int_as_float(max_key(__float_as_int(wave_reduce<OP_MAXI>(k))));
+  }
   v = op2<OP>(v, dpp_f<0xB1>(v));   // quad_perm [1,0,3,2]
   v = op2<OP>(v, dpp_f<0x4E>(v));   // quad_perm [2,3,0,1]
   v = op2<OP>(v, dpp_f<0x141>(v));  // row_half_mirror
@@ -398,7 +410,7 @@ __device__ RowStats combine_part1(const KParams& P, int r, float kT, float* red)
 
 struct FinShared {
   float red[kWaves * 8];
-  float f[8];
+  float f[12];
   int i[8];
 };
 
@@ -907,13 +919,23 @@ __global__ __launch_bounds__(kThreads) void row_kernel(KParams P) {
 struct SupStats {
   float Mp, Mq, Sp, Sq, Wsum, BA;
   int xstar, nonfinite;
+  float margin;  // p(x) - u q(x) of the accept test (sampled verification)
 };
+
+// Accept test of sampled verification at T = 1: u q(x) < p(x).
+__device__ __forceinline__ float accept_margin(float zpx, float zqx, float u, float Mp, float Mq, float Sp,
+                                              float Sq) {
+  const float px = fexp2((zpx - Mp) * kLog2e) * __builtin_amdgcn_rcpf(Sp);
+  const float qx = fexp2((zqx - Mq) * kLog2e) * __builtin_amdgcn_rcpf(Sq);
+  return px - u * qx;
+}
 
 // Combines the G chunk records of row r (identical in every workgroup of the
 // row).  With G <= 64 wave 0 alone reduces them (lane j holds chunk j) and
 // hands the results to the other waves through fs.f; otherwise every wave
 // takes part.
-__device__ SupStats combine_sup(const KParams& P, int r, FinShared& fs) {
+template <bool SAMPLED>
+__device__ SupStats combine_sup(const KParams& P, int r, FinShared& fs, float zpx, float zqx, float u) {
   const int tid = threadIdx.x;
   const int G = P.G;
   auto reduce = [&](float mp, float mq, float sp, float sq, float w, float a, int idx, bool valid,
@@ -970,6 +992,7 @@ __device__ SupStats combine_sup(const KParams& P, int r, FinShared& fs) {
         fs.f[1] = m[1];
 #pragma unroll
         for (int q = 0; q < 6; ++q) fs.f[2 + q] = v[q];
+        if (SAMPLED) fs.f[8] = accept_margin(zpx, zqx, u, m[0], m[1], v[0], v[1]);
       }
     }
     __syncthreads();
@@ -982,6 +1005,8 @@ __device__ SupStats combine_sup(const KParams& P, int r, FinShared& fs) {
     int idx = kIntMax;
     if (tid < G) load(tid, mp, mq, sp, sq, w, a, idx);
     reduce(mp, mq, sp, sq, w, a, idx, tid < G, m, v, true);
+    if (SAMPLED && tid == 0) fs.f[8] = accept_margin(zpx, zqx, u, m[0], m[1], v[0], v[1]);
+    __syncthreads();
   }
   SupStats s;
   s.Mp = m[0];
@@ -992,13 +1017,14 @@ __device__ SupStats combine_sup(const KParams& P, int r, FinShared& fs) {
   s.BA = v[3];
   s.xstar = __float_as_int(v[4]);
   s.nonfinite = __float_as_int(v[5]) != 0;
+  s.margin = SAMPLED ? fs.f[8] : 0.f;
   return s;
 }
 
 // Gradient value of the fast path (no entry clipped) and of the exact path.
-__device__ __forceinline__ float grad_fast(float zq, float zp, float lse_q2, float D, float lam, float c1) {
+__device__ __forceinline__ float grad_fast(float zq, float zp, float lse_q2, float lam, float c1) {
   const float q = fexp2(fmaf(zq, kLog2e, -lse_q2));
-  return q * fmaf(lam, (zq - zp) - D, c1);
+  return q * fmaf(lam, zq - zp, c1);
 }
 __device__ __forceinline__ float grad_exact(float zq, float zp, float lse_q2, float D, float lam, float lamS,
                                             float c) {
@@ -1009,8 +1035,14 @@ __device__ __forceinline__ float grad_exact(float zq, float zp, float lse_q2, fl
   return fmaf(-lamS, q, fmaf(lam, sterm, q));
 }
 
+// Aligned bf16 chunks fit 80 VGPRs, so six workgroups share a CU (only the
+// rarely taken exact path spills); fp32 chunks take twice the registers and
+// the element-wise loads of unaligned rows more.
+template <bool BF16, bool ALIGNED>
+constexpr int sup_min_waves() { return BF16 && ALIGNED ? (kElems <= 32 ? 6 : 4) : 1; }
+
 template <bool BF16, bool ALIGNED, int VMODE>
-__global__ __launch_bounds__(kThreads) void sup_kernel(KParams P) {
+__global__ __launch_bounds__(kThreads, (sup_min_waves<BF16, ALIGNED>())) void sup_kernel(KParams P) {
   constexpr bool SAMPLED = VMODE == 2, VERIFY = VMODE != 0;
   constexpr int VEC = Chunk<BF16>::VEC;
   constexpr int NV = kElems / VEC;
@@ -1132,7 +1164,7 @@ __global__ __launch_bounds__(kThreads) void sup_kernel(KParams P) {
     const unsigned long long any = __ballot(rej);
     if (l == 0) fs.i[0] = any != 0ull;
   }
-  const SupStats st = combine_sup(P, r, fs);
+  const SupStats st = combine_sup<SAMPLED>(P, r, fs, zpx, zqx, u_acc);
   const bool earlier_rejected = SAMPLED && fs.i[0] != 0;
   const float lse_q2 = st.Mq * kLog2e + flog2(st.Sq);
   const float lse_p2 = st.Mp * kLog2e + flog2(st.Sp);
@@ -1146,14 +1178,11 @@ __global__ __launch_bounds__(kThreads) void sup_kernel(KParams P) {
 
   bool accept = true;
   if constexpr (SAMPLED) {
-    const float px = fexp2((zpx - st.Mp) * kLog2e) * __builtin_amdgcn_rcpf(st.Sp);
-    const float qx = fexp2((zqx - st.Mq) * kLog2e) * __builtin_amdgcn_rcpf(st.Sq);
-    const float u = u_acc;
-    accept = u * qx < px;
+    accept = st.margin > 0.f;
     if (tid == 0 && j == 0) {
       pub_store(P.rowrec + (size_t)r * kRowRec + 1, accept ? 1.f : 0.f);
-      pub_store(P.rowrec + (size_t)r * kRowRec + 2, px - u * qx);
-      if (P.margins) P.margins[(size_t)b * (k + 1) + i] = px - u * qx;
+      pub_store(P.rowrec + (size_t)r * kRowRec + 2, st.margin);
+      if (P.margins) P.margins[(size_t)b * (k + 1) + i] = st.margin;
     }
   }
 
@@ -1208,7 +1237,8 @@ __global__ __launch_bounds__(kThreads) void sup_kernel(KParams P) {
   float Rrow = KL;
   float gstar = 0.f;
   if (fast) {
-    const float c1 = 1.f - lam * KL;
+    // g = q (1 + lambda (dz - D - KL)) = q (lambda dz + c1)
+    const float c1 = fmaf(-lam, D, 1.f - lam * KL);
     // The residual sweep shares the gradient's unpacked logits and q.
     auto sweep = [&](auto with_res) {
 #pragma unroll
@@ -1219,7 +1249,7 @@ __global__ __launch_bounds__(kThreads) void sup_kernel(KParams P) {
           const int e = s2 * VEC + u;
           const float zq = cq.get(e), zp = cp.get(e);
           const float q = fexp2(fmaf(zq, kLog2e, -lse_q2));
-          g[u] = q * fmaf(lam, (zq - zp) - D, c1);
+          g[u] = q * fmaf(lam, zq - zp, c1);
           if constexpr (decltype(with_res)::value)
             Zpart += fmaxf(0.f, fexp2(fmaf(zp, kLog2e, -lse_p2)) - q);
         }
@@ -1228,7 +1258,7 @@ __global__ __launch_bounds__(kThreads) void sup_kernel(KParams P) {
     };
     if (need_res) sweep(std::true_type{});
     else if (P.grad) sweep(std::false_type{});
-    gstar = grad_fast(zqs, st.Mp, lse_q2, D, lam, c1) - 1.f;
+    gstar = grad_fast(zqs, st.Mp, lse_q2, lam, c1) - 1.f;
   } else {
     // Exact path: clipped sums, second barrier, then the gradient (the
     // per-entry terms are recomputed from the packed logits).
