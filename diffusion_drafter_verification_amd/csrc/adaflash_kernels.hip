@@ -121,6 +121,11 @@ __device__ __forceinline__ float op_identity() {
   return __int_as_float(0x7fffffff);
 }
 
+// A value known to be the same in every lane, moved to a scalar register.
+__device__ __forceinline__ float uniform(float x) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
+
 // Order-preserving map of float bit patterns to signed integers (and back:
 // the map is its own inverse).  A float maximum becomes an integer maximum,
 // which needs no NaN canonicalisation.  Only used where no operand is NaN.
@@ -158,6 +163,7 @@ __device__ __forceinline__ void wg_reduce(float (&v)[N], const int (&ops)[N], fl
     float x = v[n];
     if (ops[n] == OP_SUM) x = wave_reduce<OP_SUM>(x);
     else if (ops[n] == OP_MAX) x = wave_reduce<OP_MAX>(x);
+    else if (ops[n] == OP_MAXI) x = wave_reduce<OP_MAXI>(x);
     else x = wave_reduce<OP_MINI>(x);
     v[n] = x;
   }
@@ -172,8 +178,9 @@ __device__ __forceinline__ void wg_reduce(float (&v)[N], const int (&ops)[N], fl
     float x;
     if (ops[n] == OP_SUM) x = (a + b) + (c + d);
     else if (ops[n] == OP_MAX) x = fmaxf(fmaxf(a, b), fmaxf(c, d));
+    else if (ops[n] == OP_MAXI) x = op2<OP_MAXI>(op2<OP_MAXI>(a, b), op2<OP_MAXI>(c, d));
     else x = op2<OP_MINI>(op2<OP_MINI>(a, b), op2<OP_MINI>(c, d));
-    v[n] = x;
+    v[n] = uniform(x);
   }
   __syncthreads();
 }
@@ -348,6 +355,24 @@ __device__ __forceinline__ float load_logit(const void* row, int v) {
   else return ((const float*)row)[v];
 }
 
+// Uniform loads of read-only data through the scalar cache (the data were
+// written before the kernel started; the scalar cache is invalidated at each
+// kernel launch).  The result lives in a scalar register.
+typedef const __attribute__((address_space(4))) uint32_t* const_u32_ptr;
+__device__ __forceinline__ uint32_t sload_u32(const void* p) { return *(const_u32_ptr)p; }
+// Logit v of a row: the aligned dword that holds it (bf16: a 4-byte aligned
+// pair, never past the allocation's rounded-up end), then the right half.
+template <bool BF16>
+__device__ __forceinline__ float sload_logit(const void* row, int v) {
+  if constexpr (BF16) {
+    const uintptr_t a = (uintptr_t)((const uint16_t*)row + v);
+    const uint32_t w = sload_u32((const void*)(a & ~(uintptr_t)3));
+    return __uint_as_float((a & 2) ? (w & 0xffff0000u) : (w << 16));
+  } else {
+    return __uint_as_float(sload_u32((const float*)row + v));
+  }
+}
+
 // Two values rounded to bf16 (nearest even) and packed: one v_cvt_pk_bf16_f32.
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -412,6 +437,8 @@ struct FinShared {
   float red[kWaves * 8];
   float f[12];
   int i[8];
+  float slot[kWaves][kElems / 4];   // per-wave slot totals of the in-chunk scan
+  unsigned long long amax[72];      // greedy: per-row (value, index) argmax keys
 };
 
 // Chunk-level inverse CDF: thread t < G holds the mass of chunk t.  Returns the
@@ -442,6 +469,23 @@ __device__ void locate_chunk(float mj, int G, float us, FinShared& fs, int* jc_o
   __syncthreads();
 }
 
+// Inclusive prefix sum across the 64 lanes of a wave.
+__device__ __forceinline__ float wave_scan_incl(float v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float t = __shfl_up(v, off, 64);
+    if (lane >= off) v += t;
+  }
+  return v;
+}
+
+// Order-preserving unsigned key of a float for 64-bit (value, index) maxima.
+__device__ __forceinline__ unsigned int ukey(float x) {
+  const unsigned int u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 // Draws the correction or bonus token for request b.  Runs on one workgroup.
 template <bool BF16, bool ALIGNED, int VMODE>
 __device__ void finalize_request(const KParams& P, int b, FinShared& fs) {
@@ -453,116 +497,145 @@ __device__ void finalize_request(const KParams& P, int b, FinShared& fs) {
   float sample_margin = __int_as_float(0x7fc00000);
 
   if constexpr (VMODE == 1) {
-    // Greedy: row argmax from the chunk records; stop at the first mismatch.
-    for (int i = 0; i <= L; ++i) {
-      const int r = r0 + i;
-      float4 a = make_float4(neg_inf(), __int_as_float(kIntMax), 0.f, 0.f);
-      if (tid < G) {
-        const float* rec = P.part1 + ((size_t)r * G + tid) * kRec1;
-        a.x = pub_load(rec + 0);
-        a.y = pub_load(rec + 1);
-      }
-      float v1[1] = {a.x};
-      const int o1[1] = {OP_MAX};
-      wg_reduce<1>(v1, o1, fs.red);
-      float v2[1] = {__int_as_float(a.x == v1[0] ? __float_as_int(a.y) : kIntMax)};
-      const int o2[1] = {OP_MINI};
-      wg_reduce<1>(v2, o2, fs.red);
-      int am = __float_as_int(v2[0]);
-      if (am == kIntMax) {  // NaN row: no chunk holds the maximum
+    // Greedy: the argmax of rows 0..L from their chunk records, all rows at
+    // once (largest maximum, then lowest index, as one 64-bit key), then the
+    // first position whose draft token differs from its row's argmax.
+    const int nrows = L + 1;
+    for (int i = tid; i < nrows; i += kThreads) fs.amax[i] = 0ull;
+    __syncthreads();
+    for (int q = tid; q < nrows * G; q += kThreads) {
+      const int i = q / G, j = q - i * G;
+      const float* rec = P.part1 + ((size_t)(r0 + i) * G + j) * kRec1;
+      const float m = pub_load(rec + 0);
+      const unsigned int idx = (unsigned int)__float_as_int(pub_load(rec + 1));
+      const unsigned long long key = ((unsigned long long)ukey(m) << 32) | (0xffffffffu - idx);
+      atomicMax(&fs.amax[i], key);
+    }
+    __syncthreads();
+    int mism = kIntMax;
+    int bad = 0;
+    for (int i = tid; i < nrows; i += kThreads) {
+      int am = (int)(0xffffffffu - (unsigned int)(fs.amax[i] & 0xffffffffull));
+      if (am == kIntMax || am < 0 || am >= V) {  // NaN row: no chunk holds the maximum
         am = 0;
-        if (tid == 0) flag(P.status, ADAFLASH_FLAG_NONFINITE);
+        bad = 1;
       }
       if (i < L) {
         int x = P.tokens[(size_t)b * k + i];
         x = x < 0 ? 0 : (x >= V ? V - 1 : x);
-        if (x != am) {
-          A = i;
-          token = am;
-          break;
-        }
-      } else {
-        token = am;
+        if (x != am) mism = min(mism, i);
       }
+      fs.amax[i] = (unsigned long long)am;  // now the row's argmax
     }
+    float v[2] = {__int_as_float(mism), __int_as_float(bad)};
+    const int ops[2] = {OP_MINI, OP_MAXI};
+    wg_reduce<2>(v, ops, fs.red);
+    if (tid == 0 && __float_as_int(v[1])) flag(P.status, ADAFLASH_FLAG_NONFINITE);
+    A = __float_as_int(v[0]) < L ? __float_as_int(v[0]) : L;
+    token = (int)fs.amax[A];
   } else {
     // Sampled: first rejected row from the per-row accept flags.
     int first = kIntMax;
     for (int i = tid; i < L; i += kThreads)
       if (pub_load(P.rowrec + (size_t)(r0 + i) * kRowRec + 1) == 0.f) first = min(first, i);
+    const float us = P.uniforms[(size_t)b * (k + 1) + k];
     float v1[1] = {__int_as_float(first)};
     const int o1[1] = {OP_MINI};
     wg_reduce<1>(v1, o1, fs.red);
     first = __float_as_int(v1[0]);
     A = first < L ? first : L;
 
-    const int rs = r0 + A;  // row the draw reads: rejected row or bonus row L
-    const RowStats st = combine_part1<true, false>(P, rs, P.kT, fs.red);
-    const float us = P.uniforms[(size_t)b * (k + 1) + k];
-    const void* trow = BF16 ? (const void*)((const uint16_t*)P.target + ((size_t)b * (k + 1) + A) * V)
-                            : (const void*)((const float*)P.target + ((size_t)b * (k + 1) + A) * V);
-    const void* drow = nullptr;
-    const float invSp = 1.f / st.SpT, invSq = 1.f / st.SqT;
-    bool resid = false;
+    // Row statistics at T of the row the draw reads (rejected row A or the
+    // bonus row L) and, for a rejected row, its per-chunk residual masses:
+    // all loaded in one round.
+    const int rs = r0 + A;
+    float mp = neg_inf(), spT = 0.f, mq = neg_inf(), sqT = 0.f, res = 0.f;
+    if (tid < G) {
+      const float* rec = P.part1 + ((size_t)rs * G + tid) * kRec1;
+      mp = pub_load(rec + 0);
+      spT = pub_load(rec + 2);
+      if (A < L) {
+        mq = pub_load(rec + 4);
+        sqT = pub_load(rec + 5);
+        res = pub_load(P.part2 + ((size_t)rs * G + tid) * kRec2 + 2);
+      }
+    }
+    float m[2] = {mp, mq};
+    const int mops[2] = {OP_MAX, OP_MAX};
+    wg_reduce<2>(m, mops, fs.red);
+    const float Mp = m[0], Mq = m[1];
+    const float pj = mp == neg_inf() ? 0.f : spT * fexp2((mp - Mp) * P.kT);
+    const float qj = mq == neg_inf() ? 0.f : sqT * fexp2((mq - Mq) * P.kT);
+    float sv[3] = {pj, qj, res};
+    const int sops[3] = {OP_SUM, OP_SUM, OP_SUM};
+    wg_reduce<3>(sv, sops, fs.red);
+    const float SpT = sv[0], SqT = sv[1];
+    const float invSp = 1.f / SpT, invSq = 1.f / SqT;
+    const bool resid = A < L && sv[2] > 0.f;
+    const float mj = tid < G ? (resid ? res : pj * invSp) : 0.f;
     int jc = 0;
     float base = 0.f, thr = 0.f, tot = 1.f;
-    if (A < L) {
-      drow = BF16 ? (const void*)((const uint16_t*)P.draft + ((size_t)b * k + A) * V)
-                  : (const void*)((const float*)P.draft + ((size_t)b * k + A) * V);
-      const float mj = tid < G ? pub_load(P.part2 + ((size_t)rs * G + tid) * kRec2 + 2) : 0.f;
-      locate_chunk(mj, G, us, fs, &jc, &base, &thr, &tot);
-      resid = tot > 0.f;
-    }
-    if (!resid) {
-      // Draw from p of row rs (bonus row, or the rejected row when Z == 0).
-      float mj = 0.f;
-      if (tid < G) {
-        const float* rec = P.part1 + ((size_t)rs * G + tid) * kRec1;
-        const float m = pub_load(rec + 0), sT = pub_load(rec + 2);
-        mj = m == neg_inf() ? 0.f : sT * fexp2((m - st.Mp) * P.kT) * invSp;
-      }
-      locate_chunk(mj, G, us, fs, &jc, &base, &thr, &tot);
-    }
+    locate_chunk(mj, G, us, fs, &jc, &base, &thr, &tot);
 
-    // Scan chunk jc in index order.
+    // Scan chunk jc in index order: per-entry masses, one prefix sum over
+    // (slot, thread, entry), the lowest index whose running sum passes thr.
+    const void* trow = BF16 ? (const void*)((const uint16_t*)P.target + (size_t)rs * V)
+                            : (const void*)((const float*)P.target + (size_t)rs * V);
+    const void* drow = BF16 ? (const void*)((const uint16_t*)P.draft + ((size_t)b * k + A) * V)
+                            : (const void*)((const float*)P.draft + ((size_t)b * k + A) * V);
     const int v0 = jc * kChunk;
     Chunk<BF16> cp, cq;
     load_chunk<BF16, ALIGNED>(cp, trow, v0, V);
     if (resid) load_chunk<BF16, ALIGNED>(cq, drow, v0, V);
-    const float ap = -st.Mp * P.kT, aq = -st.Mq * P.kT;
+    const float ap = -Mp * P.kT, aq = -Mq * P.kT;
     constexpr int VEC = Chunk<BF16>::VEC;
     constexpr int NV = kElems / VEC;
-    float carry = base;
-    int found = kIntMax, last_pos = -1;
-    float found_before = 0.f, found_at = 0.f, last_before = 0.f, last_at = 0.f;
+    const int lane = tid & 63, wave = tid >> 6;
+    float w[kElems];
+    float incl[NV], tsum[NV];
 #pragma unroll
-    for (int s = 0; s < NV; ++s) {
-      float w[VEC];
-      float tsum = 0.f;
+    for (int s2 = 0; s2 < NV; ++s2) {
+      float ts = 0.f;
 #pragma unroll
       for (int u = 0; u < VEC; ++u) {
-        const int e = s * VEC + u;
+        const int e = s2 * VEC + u;
         const float zp = cp.get(e);
-        float m;
+        float mass;
         if (resid) {
           const float pv = fexp2(fmaf(zp, P.kT, ap)) * invSp;
           const float qv = fexp2(fmaf(cq.get(e), P.kT, aq)) * invSq;
-          m = fmaxf(0.f, pv - qv);
+          mass = fmaxf(0.f, pv - qv);
         } else {
-          m = zp == neg_inf() ? 0.f : fexp2(fmaf(zp, P.kT, ap)) * invSp;
+          mass = zp == neg_inf() ? 0.f : fexp2(fmaf(zp, P.kT, ap)) * invSp;
         }
-        w[u] = m;
-        tsum += m;
+        w[e] = entry_index<BF16>(v0, e) < V ? mass : 0.f;
+        ts += w[e];
       }
-      float slot_total;
-      const float excl = wg_scan_excl(tsum, fs.red, &slot_total);
-      float cum = carry + excl;
+      tsum[s2] = ts;
+      incl[s2] = wave_scan_incl(ts);
+      if (lane == 63) fs.slot[wave][s2] = incl[s2];
+    }
+    __syncthreads();
+    float run = base;  // running sum before this thread's first entry of the slot
+    int found = kIntMax, last_pos = -1;
+    float found_before = 0.f, found_at = 0.f, last_before = 0.f, last_at = 0.f;
+#pragma unroll
+    for (int s2 = 0; s2 < NV; ++s2) {
+      float woff = 0.f, stot = 0.f;
+#pragma unroll
+      for (int w2 = 0; w2 < kWaves; ++w2) {
+        const float t = fs.slot[w2][s2];
+        if (w2 < wave) woff += t;
+        stot += t;
+      }
+      float cum = run + woff + (incl[s2] - tsum[s2]);
 #pragma unroll
       for (int u = 0; u < VEC; ++u) {
+        const int e = s2 * VEC + u;
+        const int idx = entry_index<BF16>(v0, e);
         const float before = cum;
-        cum += w[u];
-        const int idx = entry_index<BF16>(v0, s * VEC + u);
-        if (w[u] > 0.f && idx < V) {
+        cum += w[e];
+        if (w[e] > 0.f) {
           last_pos = idx;
           last_before = before;
           last_at = cum;
@@ -573,16 +646,7 @@ __device__ void finalize_request(const KParams& P, int b, FinShared& fs) {
           found_at = cum;
         }
       }
-      // Stop at the first slot where any thread crossed (uniform decision).
-      float v[1] = {__int_as_float(found)};
-      const int o[1] = {OP_MINI};
-      wg_reduce<1>(v, o, fs.red);
-      const int slot_found = __float_as_int(v[0]);
-      carry += slot_total;
-      if (slot_found != kIntMax) {
-        if (found != slot_found) found = kIntMax;  // keep only the lowest index
-        break;
-      }
+      run += stot;
     }
     // Winner: the lowest crossing index, else the last positive-mass entry.
     float v2[2] = {__int_as_float(found), __int_as_float(last_pos < 0 ? kIntMax : -last_pos)};
@@ -957,9 +1021,9 @@ __device__ SupStats combine_sup(const KParams& P, int r, FinShared& fs, float zp
     v[2] = fq > 0.f ? w * fq : 0.f;
     v[3] = fq > 0.f ? fq * a : neg_inf();
     v[4] = __int_as_float(mp == m[0] ? idx : kIntMax);
-    v[5] = __int_as_float(fin ? 0 : 1);  // OP_MAX on these two bit patterns is an integer max
+    v[5] = __int_as_float(fin ? 0 : 1);
     if (whole_group) {
-      const int ops[6] = {OP_SUM, OP_SUM, OP_SUM, OP_MAX, OP_MINI, OP_MAX};
+      const int ops[6] = {OP_SUM, OP_SUM, OP_SUM, OP_MAX, OP_MINI, OP_MAXI};
       wg_reduce<6>(v, ops, fs.red);
     } else {
       v[0] = wave_reduce<OP_SUM>(v[0]);
@@ -967,7 +1031,7 @@ __device__ SupStats combine_sup(const KParams& P, int r, FinShared& fs, float zp
       v[2] = wave_reduce<OP_SUM>(v[2]);
       v[3] = wave_reduce<OP_MAX>(v[3]);
       v[4] = wave_reduce<OP_MINI>(v[4]);
-      v[5] = wave_reduce<OP_MAX>(v[5]);
+      v[5] = wave_reduce<OP_MAXI>(v[5]);
     }
   };
   auto load = [&](int c, float& mp, float& mq, float& sp, float& sq, float& w, float& a, int& idx) {
@@ -1009,15 +1073,15 @@ __device__ SupStats combine_sup(const KParams& P, int r, FinShared& fs, float zp
     __syncthreads();
   }
   SupStats s;
-  s.Mp = m[0];
-  s.Mq = m[1];
-  s.Sp = v[0];
-  s.Sq = v[1];
-  s.Wsum = v[2];
-  s.BA = v[3];
-  s.xstar = __float_as_int(v[4]);
-  s.nonfinite = __float_as_int(v[5]) != 0;
-  s.margin = SAMPLED ? fs.f[8] : 0.f;
+  s.Mp = uniform(m[0]);
+  s.Mq = uniform(m[1]);
+  s.Sp = uniform(v[0]);
+  s.Sq = uniform(v[1]);
+  s.Wsum = uniform(v[2]);
+  s.BA = uniform(v[3]);
+  s.xstar = __float_as_int(uniform(v[4]));
+  s.nonfinite = __float_as_int(uniform(v[5])) != 0;
+  s.margin = SAMPLED ? uniform(fs.f[8]) : 0.f;
   return s;
 }
 
@@ -1035,14 +1099,17 @@ __device__ __forceinline__ float grad_exact(float zq, float zp, float lse_q2, fl
   return fmaf(-lamS, q, fmaf(lam, sterm, q));
 }
 
-// Aligned bf16 chunks fit 80 VGPRs, so six workgroups share a CU (only the
-// rarely taken exact path spills); fp32 chunks take twice the registers and
-// the element-wise loads of unaligned rows more.
-template <bool BF16, bool ALIGNED>
-constexpr int sup_min_waves() { return BF16 && ALIGNED ? (kElems <= 32 ? 6 : 4) : 1; }
+// Workgroups per CU: aligned bf16 chunks fit 80 VGPRs (six per CU), and the
+// fused sampled variant 72 (seven per CU; two values of the rarely taken
+// exact path spill, measured faster than six); fp32 chunks take twice the
+// registers and the element-wise loads of unaligned rows more.
+template <bool BF16, bool ALIGNED, int VMODE>
+constexpr int sup_min_waves() {
+  return BF16 && ALIGNED ? (kElems <= 32 ? (VMODE == 2 ? 7 : 6) : 4) : 1;
+}
 
 template <bool BF16, bool ALIGNED, int VMODE>
-__global__ __launch_bounds__(kThreads, (sup_min_waves<BF16, ALIGNED>())) void sup_kernel(KParams P) {
+__global__ __launch_bounds__(kThreads, (sup_min_waves<BF16, ALIGNED, VMODE>())) void sup_kernel(KParams P) {
   constexpr bool SAMPLED = VMODE == 2, VERIFY = VMODE != 0;
   constexpr int VEC = Chunk<BF16>::VEC;
   constexpr int NV = kElems / VEC;
@@ -1081,16 +1148,16 @@ __global__ __launch_bounds__(kThreads, (sup_min_waves<BF16, ALIGNED>())) void su
   int xtok = 0, n = 0;
   float u_acc = 0.f, zpx = 0.f, zqx = 0.f;
   if (draft_row) {
-    n = P.row_offsets[b] + i;  // packed row
+    n = (int)sload_u32(P.row_offsets + b) + i;  // packed row
     if constexpr (SAMPLED) {
-      xtok = P.tokens[(size_t)b * k + i];
+      xtok = (int)sload_u32(P.tokens + (size_t)b * k + i);
       if (xtok < 0 || xtok >= V) {
         if (tid == 0 && j == 0) flag(P.status, ADAFLASH_FLAG_BAD_TOKEN);
         xtok = xtok < 0 ? 0 : V - 1;
       }
-      u_acc = P.uniforms[(size_t)b * (k + 1) + i];
-      zpx = load_logit<BF16>(trow, xtok);
-      zqx = load_logit<BF16>(drow, xtok);
+      u_acc = __uint_as_float(sload_u32(P.uniforms + (size_t)b * (k + 1) + i));
+      zpx = sload_logit<BF16>(trow, xtok);
+      zqx = sload_logit<BF16>(drow, xtok);
     }
   }
   float mp = neg_inf(), mq = neg_inf();
@@ -1118,8 +1185,8 @@ __global__ __launch_bounds__(kThreads, (sup_min_waves<BF16, ALIGNED>())) void su
     cand = v0 + (ce / VEC) * (kThreads * VEC) + tid * VEC + (ce % VEC);
   }
   float sp = 0.f, sq = 0.f, W = 0.f, Amax = neg_inf();
-  const float ap = Mw[0] == neg_inf() ? 0.f : -Mw[0] * kLog2e;
-  const float aq = Mw[1] == neg_inf() ? 0.f : -Mw[1] * kLog2e;
+  const float ap = uniform(Mw[0] == neg_inf() ? 0.f : -Mw[0] * kLog2e);
+  const float aq = uniform(Mw[1] == neg_inf() ? 0.f : -Mw[1] * kLog2e);
   if (draft_row) {
 #pragma unroll
     for (int e = 0; e < kElems; ++e) {
@@ -1166,10 +1233,10 @@ __global__ __launch_bounds__(kThreads, (sup_min_waves<BF16, ALIGNED>())) void su
   }
   const SupStats st = combine_sup<SAMPLED>(P, r, fs, zpx, zqx, u_acc);
   const bool earlier_rejected = SAMPLED && fs.i[0] != 0;
-  const float lse_q2 = st.Mq * kLog2e + flog2(st.Sq);
-  const float lse_p2 = st.Mp * kLog2e + flog2(st.Sp);
-  const float D = (lse_q2 - lse_p2) * kLn2;
-  const float KL = st.Wsum / st.Sq - D;
+  const float lse_q2 = uniform(st.Mq * kLog2e + flog2(st.Sq));
+  const float lse_p2 = uniform(st.Mp * kLog2e + flog2(st.Sp));
+  const float D = uniform((lse_q2 - lse_p2) * kLn2);
+  const float KL = uniform(st.Wsum / st.Sq - D);
   const float bound = (st.BA + fmaxf(0.f, -D)) / st.Sq;
   const float c = P.clip_c, lam = P.lambda;
   const bool fast = !st.nonfinite && bound <= 0.999f * c;
@@ -1191,10 +1258,10 @@ __global__ __launch_bounds__(kThreads, (sup_min_waves<BF16, ALIGNED>())) void su
   const int xs = st.xstar;
   const int xo = xs - v0;
   const bool xs_here = xo >= 0 && xo < kChunk && ((xo % (kThreads * VEC)) / VEC) == tid;
-  // The thread holding x* reads z_q[x*] now (z_p[x*] is the row maximum); its
-  // gradient entry is rewritten after the sweep with the one-hot term.
-  float zqs = 0.f;
-  if (xs_here) zqs = load_logit<BF16>(drow, xs);
+  // z_q[x*] (one value for the workgroup; z_p[x*] is the row maximum).  The
+  // thread holding x* rewrites its gradient entry after the sweep with the
+  // one-hot term.
+  const float zqs = xs >= 0 && xs < V ? sload_logit<BF16>(drow, xs) : 0.f;
 
   // Residual mass max(0, p - q) of a rejected row.
   const bool need_res = SAMPLED && !accept && !earlier_rejected;
@@ -1238,7 +1305,7 @@ __global__ __launch_bounds__(kThreads, (sup_min_waves<BF16, ALIGNED>())) void su
   float gstar = 0.f;
   if (fast) {
     // g = q (1 + lambda (dz - D - KL)) = q (lambda dz + c1)
-    const float c1 = fmaf(-lam, D, 1.f - lam * KL);
+    const float c1 = uniform(fmaf(-lam, D, 1.f - lam * KL));
     // The residual sweep shares the gradient's unpacked logits and q.
     auto sweep = [&](auto with_res) {
 #pragma unroll
@@ -1294,7 +1361,7 @@ __global__ __launch_bounds__(kThreads, (sup_min_waves<BF16, ALIGNED>())) void su
     const int srops[2] = {OP_SUM, OP_SUM};
     wg_reduce<2>(sr, srops, fs.red);
     Rrow = sr[1];
-    const float lamS = lam * sr[0];
+    const float lamS = uniform(lam * sr[0]);
     cp.opaque();
     cq.opaque();
     if (P.grad) {
@@ -1305,6 +1372,8 @@ __global__ __launch_bounds__(kThreads, (sup_min_waves<BF16, ALIGNED>())) void su
         for (int u = 0; u < VEC; ++u) {
           const int e = s2 * VEC + u;
           g[u] = grad_exact(cq.get(e), cp.get(e), lse_q2, D, lam, lamS, c);
+          // Rarely taken path: limit the interleaving (and registers) here.
+          if (u & 1) __builtin_amdgcn_sched_barrier(0);
         }
         store_slot(s2, g);
       }
@@ -1339,13 +1408,15 @@ __global__ __launch_bounds__(kThreads) void final_kernel(KParams P) {
 
 // --------------------------------------------------------------- pack kernel
 
-// One workgroup of 1024 threads: clamp verify lengths, prefix sum of the
-// verified rows (packed row offsets), counter reset, status initialisation.
+// One workgroup of 1024 threads: clamps the verify lengths, writes the packed
+// row offsets (prefix sum: a scan inside each wave, then across the 16
+// waves), clears the arrival counters, marks every row's accept flag as not
+// yet known, and initialises the status word.
 __global__ __launch_bounds__(1024) void pack_kernel(const int32_t* verify_len, int B, int k,
                                                      int32_t* row_offsets, Workspace ws, int32_t* status) {
-  __shared__ int s_scan[1024];
+  __shared__ int s_wave[16];
   __shared__ int s_flags;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid == 0) s_flags = 0;
   __syncthreads();
   int carry = 0;
@@ -1360,23 +1431,30 @@ __global__ __launch_bounds__(1024) void pack_kernel(const int32_t* verify_len, i
       }
       ws.Lc[b] = L;
     }
-    s_scan[tid] = L;
+    int x = L;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(x, off, 64);
+      if (lane >= off) x += t;
+    }
+    if (lane == 63) s_wave[wave] = x;
     __syncthreads();
-    // Hillis-Steele inclusive scan.
-    for (int off = 1; off < 1024; off <<= 1) {
-      const int a = tid >= off ? s_scan[tid - off] : 0;
-      __syncthreads();
-      s_scan[tid] += a;
-      __syncthreads();
+    int woff = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+      const int t = s_wave[w];
+      if (w < wave) woff += t;
+      tot += t;
     }
-    if (b < B) {
-      row_offsets[b] = carry + s_scan[tid] - L;
-      for (int ii = 0; ii <= k; ++ii) {
-        ws.rowcnt[((size_t)b * (k + 1) + ii) * kCounterStride] = 0;
-        ws.rowrec[((size_t)b * (k + 1) + ii) * kRowRec + 1] = 2.f;  // accept flag: not yet known
-      }
+    if (b < B) row_offsets[b] = carry + woff + x - L;
+    // Row slots of this block's requests, spread over the threads.
+    const int pairs = min(1024, B - base) * (k + 1);
+    const size_t r0 = (size_t)base * (k + 1);
+    for (int q = tid; q < pairs; q += 1024) {
+      ws.rowcnt[(r0 + q) * kCounterStride] = 0;
+      ws.rowrec[(r0 + q) * kRowRec + 1] = 2.f;  // accept flag: not yet known
     }
-    carry += s_scan[1023];
+    carry += tot;
     __syncthreads();
   }
   if (tid == 0) {
