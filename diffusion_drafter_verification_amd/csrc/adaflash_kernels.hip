@@ -381,6 +381,18 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
 
+// Two values rounded to fp16 (nearest even) and packed: one v_cvt_pk_f16_f32.
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  const f32x2_t f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2_t));
+}
+// Half h (0 or 1) of a packed fp16 pair times y, plus z: one v_fma_mix_f32.
+__device__ __forceinline__ float fma_f16(uint32_t w, int h, float y, float z) {
+  const f16x2_t v = __builtin_bit_cast(f16x2_t, w);
+  return __builtin_fmaf(h ? (float)v.y : (float)v.x, y, z);
+}
+
 // ------------------------------------------------------------ row statistics
 
 struct RowStats {
@@ -1085,11 +1097,7 @@ __device__ SupStats combine_sup(const KParams& P, int r, FinShared& fs, float zp
   return s;
 }
 
-// Gradient value of the fast path (no entry clipped) and of the exact path.
-__device__ __forceinline__ float grad_fast(float zq, float zp, float lse_q2, float lam, float c1) {
-  const float q = fexp2(fmaf(zq, kLog2e, -lse_q2));
-  return q * fmaf(lam, zq - zp, c1);
-}
+// Gradient value of the exact path (q recomputed in fp32: clip decisions).
 __device__ __forceinline__ float grad_exact(float zq, float zp, float lse_q2, float D, float lam, float lamS,
                                             float c) {
   const float q = fexp2(fmaf(zq, kLog2e, -lse_q2));
@@ -1115,6 +1123,13 @@ __global__ __launch_bounds__(kThreads, (sup_min_waves<BF16, ALIGNED, VMODE>())) 
   constexpr int NV = kElems / VEC;
   __shared__ FinShared fs;
   __shared__ int sh_ok;
+  // bf16 logits: exp(z_q - m) of this thread's draft entries from pass 1, as
+  // fp16 pairs (slot-major, 16 KB); the fast-path gradient reads q back
+  // instead of recomputing an exponential (fp16 keeps q to 2^-11, well inside
+  // the bf16 output's rounding).  fp32 logits recompute q.  Each thread reads
+  // only what it wrote.
+  constexpr bool ECACHE = BF16;
+  __shared__ uint32_t ecache[ECACHE ? kElems / 2 * kThreads : 1];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -1189,14 +1204,27 @@ __global__ __launch_bounds__(kThreads, (sup_min_waves<BF16, ALIGNED, VMODE>())) 
   const float aq = uniform(Mw[1] == neg_inf() ? 0.f : -Mw[1] * kLog2e);
   if (draft_row) {
 #pragma unroll
-    for (int e = 0; e < kElems; ++e) {
-      const float zq = cq.get(e), zp = cp.get(e);
-      const float ee = fexp2(fmaf(zq, kLog2e, aq));
-      sp += fexp2(fmaf(zp, kLog2e, ap));
-      sq += ee;
-      const float pr = ee * (zq - zp);
-      W += pr;
-      Amax = fmaxf(Amax, pr);
+    for (int s2 = 0; s2 < NV; ++s2) {
+      uint32_t hw[VEC / 2];
+#pragma unroll
+      for (int u = 0; u < VEC; u += 2) {
+        float ee2[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int e = s2 * VEC + u + t;
+          const float zq = cq.get(e), zp = cp.get(e);
+          const float ee = fexp2(fmaf(zq, kLog2e, aq));
+          sp += fexp2(fmaf(zp, kLog2e, ap));
+          sq += ee;
+          const float pr = ee * (zq - zp);
+          W += pr;
+          Amax = fmaxf(Amax, pr);
+          ee2[t] = ee;
+        }
+        if constexpr (ECACHE) hw[u / 2] = pack_f16x2(ee2[0], ee2[1]);
+      }
+      if constexpr (ECACHE)
+        *(uint4*)(ecache + ((size_t)s2 * kThreads + tid) * 4) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
     }
   } else if (SAMPLED) {
 #pragma unroll
@@ -1304,19 +1332,33 @@ __global__ __launch_bounds__(kThreads, (sup_min_waves<BF16, ALIGNED, VMODE>())) 
   float Rrow = KL;
   float gstar = 0.f;
   if (fast) {
-    // g = q (1 + lambda (dz - D - KL)) = q (lambda dz + c1)
-    const float c1 = uniform(fmaf(-lam, D, 1.f - lam * KL));
-    // The residual sweep shares the gradient's unpacked logits and q.
+    // g = q (1 + lambda (dz - D - KL)) = q (lambda dz + c1), with q = e s the
+    // cached pass-1 exponential e = exp(z_q - m) scaled by s = exp(m - lse_q).
+    const float c1 = fmaf(-lam, D, 1.f - lam * KL);
+    const float sc = uniform(fexp2(-aq - lse_q2));
+    const float lsc = uniform(lam * sc), csc = uniform(c1 * sc);
+    // The residual sweep shares the gradient's unpacked logits; its q is
+    // recomputed in fp32 (p - q cancels).
     auto sweep = [&](auto with_res) {
 #pragma unroll
       for (int s2 = 0; s2 < NV; ++s2) {
+        uint32_t hw[VEC / 2];
+        if constexpr (ECACHE) {
+          const uint4 h4 = *(const uint4*)(ecache + ((size_t)s2 * kThreads + tid) * 4);
+          hw[0] = h4.x;
+          hw[1] = h4.y;
+          hw[2] = h4.z;
+          hw[3] = h4.w;
+        }
         float g[VEC];
 #pragma unroll
         for (int u = 0; u < VEC; ++u) {
           const int e = s2 * VEC + u;
           const float zq = cq.get(e), zp = cp.get(e);
-          const float q = fexp2(fmaf(zq, kLog2e, -lse_q2));
-          g[u] = q * fmaf(lam, zq - zp, c1);
+          float q = 0.f;
+          if (!ECACHE || decltype(with_res)::value) q = fexp2(fmaf(zq, kLog2e, -lse_q2));
+          if constexpr (ECACHE) g[u] = fma_f16(hw[u / 2], u & 1, fmaf(lsc, zq - zp, csc), 0.f);
+          else g[u] = q * fmaf(lam, zq - zp, c1);
           if constexpr (decltype(with_res)::value)
             Zpart += fmaxf(0.f, fexp2(fmaf(zp, kLog2e, -lse_p2)) - q);
         }
@@ -1325,7 +1367,15 @@ __global__ __launch_bounds__(kThreads, (sup_min_waves<BF16, ALIGNED, VMODE>())) 
     };
     if (need_res) sweep(std::true_type{});
     else if (P.grad) sweep(std::false_type{});
-    gstar = grad_fast(zqs, st.Mp, lse_q2, lam, c1) - 1.f;
+    if (xs_here) {
+      if constexpr (ECACHE) {
+        const int xs_slot = xo / (kThreads * VEC), xs_u = xo % VEC;
+        const uint32_t w = ecache[((size_t)xs_slot * kThreads + tid) * 4 + xs_u / 2];
+        gstar = fma_f16(w, xs_u & 1, fmaf(lsc, zqs - st.Mp, csc), 0.f) - 1.f;
+      } else {
+        gstar = fexp2(fmaf(zqs, kLog2e, -lse_q2)) * fmaf(lam, zqs - st.Mp, c1) - 1.f;
+      }
+    }
   } else {
     // Exact path: clipped sums, second barrier, then the gradient (the
     // per-entry terms are recomputed from the packed logits).
