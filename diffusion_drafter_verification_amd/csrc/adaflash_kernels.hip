@@ -56,6 +56,7 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr int kWaves = kThreads / 64;
+static_assert(kWaves == 4, "the workgroup reductions combine four waves");
 constexpr int kIntMax = 0x7fffffff;
 constexpr int kSpinLimit = 1 << 18;  // bound on polls (~0.2 us of s_sleep between polls)
 
@@ -151,6 +152,54 @@ __device__ __forceinline__ float wave_reduce(float v) {
   v = op2<OP>(v, dpp_rows<0x142, 0xA>(v, op_identity<OP>()));  // row_bcast:15
   v = op2<OP>(v, dpp_rows<0x143, 0xC>(v, op_identity<OP>()));  // row_bcast:31
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// As wave_reduce, but the result is left in lane 63 only (no broadcast).
+template <int OP>
+__device__ __forceinline__ float wave_reduce_l63(float v) {
+  if constexpr (OP == OP_MAX) {
+    const float k = __int_as_float(max_key(__float_as_int(v)));
+    return __int_as_float(max_key(__float_as_int(wave_reduce_l63<OP_MAXI>(k))));
+  }
+  v = op2<OP>(v, dpp_f<0xB1>(v));
+  v = op2<OP>(v, dpp_f<0x4E>(v));
+  v = op2<OP>(v, dpp_f<0x141>(v));
+  v = op2<OP>(v, dpp_f<0x140>(v));
+  v = op2<OP>(v, dpp_rows<0x142, 0xA>(v, op_identity<OP>()));
+  v = op2<OP>(v, dpp_rows<0x143, 0xC>(v, op_identity<OP>()));
+  return v;
+}
+
+// Workgroup reduction whose results only thread 0 needs: the same values, in
+// the same combination order, as wg_reduce, valid in thread 0 only.  `red` is
+// free again once every thread has passed the next barrier.
+template <int N>
+__device__ __forceinline__ void wg_reduce_lead(float (&v)[N], const int (&ops)[N], float* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    float x = v[n];
+    if (ops[n] == OP_SUM) x = wave_reduce_l63<OP_SUM>(x);
+    else if (ops[n] == OP_MAX) x = wave_reduce_l63<OP_MAX>(x);
+    else if (ops[n] == OP_MAXI) x = wave_reduce_l63<OP_MAXI>(x);
+    else x = wave_reduce_l63<OP_MINI>(x);
+    v[n] = x;
+  }
+  if (lane == 63) {
+#pragma unroll
+    for (int n = 0; n < N; ++n) red[wave * N + n] = v[n];
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      float a = red[0 * N + n], b = red[1 * N + n], c = red[2 * N + n], d = red[3 * N + n];
+      if (ops[n] == OP_SUM) v[n] = (a + b) + (c + d);
+      else if (ops[n] == OP_MAX) v[n] = fmaxf(fmaxf(a, b), fmaxf(c, d));
+      else if (ops[n] == OP_MAXI) v[n] = op2<OP_MAXI>(op2<OP_MAXI>(a, b), op2<OP_MAXI>(c, d));
+      else v[n] = op2<OP_MINI>(op2<OP_MINI>(a, b), op2<OP_MINI>(c, d));
+    }
+  }
 }
 
 // Workgroup reduction of N values with per-value operators; every thread gets
@@ -295,22 +344,30 @@ __device__ __forceinline__ int entry_index(int v0, int e) {
   return v0 + (e / VEC) * (kThreads * VEC) + (int)threadIdx.x * VEC + (e % VEC);
 }
 
+// Buffer resource of one row (base and byte length in scalar registers).  A
+// whole-chunk access then needs one thread offset in a vector register and
+// the slot offset in a scalar register: no 64-bit address arithmetic per slot.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* row, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(row), 0, bytes, 0x00020000);
+}
+
 template <bool BF16, bool ALIGNED>
 __device__ __forceinline__ void load_chunk(Chunk<BF16>& c, const void* row, int v0, int V) {
   constexpr int VEC = Chunk<BF16>::VEC;
   constexpr int NV = kElems / VEC;
+  constexpr int ES = BF16 ? 2 : 4;
   const uint32_t ninf = BF16 ? 0xff7fff7fu : 0xff7fffffu;  // -max finite
   if constexpr (ALIGNED) {
     if (v0 + kChunk <= V) {  // whole chunk inside the row: no per-slot guards
+      const __amdgpu_buffer_rsrc_t rs = row_rsrc(row, V * ES);
+      const int toff = (int)threadIdx.x * 16;
 #pragma unroll
       for (int s = 0; s < NV; ++s) {
-        const int idx0 = v0 + s * (kThreads * VEC) + (int)threadIdx.x * VEC;
-        const uint4 q = BF16 ? *(const uint4*)((const uint16_t*)row + idx0)
-                             : *(const uint4*)((const float*)row + idx0);
-        c.w[s * 4 + 0] = q.x;
-        c.w[s * 4 + 1] = q.y;
-        c.w[s * 4 + 2] = q.z;
-        c.w[s * 4 + 3] = q.w;
+        const auto q = __builtin_amdgcn_raw_buffer_load_b128(rs, toff, (v0 + s * (kThreads * VEC)) * ES, 0);
+        c.w[s * 4 + 0] = q[0];
+        c.w[s * 4 + 1] = q[1];
+        c.w[s * 4 + 2] = q[2];
+        c.w[s * 4 + 3] = q[3];
       }
       return;
     }
@@ -387,6 +444,36 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
   const f32x2_t f = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2_t));
 }
+// z_q - z_p of the eight bf16 entries in four packed words of each row: a
+// byte permute puts the two rows' halves side by side and a bf16 dot product
+// with (1, -1) subtracts them (the products are exact).  The three-operand
+// dot form with a zero addend is written out (the compiler otherwise picks
+// the accumulating form plus a move).  The compiler does not see the hazards
+// of an asm block: a dot result may be read by another VALU instruction only
+// three wait states after it is written, hence the closing s_nop; the opening
+// one keeps two wait states after the permutes.
+__device__ __forceinline__ void bf16_diff8(const uint32_t* wq, const uint32_t* wp, float (&dz)[8]) {
+  uint32_t pr[8];
+#pragma unroll
+  for (int h = 0; h < 8; ++h)
+    pr[h] = __builtin_amdgcn_perm(wp[h >> 1], wq[h >> 1], (h & 1) ? 0x07060302u : 0x05040100u);
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_dot2_f32_bf16 %0, %8, %16, 0\n\t"
+      "v_dot2_f32_bf16 %1, %9, %16, 0\n\t"
+      "v_dot2_f32_bf16 %2, %10, %16, 0\n\t"
+      "v_dot2_f32_bf16 %3, %11, %16, 0\n\t"
+      "v_dot2_f32_bf16 %4, %12, %16, 0\n\t"
+      "v_dot2_f32_bf16 %5, %13, %16, 0\n\t"
+      "v_dot2_f32_bf16 %6, %14, %16, 0\n\t"
+      "v_dot2_f32_bf16 %7, %15, %16, 0\n\t"
+      "s_nop 2"
+      : "=&v"(dz[0]), "=&v"(dz[1]), "=&v"(dz[2]), "=&v"(dz[3]), "=&v"(dz[4]), "=&v"(dz[5]), "=&v"(dz[6]),
+        "=&v"(dz[7])
+      : "v"(pr[0]), "v"(pr[1]), "v"(pr[2]), "v"(pr[3]), "v"(pr[4]), "v"(pr[5]), "v"(pr[6]), "v"(pr[7]),
+        "s"(0xbf803f80u));  // bf16 pair (1, -1)
+}
+
 // Half h (0 or 1) of a packed fp16 pair times y, plus z: one v_fma_mix_f32.
 __device__ __forceinline__ float fma_f16(uint32_t w, int h, float y, float z) {
   const f16x2_t v = __builtin_bit_cast(f16x2_t, w);
@@ -994,7 +1081,9 @@ __global__ __launch_bounds__(kThreads) void row_kernel(KParams P) {
 
 struct SupStats {
   float Mp, Mq, Sp, Sq, Wsum, BA;
-  int xstar, nonfinite;
+  int xstar;     // lowest index of the row maximum of z_p, or (chunk-level
+                 // records) the lowest chunk holding it
+  int nonfinite;
   float margin;  // p(x) - u q(x) of the accept test (sampled verification)
 };
 
@@ -1009,8 +1098,9 @@ __device__ __forceinline__ float accept_margin(float zpx, float zqx, float u, fl
 // Combines the G chunk records of row r (identical in every workgroup of the
 // row).  With G <= 64 wave 0 alone reduces them (lane j holds chunk j) and
 // hands the results to the other waves through fs.f; otherwise every wave
-// takes part.
-template <bool SAMPLED>
+// takes part.  CHUNK_X: the records carry no argmax; xstar is then the lowest
+// chunk whose maximum is the row maximum.
+template <bool SAMPLED, bool CHUNK_X>
 __device__ SupStats combine_sup(const KParams& P, int r, FinShared& fs, float zpx, float zqx, float u) {
   const int tid = threadIdx.x;
   const int G = P.G;
@@ -1049,7 +1139,7 @@ __device__ SupStats combine_sup(const KParams& P, int r, FinShared& fs, float zp
   auto load = [&](int c, float& mp, float& mq, float& sp, float& sq, float& w, float& a, int& idx) {
     const float* rec = P.part1 + ((size_t)r * G + c) * kRec1;
     mp = pub_load(rec + 0);
-    idx = __float_as_int(pub_load(rec + 1));
+    idx = CHUNK_X ? c : __float_as_int(pub_load(rec + 1));
     sp = pub_load(rec + 2);
     w = pub_load(rec + 3);
     mq = pub_load(rec + 4);
@@ -1119,6 +1209,7 @@ constexpr int sup_min_waves() {
 template <bool BF16, bool ALIGNED, int VMODE>
 __global__ __launch_bounds__(kThreads, (sup_min_waves<BF16, ALIGNED, VMODE>())) void sup_kernel(KParams P) {
   constexpr bool SAMPLED = VMODE == 2, VERIFY = VMODE != 0;
+  constexpr bool DEFER_X = VMODE != 1;  // argmax searched after the row barrier
   constexpr int VEC = Chunk<BF16>::VEC;
   constexpr int NV = kElems / VEC;
   __shared__ FinShared fs;
@@ -1189,15 +1280,18 @@ __global__ __launch_bounds__(kThreads, (sup_min_waves<BF16, ALIGNED, VMODE>())) 
     const int ops[2] = {OP_MAX, OP_MAX};
     wg_reduce<2>(Mw, ops, fs.red);
   }
-  // Lowest index of this chunk holding the maximum of z_p (only threads that
-  // hold it search; the entry number is tracked and converted once).
+  // Greedy verification needs every row's argmax in the finaliser: the lowest
+  // index of this chunk holding the chunk maximum of z_p goes into the record
+  // (only threads that hold it search).  Otherwise only the chunk that holds
+  // the row maximum looks for it, after the row barrier.
   int cand = kIntMax;
-  if (mp == Mw[0]) {
+  if (!DEFER_X && mp == Mw[0]) {
     int ce = 0;
 #pragma unroll
     for (int e = kElems - 1; e >= 0; --e)
       if (cp.get(e) == Mw[0]) ce = e;
-    cand = v0 + (ce / VEC) * (kThreads * VEC) + tid * VEC + (ce % VEC);
+    cand = entry_index<BF16>(v0, ce);
+    if (cand >= V) cand = kIntMax;  // padding (a row of -inf only)
   }
   float sp = 0.f, sq = 0.f, W = 0.f, Amax = neg_inf();
   const float ap = uniform(Mw[0] == neg_inf() ? 0.f : -Mw[0] * kLog2e);
@@ -1231,13 +1325,16 @@ __global__ __launch_bounds__(kThreads, (sup_min_waves<BF16, ALIGNED, VMODE>())) 
     for (int e = 0; e < kElems; ++e) sp += fexp2(fmaf(cp.get(e), kLog2e, ap));
   }
   {
+    // Only thread 0 publishes the record; fs.red is next written after the
+    // row barrier.
+    constexpr int NR = DEFER_X ? 4 : 5;
     float v[5] = {sp, sq, W, Amax, __int_as_float(cand)};
     const int ops[5] = {OP_SUM, OP_SUM, OP_SUM, OP_MAX, OP_MINI};
-    wg_reduce<5>(v, ops, fs.red);
+    wg_reduce_lead<NR>(reinterpret_cast<float(&)[NR]>(v), reinterpret_cast<const int(&)[NR]>(ops), fs.red);
     if (tid == 0) {
       float* rec = P.part1 + ((size_t)r * G + j) * kRec1;
       pub_store(rec + 0, Mw[0]);
-      pub_store(rec + 1, v[4]);
+      if (!DEFER_X) pub_store(rec + 1, v[4]);
       pub_store(rec + 2, v[0]);
       pub_store(rec + 3, v[2]);
       pub_store(rec + 4, Mw[1]);
@@ -1259,7 +1356,7 @@ __global__ __launch_bounds__(kThreads, (sup_min_waves<BF16, ALIGNED, VMODE>())) 
     const unsigned long long any = __ballot(rej);
     if (l == 0) fs.i[0] = any != 0ull;
   }
-  const SupStats st = combine_sup<SAMPLED>(P, r, fs, zpx, zqx, u_acc);
+  const SupStats st = combine_sup<SAMPLED, DEFER_X>(P, r, fs, zpx, zqx, u_acc);
   const bool earlier_rejected = SAMPLED && fs.i[0] != 0;
   const float lse_q2 = uniform(st.Mq * kLog2e + flog2(st.Sq));
   const float lse_p2 = uniform(st.Mp * kLog2e + flog2(st.Sp));
@@ -1268,7 +1365,9 @@ __global__ __launch_bounds__(kThreads, (sup_min_waves<BF16, ALIGNED, VMODE>())) 
   const float bound = (st.BA + fmaxf(0.f, -D)) / st.Sq;
   const float c = P.clip_c, lam = P.lambda;
   const bool fast = !st.nonfinite && bound <= 0.999f * c;
-  if (tid == 0 && j == 0 && !(st.Mp < __builtin_inff() && st.Sp > 0.f && st.Sq > 0.f))
+  // (A row maximum at the padding value means a row of -inf only.)
+  const float pad = __uint_as_float(BF16 ? 0xff7f0000u : 0xff7fffffu);
+  if (tid == 0 && j == 0 && !(st.Mp < __builtin_inff() && st.Mp > pad && st.Sp > 0.f && st.Sq > 0.f))
     flag(P.status, ADAFLASH_FLAG_NONFINITE);
 
   bool accept = true;
@@ -1281,11 +1380,28 @@ __global__ __launch_bounds__(kThreads, (sup_min_waves<BF16, ALIGNED, VMODE>())) 
     }
   }
 
+  int xs = st.xstar;
+  if constexpr (DEFER_X) {
+    // st.xstar is the lowest chunk whose maximum is the row maximum; that
+    // chunk finds the lowest index holding it.
+    xs = kIntMax;
+    if (j == st.xstar) {
+      int ce = kIntMax;
+#pragma unroll
+      for (int e = kElems - 1; e >= 0; --e)
+        if (cp.get(e) == st.Mp) ce = e;
+      int cidx = ce == kIntMax ? kIntMax : entry_index<BF16>(v0, ce);
+      if (cidx >= V) cidx = kIntMax;  // padding (a row of -inf only)
+      float x1[1] = {__int_as_float(cidx)};
+      const int o1[1] = {OP_MINI};
+      wg_reduce<1>(x1, o1, fs.red);
+      xs = __float_as_int(x1[0]);
+    }
+  }
   cp.opaque();
   cq.opaque();
-  const int xs = st.xstar;
   const int xo = xs - v0;
-  const bool xs_here = xo >= 0 && xo < kChunk && ((xo % (kThreads * VEC)) / VEC) == tid;
+  const bool xs_here = xs < V && xo >= 0 && xo < kChunk && ((xo % (kThreads * VEC)) / VEC) == tid;
   // z_q[x*] (one value for the workgroup; z_p[x*] is the row maximum).  The
   // thread holding x* rewrites its gradient entry after the sweep with the
   // one-hot term.
@@ -1295,8 +1411,19 @@ __global__ __launch_bounds__(kThreads, (sup_min_waves<BF16, ALIGNED, VMODE>())) 
   const bool need_res = SAMPLED && !accept && !earlier_rejected;
   float Zpart = 0.f;
 
+  const bool whole = v0 + kChunk <= V;
   auto store_slot = [&](int s2, const float (&g)[VEC]) {
     const int idx0 = v0 + s2 * (kThreads * VEC) + tid * VEC;
+    if constexpr (BF16 && ALIGNED) {
+      if (whole) {
+        const __amdgpu_buffer_rsrc_t rs = row_rsrc((const uint16_t*)P.grad + (size_t)n * V, V * 2);
+        typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+        const u32x4_t o = {pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]), pack_bf16x2(g[4], g[5]),
+                           pack_bf16x2(g[6], g[7])};
+        __builtin_amdgcn_raw_buffer_store_b128(o, rs, tid * 16, (v0 + s2 * (kThreads * VEC)) * 2, 0);
+        return;
+      }
+    }
     if constexpr (BF16) {
       uint16_t* gr = (uint16_t*)P.grad + (size_t)n * V;
       if constexpr (ALIGNED) {
@@ -1351,14 +1478,20 @@ __global__ __launch_bounds__(kThreads, (sup_min_waves<BF16, ALIGNED, VMODE>())) 
           hw[3] = h4.w;
         }
         float g[VEC];
+        float dz8[8];
+        if constexpr (ECACHE && !decltype(with_res)::value) bf16_diff8(&cq.w[s2 * 4], &cp.w[s2 * 4], dz8);
 #pragma unroll
         for (int u = 0; u < VEC; ++u) {
           const int e = s2 * VEC + u;
           const float zq = cq.get(e), zp = cp.get(e);
           float q = 0.f;
           if (!ECACHE || decltype(with_res)::value) q = fexp2(fmaf(zq, kLog2e, -lse_q2));
-          if constexpr (ECACHE) g[u] = fma_f16(hw[u / 2], u & 1, fmaf(lsc, zq - zp, csc), 0.f);
-          else g[u] = q * fmaf(lam, zq - zp, c1);
+          if constexpr (ECACHE) {
+            const float dz = decltype(with_res)::value ? zq - zp : dz8[u];
+            g[u] = fma_f16(hw[u / 2], u & 1, fmaf(lsc, dz, csc), 0.f);
+          } else {
+            g[u] = q * fmaf(lam, zq - zp, c1);
+          }
           if constexpr (decltype(with_res)::value)
             Zpart += fmaxf(0.f, fexp2(fmaf(zp, kLog2e, -lse_p2)) - q);
         }
