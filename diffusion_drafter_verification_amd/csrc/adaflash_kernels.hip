@@ -338,6 +338,34 @@ struct Chunk {
   }
 };
 
+// Largest entry of a chunk (exact, as a float).  bf16: packed 16-bit integer
+// maxima and minima of the raw words, two entries per instruction and no
+// unpacking.  Patterns of non-negative values order like signed integers,
+// while among negative values the largest has the smallest signed pattern:
+// the maximum is the largest signed pattern if that is non-negative, else
+// the smallest one.
+template <bool BF16>
+__device__ __forceinline__ float chunk_max(const Chunk<BF16>& c) {
+  if constexpr (BF16) {
+    typedef short s16x2_t __attribute__((ext_vector_type(2)));
+    s16x2_t mx = {-32768, -32768}, mn = {32767, 32767};
+#pragma unroll
+    for (int q = 0; q < Chunk<BF16>::NW; ++q) {
+      const s16x2_t w = __builtin_bit_cast(s16x2_t, c.w[q]);
+      mx = __builtin_elementwise_max(mx, w);
+      mn = __builtin_elementwise_min(mn, w);
+    }
+    const int a = max((int)mx.x, (int)mx.y);
+    const int bits = a >= 0 ? a : min((int)mn.x, (int)mn.y);
+    return __uint_as_float((uint32_t)(uint16_t)bits << 16);
+  } else {
+    float m = neg_inf();
+#pragma unroll
+    for (int e = 0; e < kElems; ++e) m = fmaxf(m, c.get(e));
+    return m;
+  }
+}
+
 template <bool BF16>
 __device__ __forceinline__ int entry_index(int v0, int e) {
   constexpr int VEC = Chunk<BF16>::VEC;
@@ -534,7 +562,7 @@ __device__ RowStats combine_part1(const KParams& P, int r, float kT, float* red)
 
 struct FinShared {
   float red[kWaves * 8];
-  float f[12];
+  float f[16];
   int i[8];
   float slot[kWaves][kElems / 4];   // per-wave slot totals of the in-chunk scan
   unsigned long long amax[72];      // greedy: per-row (value, index) argmax keys
@@ -831,13 +859,8 @@ __global__ __launch_bounds__(kThreads) void row_kernel(KParams P) {
   load_chunk<BF16, ALIGNED>(cp, trow, v0, V);
   if (need_q) load_chunk<BF16, ALIGNED>(cq, drow, v0, V);
 
-  float mp = neg_inf(), mq = neg_inf();
-#pragma unroll
-  for (int e = 0; e < kElems; ++e) mp = fmaxf(mp, cp.get(e));
-  if (need_q) {
-#pragma unroll
-    for (int e = 0; e < kElems; ++e) mq = fmaxf(mq, cq.get(e));
-  }
+  float mp = chunk_max<BF16>(cp), mq = neg_inf();
+  if (need_q) mq = chunk_max<BF16>(cq);
   cp.opaque();
   cq.opaque();
   {
@@ -1085,7 +1108,22 @@ struct SupStats {
                  // records) the lowest chunk holding it
   int nonfinite;
   float margin;  // p(x) - u q(x) of the accept test (sampled verification)
+  // Derived row values: log2 normalisers of q and p, D = lse_q - lse_p, the
+  // unclipped reverse KL, and the bound on the largest per-entry term.
+  float lse_q2, lse_p2, D, KL, bound;
 };
+
+__device__ __forceinline__ void derive_sup(float Mp, float Mq, float Sp, float Sq, float Wsum, float BA,
+                                           float (&d)[5]) {
+  const float lq = Mq * kLog2e + flog2(Sq);
+  const float lp = Mp * kLog2e + flog2(Sp);
+  const float D = (lq - lp) * kLn2;
+  d[0] = lq;
+  d[1] = lp;
+  d[2] = D;
+  d[3] = Wsum / Sq - D;
+  d[4] = (BA + fmaxf(0.f, -D)) / Sq;
+}
 
 // Accept test of sampled verification at T = 1: u q(x) < p(x).
 __device__ __forceinline__ float accept_margin(float zpx, float zqx, float u, float Mp, float Mq, float Sp,
@@ -1146,7 +1184,7 @@ __device__ SupStats combine_sup(const KParams& P, int r, FinShared& fs, float zp
     sq = pub_load(rec + 5);
     a = pub_load(rec + 6);
   };
-  float m[2], v[6];
+  float m[2], v[6], dv[5];
   if (G <= 64) {
     if (tid < 64) {
       float mp = neg_inf(), mq = neg_inf(), sp = 0.f, sq = 0.f, w = 0.f, a = neg_inf();
@@ -1159,6 +1197,11 @@ __device__ SupStats combine_sup(const KParams& P, int r, FinShared& fs, float zp
 #pragma unroll
         for (int q = 0; q < 6; ++q) fs.f[2 + q] = v[q];
         if (SAMPLED) fs.f[8] = accept_margin(zpx, zqx, u, m[0], m[1], v[0], v[1]);
+        // The derived values once here rather than in every wave.
+        float d[5];
+        derive_sup(m[0], m[1], v[0], v[1], v[2], v[3], d);
+#pragma unroll
+        for (int q = 0; q < 5; ++q) fs.f[9 + q] = d[q];
       }
     }
     __syncthreads();
@@ -1166,12 +1209,15 @@ __device__ SupStats combine_sup(const KParams& P, int r, FinShared& fs, float zp
     m[1] = fs.f[1];
 #pragma unroll
     for (int q = 0; q < 6; ++q) v[q] = fs.f[2 + q];
+#pragma unroll
+    for (int q = 0; q < 5; ++q) dv[q] = fs.f[9 + q];
   } else {
     float mp = neg_inf(), mq = neg_inf(), sp = 0.f, sq = 0.f, w = 0.f, a = neg_inf();
     int idx = kIntMax;
     if (tid < G) load(tid, mp, mq, sp, sq, w, a, idx);
     reduce(mp, mq, sp, sq, w, a, idx, tid < G, m, v, true);
     if (SAMPLED && tid == 0) fs.f[8] = accept_margin(zpx, zqx, u, m[0], m[1], v[0], v[1]);
+    derive_sup(m[0], m[1], v[0], v[1], v[2], v[3], dv);
     __syncthreads();
   }
   SupStats s;
@@ -1184,6 +1230,11 @@ __device__ SupStats combine_sup(const KParams& P, int r, FinShared& fs, float zp
   s.xstar = __float_as_int(uniform(v[4]));
   s.nonfinite = __float_as_int(uniform(v[5])) != 0;
   s.margin = SAMPLED ? uniform(fs.f[8]) : 0.f;
+  s.lse_q2 = uniform(dv[0]);
+  s.lse_p2 = uniform(dv[1]);
+  s.D = uniform(dv[2]);
+  s.KL = uniform(dv[3]);
+  s.bound = uniform(dv[4]);
   return s;
 }
 
@@ -1266,13 +1317,8 @@ __global__ __launch_bounds__(kThreads, (sup_min_waves<BF16, ALIGNED, VMODE>())) 
       zqx = sload_logit<BF16>(drow, xtok);
     }
   }
-  float mp = neg_inf(), mq = neg_inf();
-#pragma unroll
-  for (int e = 0; e < kElems; ++e) mp = fmaxf(mp, cp.get(e));
-  if (draft_row) {
-#pragma unroll
-    for (int e = 0; e < kElems; ++e) mq = fmaxf(mq, cq.get(e));
-  }
+  float mp = chunk_max<BF16>(cp), mq = neg_inf();
+  if (draft_row) mq = chunk_max<BF16>(cq);
   cp.opaque();
   cq.opaque();
   float Mw[2] = {mp, mq};
@@ -1358,13 +1404,9 @@ __global__ __launch_bounds__(kThreads, (sup_min_waves<BF16, ALIGNED, VMODE>())) 
   }
   const SupStats st = combine_sup<SAMPLED, DEFER_X>(P, r, fs, zpx, zqx, u_acc);
   const bool earlier_rejected = SAMPLED && fs.i[0] != 0;
-  const float lse_q2 = uniform(st.Mq * kLog2e + flog2(st.Sq));
-  const float lse_p2 = uniform(st.Mp * kLog2e + flog2(st.Sp));
-  const float D = uniform((lse_q2 - lse_p2) * kLn2);
-  const float KL = uniform(st.Wsum / st.Sq - D);
-  const float bound = (st.BA + fmaxf(0.f, -D)) / st.Sq;
+  const float lse_q2 = st.lse_q2, lse_p2 = st.lse_p2, D = st.D, KL = st.KL;
   const float c = P.clip_c, lam = P.lambda;
-  const bool fast = !st.nonfinite && bound <= 0.999f * c;
+  const bool fast = !st.nonfinite && st.bound <= 0.999f * c;
   // (A row maximum at the padding value means a row of -inf only.)
   const float pad = __uint_as_float(BF16 ? 0xff7f0000u : 0xff7fffffu);
   if (tid == 0 && j == 0 && !(st.Mp < __builtin_inff() && st.Mp > pad && st.Sp > 0.f && st.Sq > 0.f))
