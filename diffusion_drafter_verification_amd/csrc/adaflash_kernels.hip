@@ -1621,6 +1621,169 @@ __global__ __launch_bounds__(kThreads, (sup_min_waves<BF16, ALIGNED, VMODE>())) 
   }
 }
 
+// -------------------------------------------- sampled verification (no OPD)
+
+// Sampled verification without supervision needs the row statistics in one
+// place only (the accept test), and the residual of one row per request, so
+// it runs without any barrier between workgroups: vstat_kernel publishes the
+// chunk statistics of every row in use and exits; vres_kernel (one workgroup
+// per request and chunk) combines them, runs the accept tests, finds the
+// first rejection and, for a rejected request, computes the residual mass of
+// its chunk of that row (the one row read a second time); final_kernel draws.
+
+// Pass 1 of one (row, chunk): chunk maxima of z_p (and z_q for draft rows)
+// and sums of exp((z - m) / T), published as a part1 record.
+template <bool BF16, bool ALIGNED>
+__global__ __launch_bounds__(kThreads) void vstat_kernel(KParams P) {
+  __shared__ float red[kWaves * 8];
+  const int tid = threadIdx.x;
+  const int G = P.G, k = P.k, V = P.V;
+  const int s_ = (int)blockIdx.x / G;
+  const int j = (int)blockIdx.x - s_ * G;
+  const int b = s_ / (k + 1), i = s_ - b * (k + 1);
+  const int L = P.Lc[b];
+  if (i > L) return;
+  const int r = s_;
+  const bool draft_row = i < L;
+  const int v0 = j * kChunk;
+  const void* trow = BF16 ? (const void*)((const uint16_t*)P.target + (size_t)r * V)
+                          : (const void*)((const float*)P.target + (size_t)r * V);
+  Chunk<BF16> cp, cq;
+  load_chunk<BF16, ALIGNED>(cp, trow, v0, V);
+  if (draft_row) {
+    const void* drow = BF16 ? (const void*)((const uint16_t*)P.draft + ((size_t)b * k + i) * V)
+                            : (const void*)((const float*)P.draft + ((size_t)b * k + i) * V);
+    load_chunk<BF16, ALIGNED>(cq, drow, v0, V);
+  }
+  float m[2] = {chunk_max<BF16>(cp), draft_row ? chunk_max<BF16>(cq) : neg_inf()};
+  cp.opaque();
+  cq.opaque();
+  {
+    const int ops[2] = {OP_MAX, OP_MAX};
+    wg_reduce<2>(m, ops, red);
+  }
+  const float ap = uniform(m[0] == neg_inf() ? 0.f : -m[0] * P.kT);
+  const float aq = uniform(m[1] == neg_inf() ? 0.f : -m[1] * P.kT);
+  float sv[2] = {0.f, 0.f};
+#pragma unroll
+  for (int e = 0; e < kElems; ++e) sv[0] += fexp2(fmaf(cp.get(e), P.kT, ap));
+  if (draft_row) {
+#pragma unroll
+    for (int e = 0; e < kElems; ++e) sv[1] += fexp2(fmaf(cq.get(e), P.kT, aq));
+  }
+  const int ops[2] = {OP_SUM, OP_SUM};
+  wg_reduce_lead<2>(sv, ops, red);
+  if (tid == 0) {
+    float* rec = P.part1 + ((size_t)r * G + j) * kRec1;
+    pub_store(rec + 0, m[0]);
+    pub_store(rec + 2, sv[0]);
+    pub_store(rec + 4, m[1]);
+    pub_store(rec + 5, sv[1]);
+  }
+}
+
+// Folds a chunk record (m, s) into a running (M, S) at scale kT.
+__device__ __forceinline__ void fold_ms(float& M, float& S, float m, float s, float kT) {
+  if (m == neg_inf()) return;
+  if (M == neg_inf()) {
+    M = m;
+    S = s;
+  } else if (m > M) {
+    S = S * fexp2((M - m) * kT) + s;
+    M = m;
+  } else {
+    S += s * fexp2((m - M) * kT);
+  }
+}
+
+// One workgroup per (request b, chunk j).  Wave w takes rows w, w + 4, ...:
+// lane c folds the records of chunks c and c + 64, the wave reduces them,
+// lane 0 runs the accept test.  Every workgroup of the request does the
+// same and finds the same first rejection A; for A < L it computes the
+// residual mass sum max(0, p - q) of its chunk of row A for the finaliser.
+template <bool BF16, bool ALIGNED>
+__global__ __launch_bounds__(kThreads) void vres_kernel(KParams P) {
+  __shared__ float red[kWaves * 8];
+  __shared__ float s_row[64][4];  // Mp, SpT, Mq, SqT of every draft row
+  __shared__ int s_acc[64];
+  __shared__ int s_first;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = P.G, k = P.k, V = P.V;
+  const int b = (int)blockIdx.x / G;
+  const int j = (int)blockIdx.x - b * G;
+  const int L = P.Lc[b];
+  const int r0 = b * (k + 1);
+  for (int i = wave; i < L; i += kWaves) {
+    const int r = r0 + i;
+    float Mp = neg_inf(), Sp = 0.f, Mq = neg_inf(), Sq = 0.f;
+    for (int c = lane; c < G; c += 64) {
+      const float* rec = P.part1 + ((size_t)r * G + c) * kRec1;
+      fold_ms(Mp, Sp, pub_load(rec + 0), pub_load(rec + 2), P.kT);
+      fold_ms(Mq, Sq, pub_load(rec + 4), pub_load(rec + 5), P.kT);
+    }
+    const float RMp = wave_reduce<OP_MAX>(Mp), RMq = wave_reduce<OP_MAX>(Mq);
+    const float SpT = wave_reduce<OP_SUM>(Mp == neg_inf() ? 0.f : Sp * fexp2((Mp - RMp) * P.kT));
+    const float SqT = wave_reduce<OP_SUM>(Mq == neg_inf() ? 0.f : Sq * fexp2((Mq - RMq) * P.kT));
+    if (lane == 0) {
+      int x = P.tokens[(size_t)b * k + i];
+      if (x < 0 || x >= V) {
+        if (j == 0) flag(P.status, ADAFLASH_FLAG_BAD_TOKEN);
+        x = x < 0 ? 0 : V - 1;
+      }
+      const void* trow = BF16 ? (const void*)((const uint16_t*)P.target + (size_t)r * V)
+                              : (const void*)((const float*)P.target + (size_t)r * V);
+      const void* drow = BF16 ? (const void*)((const uint16_t*)P.draft + ((size_t)b * k + i) * V)
+                              : (const void*)((const float*)P.draft + ((size_t)b * k + i) * V);
+      const float zpx = load_logit<BF16>(trow, x), zqx = load_logit<BF16>(drow, x);
+      const float px = fexp2((zpx - RMp) * P.kT) / SpT;
+      const float qx = fexp2((zqx - RMq) * P.kT) / SqT;
+      const float u = P.uniforms[(size_t)b * (k + 1) + i];
+      const bool accept = u * qx < px;
+      s_acc[i] = accept ? 1 : 0;
+      s_row[i][0] = RMp;
+      s_row[i][1] = SpT;
+      s_row[i][2] = RMq;
+      s_row[i][3] = SqT;
+      if (j == 0) {
+        if (!(RMp < __builtin_inff()) || !(SpT > 0.f)) flag(P.status, ADAFLASH_FLAG_NONFINITE);
+        pub_store(P.rowrec + (size_t)r * kRowRec + 1, accept ? 1.f : 0.f);
+        pub_store(P.rowrec + (size_t)r * kRowRec + 2, px - u * qx);
+        if (P.margins) P.margins[(size_t)b * (k + 1) + i] = px - u * qx;
+      }
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const unsigned long long rej = __ballot(lane < L && s_acc[lane] == 0);
+    if (lane == 0) s_first = rej ? __builtin_ctzll(rej) : L;
+  }
+  __syncthreads();
+  const int A = s_first;
+  if (A >= L) return;  // every draft accepted: the bonus draw needs no residual
+
+  const int rA = r0 + A;
+  const int v0 = j * kChunk;
+  const void* trow = BF16 ? (const void*)((const uint16_t*)P.target + (size_t)rA * V)
+                          : (const void*)((const float*)P.target + (size_t)rA * V);
+  const void* drow = BF16 ? (const void*)((const uint16_t*)P.draft + ((size_t)b * k + A) * V)
+                          : (const void*)((const float*)P.draft + ((size_t)b * k + A) * V);
+  Chunk<BF16> cp, cq;
+  load_chunk<BF16, ALIGNED>(cp, trow, v0, V);
+  load_chunk<BF16, ALIGNED>(cq, drow, v0, V);
+  const float invSp = 1.f / s_row[A][1], invSq = 1.f / s_row[A][3];
+  const float ap = -s_row[A][0] * P.kT, aq = -s_row[A][2] * P.kT;
+  float z[1] = {0.f};
+#pragma unroll
+  for (int e = 0; e < kElems; ++e) {
+    const float pv = fexp2(fmaf(cp.get(e), P.kT, ap)) * invSp;
+    const float qq = fexp2(fmaf(cq.get(e), P.kT, aq)) * invSq;
+    z[0] += fmaxf(0.f, pv - qq);
+  }
+  const int o1[1] = {OP_SUM};
+  wg_reduce_lead<1>(z, o1, red);
+  if (tid == 0) pub_store(P.part2 + ((size_t)rA * G + j) * kRec2 + 2, z[0]);
+}
+
 // ----------------------------------------------------------- finalise kernel
 
 // One workgroup per request, after the row kernel: first rejection, then the
@@ -1714,7 +1877,14 @@ hipError_t dispatch_mode(const KParams& p, int grid, int opd, int vmode, bool t1
   else if (opd && vmode == 2 && t1) e = launch_sup<BF16, ALIGNED, 2>(p, grid, st);
   else if (opd) e = launch_rows<BF16, ALIGNED, true, 2, false>(p, grid, st);
   else if (vmode == 1) e = launch_rows<BF16, ALIGNED, false, 1, false>(p, grid, st);
-  else if (vmode == 2) e = launch_rows<BF16, ALIGNED, false, 2, false>(p, grid, st);
+  else if (vmode == 2) {
+    hipLaunchKernelGGL((vstat_kernel<BF16, ALIGNED>), dim3(grid), dim3(kThreads), 0, st, p);
+    e = hipGetLastError();
+    if (e == hipSuccess) {
+      hipLaunchKernelGGL((vres_kernel<BF16, ALIGNED>), dim3(p.B * p.G), dim3(kThreads), 0, st, p);
+      e = hipGetLastError();
+    }
+  }
   else return hipErrorInvalidValue;
   if (e != hipSuccess) return e;
   if (vmode == 1) return launch_final<BF16, ALIGNED, 1>(p, st);
