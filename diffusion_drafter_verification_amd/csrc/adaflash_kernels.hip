@@ -1696,11 +1696,31 @@ __device__ __forceinline__ void fold_ms(float& M, float& S, float m, float s, fl
   }
 }
 
-// One workgroup per (request b, chunk j).  Wave w takes rows w, w + 4, ...:
-// lane c folds the records of chunks c and c + 64, the wave reduces them,
-// lane 0 runs the accept test.  Every workgroup of the request does the
-// same and finds the same first rejection A; for A < L it computes the
-// residual mass sum max(0, p - q) of its chunk of row A for the finaliser.
+// Chunks of the rejected row per residual workgroup (fewer workgroups than
+// the GPU holds at once at B = 128).
+constexpr int kResChunks = 2;
+
+// Reduction inside each 16-lane row of a wave (every lane of the row gets
+// the row's result); the first four steps of wave_reduce.
+template <int OP>
+__device__ __forceinline__ float row16_reduce(float v) {
+  if constexpr (OP == OP_MAX) {
+    const float k = __int_as_float(max_key(__float_as_int(v)));
+    return __int_as_float(max_key(__float_as_int(row16_reduce<OP_MAXI>(k))));
+  }
+  v = op2<OP>(v, dpp_f<0xB1>(v));
+  v = op2<OP>(v, dpp_f<0x4E>(v));
+  v = op2<OP>(v, dpp_f<0x141>(v));
+  v = op2<OP>(v, dpp_f<0x140>(v));
+  return v;
+}
+
+// One workgroup per (request b, chunk j).  Each 16-lane row of the workgroup
+// takes one draft row (16 at a time): lane c folds the records of chunks c,
+// c + 16, ..., the lanes reduce them, the first lane runs the accept test.
+// Every workgroup of the request does the same and finds the same first
+// rejection A; for A < L it computes the residual mass sum max(0, p - q) of
+// its chunk of row A for the finaliser.
 template <bool BF16, bool ALIGNED>
 __global__ __launch_bounds__(kThreads) void vres_kernel(KParams P) {
   __shared__ float red[kWaves * 8];
@@ -1709,23 +1729,35 @@ __global__ __launch_bounds__(kThreads) void vres_kernel(KParams P) {
   __shared__ int s_first;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = P.G, k = P.k, V = P.V;
-  const int b = (int)blockIdx.x / G;
-  const int j = (int)blockIdx.x - b * G;
+  const int GH = (G + kResChunks - 1) / kResChunks;
+  const int b = (int)blockIdx.x / GH;
+  const int h = (int)blockIdx.x - b * GH;  // chunks kResChunks*h ...
+  const int j = h;                         // (workgroup h == 0 writes the row flags)
   const int L = P.Lc[b];
   const int r0 = b * (k + 1);
-  for (int i = wave; i < L; i += kWaves) {
+  const int grp = tid >> 4, l16 = tid & 15;  // 16 groups of 16 lanes
+  for (int i0 = 0; i0 < L; i0 += kThreads / 16) {
+    const int i = i0 + grp;
+    const bool live = i < L;  // uniform within the group
     const int r = r0 + i;
-    float Mp = neg_inf(), Sp = 0.f, Mq = neg_inf(), Sq = 0.f;
-    for (int c = lane; c < G; c += 64) {
-      const float* rec = P.part1 + ((size_t)r * G + c) * kRec1;
-      fold_ms(Mp, Sp, pub_load(rec + 0), pub_load(rec + 2), P.kT);
-      fold_ms(Mq, Sq, pub_load(rec + 4), pub_load(rec + 5), P.kT);
+    int x = 0;
+    float u = 0.f;
+    if (live && l16 == 0) {  // issued before the record loads
+      x = P.tokens[(size_t)b * k + i];
+      u = P.uniforms[(size_t)b * (k + 1) + i];
     }
-    const float RMp = wave_reduce<OP_MAX>(Mp), RMq = wave_reduce<OP_MAX>(Mq);
-    const float SpT = wave_reduce<OP_SUM>(Mp == neg_inf() ? 0.f : Sp * fexp2((Mp - RMp) * P.kT));
-    const float SqT = wave_reduce<OP_SUM>(Mq == neg_inf() ? 0.f : Sq * fexp2((Mq - RMq) * P.kT));
-    if (lane == 0) {
-      int x = P.tokens[(size_t)b * k + i];
+    float Mp = neg_inf(), Sp = 0.f, Mq = neg_inf(), Sq = 0.f;
+    if (live) {
+      for (int c = l16; c < G; c += 16) {
+        const float* rec = P.part1 + ((size_t)r * G + c) * kRec1;
+        fold_ms(Mp, Sp, pub_load(rec + 0), pub_load(rec + 2), P.kT);
+        fold_ms(Mq, Sq, pub_load(rec + 4), pub_load(rec + 5), P.kT);
+      }
+    }
+    const float RMp = row16_reduce<OP_MAX>(Mp), RMq = row16_reduce<OP_MAX>(Mq);
+    const float SpT = row16_reduce<OP_SUM>(Mp == neg_inf() ? 0.f : Sp * fexp2((Mp - RMp) * P.kT));
+    const float SqT = row16_reduce<OP_SUM>(Mq == neg_inf() ? 0.f : Sq * fexp2((Mq - RMq) * P.kT));
+    if (live && l16 == 0) {
       if (x < 0 || x >= V) {
         if (j == 0) flag(P.status, ADAFLASH_FLAG_BAD_TOKEN);
         x = x < 0 ? 0 : V - 1;
@@ -1737,7 +1769,6 @@ __global__ __launch_bounds__(kThreads) void vres_kernel(KParams P) {
       const float zpx = load_logit<BF16>(trow, x), zqx = load_logit<BF16>(drow, x);
       const float px = fexp2((zpx - RMp) * P.kT) / SpT;
       const float qx = fexp2((zqx - RMq) * P.kT) / SqT;
-      const float u = P.uniforms[(size_t)b * (k + 1) + i];
       const bool accept = u * qx < px;
       s_acc[i] = accept ? 1 : 0;
       s_row[i][0] = RMp;
@@ -1762,26 +1793,45 @@ __global__ __launch_bounds__(kThreads) void vres_kernel(KParams P) {
   if (A >= L) return;  // every draft accepted: the bonus draw needs no residual
 
   const int rA = r0 + A;
-  const int v0 = j * kChunk;
   const void* trow = BF16 ? (const void*)((const uint16_t*)P.target + (size_t)rA * V)
                           : (const void*)((const float*)P.target + (size_t)rA * V);
   const void* drow = BF16 ? (const void*)((const uint16_t*)P.draft + ((size_t)b * k + A) * V)
                           : (const void*)((const float*)P.draft + ((size_t)b * k + A) * V);
-  Chunk<BF16> cp, cq;
-  load_chunk<BF16, ALIGNED>(cp, trow, v0, V);
-  load_chunk<BF16, ALIGNED>(cq, drow, v0, V);
+  // All chunks' loads first, then the arithmetic.
+  Chunk<BF16> cp[kResChunks], cq[kResChunks];
+#pragma unroll
+  for (int t = 0; t < kResChunks; ++t) {
+    const int jt = kResChunks * h + t;
+    if (jt < G) {
+      load_chunk<BF16, ALIGNED>(cp[t], trow, jt * kChunk, V);
+      load_chunk<BF16, ALIGNED>(cq[t], drow, jt * kChunk, V);
+    }
+  }
   const float invSp = 1.f / s_row[A][1], invSq = 1.f / s_row[A][3];
   const float ap = -s_row[A][0] * P.kT, aq = -s_row[A][2] * P.kT;
-  float z[1] = {0.f};
+  float z[kResChunks];
+  int o[kResChunks];
 #pragma unroll
-  for (int e = 0; e < kElems; ++e) {
-    const float pv = fexp2(fmaf(cp.get(e), P.kT, ap)) * invSp;
-    const float qq = fexp2(fmaf(cq.get(e), P.kT, aq)) * invSq;
-    z[0] += fmaxf(0.f, pv - qq);
+  for (int t = 0; t < kResChunks; ++t) {
+    z[t] = 0.f;
+    o[t] = OP_SUM;
+    if (kResChunks * h + t < G) {
+#pragma unroll
+      for (int e = 0; e < kElems; ++e) {
+        const float pv = fexp2(fmaf(cp[t].get(e), P.kT, ap)) * invSp;
+        const float qq = fexp2(fmaf(cq[t].get(e), P.kT, aq)) * invSq;
+        z[t] += fmaxf(0.f, pv - qq);
+      }
+    }
   }
-  const int o1[1] = {OP_SUM};
-  wg_reduce_lead<1>(z, o1, red);
-  if (tid == 0) pub_store(P.part2 + ((size_t)rA * G + j) * kRec2 + 2, z[0]);
+  wg_reduce_lead<kResChunks>(z, o, red);
+  if (tid == 0) {
+#pragma unroll
+    for (int t = 0; t < kResChunks; ++t) {
+      const int jt = kResChunks * h + t;
+      if (jt < G) pub_store(P.part2 + ((size_t)rA * G + jt) * kRec2 + 2, z[t]);
+    }
+  }
 }
 
 // ----------------------------------------------------------- finalise kernel
@@ -1881,7 +1931,8 @@ hipError_t dispatch_mode(const KParams& p, int grid, int opd, int vmode, bool t1
     hipLaunchKernelGGL((vstat_kernel<BF16, ALIGNED>), dim3(grid), dim3(kThreads), 0, st, p);
     e = hipGetLastError();
     if (e == hipSuccess) {
-      hipLaunchKernelGGL((vres_kernel<BF16, ALIGNED>), dim3(p.B * p.G), dim3(kThreads), 0, st, p);
+      const int gh = (p.G + kResChunks - 1) / kResChunks;
+      hipLaunchKernelGGL((vres_kernel<BF16, ALIGNED>), dim3(p.B * gh), dim3(kThreads), 0, st, p);
       e = hipGetLastError();
     }
   }
