@@ -1278,13 +1278,23 @@ __global__ __launch_bounds__(kThreads, (sup_min_waves<BF16, ALIGNED, VMODE>())) 
   const int G = P.G;
   const int k = P.k, V = P.V;
   // Workgroup -> (request b, position i, chunk j); row slot r = b*(k+1) + i.
-  // Supervision alone uses positions i < k, verification also the bonus slot.
-  const int per_req = VERIFY ? k + 1 : k;
+  // Draft rows come first (slot s = b*k + i, empty for i >= L_b); the bonus
+  // rows of verification (one per request, i = L_b) close the grid, so that
+  // the grid's tail holds the short workgroups that never wait at a barrier.
   const int s_ = (int)blockIdx.x / G;
   const int j = (int)blockIdx.x - s_ * G;
-  const int b = s_ / per_req, i = s_ - b * per_req;
+  const int nd = P.B * k;
+  int b, i;
+  if (s_ < nd) {
+    b = s_ / k;
+    i = s_ - b * k;
+  } else {
+    b = s_ - nd;
+    i = -1;
+  }
   const int L = P.Lc[b];
-  if (i > L || (!VERIFY && i == L)) return;
+  if (i < 0) i = L;
+  else if (i >= L) return;
   const int r = b * (k + 1) + i;
   const bool draft_row = i < L;
   const int v0 = j * kChunk;
