@@ -62,6 +62,14 @@ def load_library() -> ctypes.CDLL:
         lib.adaflash_opd_loss_fwd_bwd.restype = i32
         lib.adaflash_opd_loss_fwd_bwd.argtypes = [i32, vp, vp, vp, i32, i32, i32, f32, f32, vp, vp,
                                                   vp, vp, vp, vp, sz, vp]
+        lib.adaflash_length_head_workspace_bytes.restype = sz
+        lib.adaflash_length_head_workspace_bytes.argtypes = [i32, i32, i32, i32]
+        lib.adaflash_length_head_forward.restype = i32
+        lib.adaflash_length_head_forward.argtypes = [vp, vp, vp, vp, f32, i32, i32, i32, i32, f32, vp, vp,
+                                                     vp, sz, vp]
+        lib.adaflash_length_head_backward.restype = i32
+        lib.adaflash_length_head_backward.argtypes = [vp, vp, vp, vp, f32, i32, i32, i32, i32, vp, vp, vp,
+                                                      vp, vp, vp, vp, vp, sz, vp]
         _lib = lib
     return _lib
 
@@ -178,4 +186,84 @@ def opd_loss_fwd_bwd(target: torch.Tensor, draft: torch.Tensor, verify_len: Opti
         ws = workspace(B, k, V, dev)
     adaflash_opd_loss_fwd_bwd(target, draft, verify_len, clip_c, lam, out["row_offsets"],
                               out["loss_ce"], out["loss_rkl"], out["grad"], out["status"], ws, stream)
+    return out
+
+
+# ------------------------------------------------------------- length head
+
+
+def adaflash_length_head_workspace_bytes(B: int, k: int, H: int, Hp: int) -> int:
+    return int(load_library().adaflash_length_head_workspace_bytes(B, k, H, Hp))
+
+
+def length_head_workspace(B: int, k: int, H: int, Hp: int, device="cuda") -> torch.Tensor:
+    n = adaflash_length_head_workspace_bytes(B, k, H, Hp)
+    if n == 0:
+        raise ValueError("invalid sizes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def _bf16(t: torch.Tensor) -> torch.Tensor:
+    if t.dtype != torch.bfloat16:
+        raise TypeError("hidden states and W1 must be bfloat16")
+    return t
+
+
+def _f32(t: torch.Tensor) -> torch.Tensor:
+    if t.dtype != torch.float32:
+        raise TypeError("b1 and w2 must be float32")
+    return t
+
+
+def adaflash_length_head_forward(hidden, W1, b1, w2, b2, gamma, a_hat, k_hat, ws, stream=None) -> None:
+    """Direct binding of adaflash_length_head_forward (see include/adaflash.h)."""
+    B, k, H = hidden.shape
+    Hp = W1.shape[0]
+    rc = load_library().adaflash_length_head_forward(
+        _ptr(_bf16(hidden)), _ptr(_bf16(W1)), _ptr(_f32(b1)), _ptr(_f32(w2)), float(b2), B, k, H, Hp,
+        float(gamma), _ptr(a_hat), _ptr(k_hat), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream))
+    _check(rc)
+
+
+def adaflash_length_head_backward(hidden, W1, b1, w2, b2, accept_len, verify_len, loss, dW1, db1, dw2, db2, ws,
+                                  stream=None) -> None:
+    """Direct binding of adaflash_length_head_backward (see include/adaflash.h)."""
+    B, k, H = hidden.shape
+    Hp = W1.shape[0]
+    rc = load_library().adaflash_length_head_backward(
+        _ptr(_bf16(hidden)), _ptr(_bf16(W1)), _ptr(_f32(b1)), _ptr(_f32(w2)), float(b2), B, k, H, Hp,
+        _ptr(accept_len), _ptr(verify_len), _ptr(loss), _ptr(dW1), _ptr(db1), _ptr(dw2), _ptr(db2), _ptr(ws),
+        ws.numel() if ws is not None else 0, _stream(stream))
+    _check(rc)
+
+
+def length_head_forward(hidden: torch.Tensor, W1: torch.Tensor, b1: torch.Tensor, w2: torch.Tensor, b2: float,
+                        gamma: float = 1.0, ws: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """Allocates the outputs and calls adaflash_length_head_forward."""
+    B, k, H = hidden.shape
+    dev = hidden.device
+    out = {"a_hat": torch.empty(B, dtype=torch.float32, device=dev),
+           "k_hat": torch.empty(B, dtype=torch.int32, device=dev)}
+    if ws is None:
+        ws = length_head_workspace(B, k, H, W1.shape[0], dev)
+    adaflash_length_head_forward(hidden, W1, b1, w2, b2, gamma, out["a_hat"], out["k_hat"], ws, stream)
+    return out
+
+
+def length_head_backward(hidden: torch.Tensor, W1: torch.Tensor, b1: torch.Tensor, w2: torch.Tensor, b2: float,
+                         accept_len: torch.Tensor, verify_len: torch.Tensor, ws: Optional[torch.Tensor] = None,
+                         stream=None) -> dict:
+    """Allocates the outputs and calls adaflash_length_head_backward."""
+    B, k, H = hidden.shape
+    Hp = W1.shape[0]
+    dev = hidden.device
+    out = {"loss": torch.empty(B, dtype=torch.float32, device=dev),
+           "dW1": torch.empty(Hp, H, dtype=torch.float32, device=dev),
+           "db1": torch.empty(Hp, dtype=torch.float32, device=dev),
+           "dw2": torch.empty(Hp, dtype=torch.float32, device=dev),
+           "db2": torch.empty(1, dtype=torch.float32, device=dev)}
+    if ws is None:
+        ws = length_head_workspace(B, k, H, Hp, dev)
+    adaflash_length_head_backward(hidden, W1, b1, w2, b2, accept_len, verify_len, out["loss"], out["dW1"],
+                                  out["db1"], out["dw2"], out["db2"], ws, stream)
     return out

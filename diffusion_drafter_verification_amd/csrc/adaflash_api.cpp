@@ -174,4 +174,92 @@ int adaflash_opd_loss_fwd_bwd(adaflash_dtype dtype, const void* target_logits,
   return run(a, workspace);
 }
 
+size_t adaflash_length_head_workspace_bytes(int B, int k, int H, int Hp) {
+  if (B < 0 || k < 1 || k > 64 || H < 16 || H > 65536 || H % 16 != 0 || Hp < 1 || Hp > 8192) return 0;
+  if ((long long)B * k >= (1LL << 24)) return 0;
+  const size_t n = lh_workspace_layout(B, k, H, Hp, nullptr, nullptr);
+  return n > 256 ? n : 256;  // (an empty batch still gets a valid, nonzero size)
+}
+
+static int lh_checks(const void* h, const void* W1, const float* b1, const float* w2, float b2, int B, int k,
+                     int H, int Hp, void* workspace, size_t workspace_bytes) {
+  if (B < 0 || k < 1 || k > 64 || H < 16 || H > 65536 || H % 16 != 0 || Hp < 1 || Hp > 8192 ||
+      (long long)B * k >= (1LL << 24))
+    return fail(ADAFLASH_E_INVALID,
+                "invalid sizes%s: need B >= 0, 1 <= k <= 64, 16 <= H <= 65536 with H %% 16 == 0, "
+                "1 <= H' <= 8192, B*k < 2^24");
+  if (B > 0 && (!h || !W1 || !b1 || !w2))
+    return fail(ADAFLASH_E_INVALID, "hidden, W1, b1 and w2 must not be NULL%s");
+  if (((uintptr_t)h & 15) || ((uintptr_t)W1 & 15))
+    return fail(ADAFLASH_E_INVALID, "hidden and W1 must be 16-byte aligned%s");
+  if (!std::isfinite(b2)) return fail(ADAFLASH_E_INVALID, "b2 must be finite%s");
+  const size_t need = lh_workspace_layout(B, k, H, Hp, nullptr, nullptr);
+  if (B > 0 && (!workspace || workspace_bytes < need))
+    return fail(ADAFLASH_E_WORKSPACE, "workspace missing or smaller than adaflash_length_head_workspace_bytes()%s");
+  return ADAFLASH_OK;
+}
+
+int adaflash_length_head_forward(const void* hidden, const void* W1, const float* b1, const float* w2, float b2,
+                                 int B, int k, int H, int Hp, float gamma, float* a_hat, int32_t* k_hat,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = lh_checks(hidden, W1, b1, w2, b2, B, k, H, Hp, workspace, workspace_bytes);
+  if (rc != ADAFLASH_OK) return rc;
+  if (!(gamma > 0.f) || std::isinf(gamma)) return fail(ADAFLASH_E_INVALID, "gamma must be finite and > 0%s");
+  if (B > 0 && !a_hat && !k_hat) return fail(ADAFLASH_E_INVALID, "a_hat and k_hat are both NULL%s");
+  LhArgs a{};
+  a.h = (const uint16_t*)hidden;
+  a.W1 = (const uint16_t*)W1;
+  a.b1 = b1;
+  a.w2 = w2;
+  a.b2 = b2;
+  a.gamma = gamma;
+  a.B = B;
+  a.k = k;
+  a.H = H;
+  a.Hp = Hp;
+  a.a_hat = a_hat;
+  a.k_hat = k_hat;
+  a.stream = (hipStream_t)stream;
+  lh_workspace_layout(B, k, H, Hp, (char*)workspace, &a.ws);
+  const hipError_t e = lh_launch(a);
+  if (e != hipSuccess) return fail(ADAFLASH_E_HIP, "HIP launch failed: %s", hipGetErrorString(e));
+  g_err[0] = 0;
+  return ADAFLASH_OK;
+}
+
+int adaflash_length_head_backward(const void* hidden, const void* W1, const float* b1, const float* w2, float b2,
+                                  int B, int k, int H, int Hp, const int32_t* accept_len,
+                                  const int32_t* verify_len, float* loss, float* dW1, float* db1, float* dw2,
+                                  float* db2, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = lh_checks(hidden, W1, b1, w2, b2, B, k, H, Hp, workspace, workspace_bytes);
+  if (rc != ADAFLASH_OK) return rc;
+  if (!dW1 || !db1 || !dw2 || !db2) return fail(ADAFLASH_E_INVALID, "dW1, db1, dw2 and db2 must not be NULL%s");
+  if (B > 0 && (!accept_len || !verify_len || !loss))
+    return fail(ADAFLASH_E_INVALID, "accept_len, verify_len and loss must not be NULL%s");
+  LhArgs a{};
+  a.h = (const uint16_t*)hidden;
+  a.W1 = (const uint16_t*)W1;
+  a.b1 = b1;
+  a.w2 = w2;
+  a.b2 = b2;
+  a.gamma = 1.f;
+  a.B = B;
+  a.k = k;
+  a.H = H;
+  a.Hp = Hp;
+  a.accept_len = accept_len;
+  a.verify_len = verify_len;
+  a.loss = loss;
+  a.dW1 = dW1;
+  a.db1 = db1;
+  a.dw2 = dw2;
+  a.db2 = db2;
+  a.stream = (hipStream_t)stream;
+  lh_workspace_layout(B, k, H, Hp, (char*)workspace, &a.ws);
+  const hipError_t e = lh_launch(a);
+  if (e != hipSuccess) return fail(ADAFLASH_E_HIP, "HIP launch failed: %s", hipGetErrorString(e));
+  g_err[0] = 0;
+  return ADAFLASH_OK;
+}
+
 }  // extern "C"

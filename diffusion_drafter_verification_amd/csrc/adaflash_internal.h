@@ -64,4 +64,38 @@ struct LaunchArgs {
 // launch error.
 hipError_t launch(const LaunchArgs& a);
 
+// Adaptive length head (adaflash_length_head.hip).
+struct LhWorkspace {
+  float* z1;         // [B*k, Hp] projection before bias and SiLU
+  float* hbar;       // [B, Hp] pooled vectors (backward)
+  float* ds;         // [B] d loss / d logit (backward)
+  uint16_t* dzh;     // [Hp, Mp] dZ1^T, bf16 high part (backward)
+  uint16_t* dzl;     // [Hp, Mp] dZ1^T, bf16 remainder (backward)
+  float* db1_part;   // [ceil(B*k/64), Hp] per-tile sums for db1 (backward)
+};
+
+size_t lh_workspace_layout(int B, int k, int H, int Hp, char* base, LhWorkspace* ws);
+
+struct LhArgs {
+  const uint16_t* h;   // [B, k, H] bf16
+  const uint16_t* W1;  // [Hp, H] bf16
+  const float* b1;     // [Hp]
+  const float* w2;     // [Hp]
+  float b2, gamma;
+  int B, k, H, Hp;
+  float* a_hat;        // [B] or null
+  int32_t* k_hat;      // [B] or null
+  const int32_t* accept_len;  // [B]: backward when non-null
+  const int32_t* verify_len;  // [B]
+  float* loss;         // [B]
+  float* dW1;          // [Hp, H]
+  float* db1;          // [Hp]
+  float* dw2;          // [Hp]
+  float* db2;          // [1]
+  LhWorkspace ws;
+  hipStream_t stream;
+};
+
+hipError_t lh_launch(const LhArgs& a);
+
 }  // namespace adaflash

@@ -159,6 +159,58 @@ ADAFLASH_API int adaflash_opd_loss_fwd_bwd(adaflash_dtype dtype, const void* tar
                               int32_t* status_flags, void* workspace, size_t workspace_bytes,
                               void* stream);
 
+/*
+ * Adaptive length head: the step before verification (it produces the verify
+ * lengths) and after it (it learns from the accept lengths).  AdaFlash review
+ * (ZH), section 2.2 "Adaptive Length Head", and AdaFlash review (EN),
+ * Algorithm 3 and "Online Update of the Length Head, Derived":
+ *   z[b,i]  = W1 h[b,i] + b1            per draft position i < k
+ *   hbar[b] = (1/k) sum_i SiLU(z[b,i])  mean over the block
+ *   a_hat[b] = sigmoid(w2 . hbar[b] + b2)   predicted accept rate
+ *   k_hat[b] = clamp(floor(gamma a_hat[b] k), 1, k)
+ *   loss[b] = (a_hat[b] - A_b / L_b)^2 with A_b accepted of the L_b verified
+ *   drafts; the gradient reaches the head's parameters only (the hidden
+ *   states are detached from the drafter).
+ * Shapes: hidden [B, k, H] bf16 (row-major, 16-byte aligned, H a multiple of
+ * 16, 16 <= H <= 65536), W1 [H', H] bf16 (16-byte aligned, 1 <= H' <= 8192),
+ * b1 [H'] fp32, w2 [H'] fp32, b2 a float, 1 <= k <= 64, B*k < 2^24.  The two
+ * dense products run on the matrix cores with fp32 accumulation.
+ */
+
+/* Bytes of device workspace the length-head entry points need (0 on invalid
+ * sizes).  The workspace needs no initialisation. */
+ADAFLASH_API size_t adaflash_length_head_workspace_bytes(int B, int k, int H, int Hp);
+
+/*
+ * adaflash_length_head_forward -- predicted accept rate and verify length.
+ *   a_hat [B] fp32 out or NULL   sigmoid output (before gamma).
+ *   k_hat [B] int32 out or NULL  clamp(floor(gamma a_hat k), 1, k), computed
+ *                                in fp32 from a_hat; usable as verify_len.
+ *   gamma > 0, finite            load scale (1 by default on the pages).
+ * At least one of a_hat, k_hat must be non-NULL.  Returns ADAFLASH_OK or a
+ * negative adaflash_status (nothing enqueued on error).
+ */
+ADAFLASH_API int adaflash_length_head_forward(const void* hidden, const void* W1, const float* b1,
+                                 const float* w2, float b2, int B, int k, int H, int Hp, float gamma,
+                                 float* a_hat, int32_t* k_hat, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/*
+ * adaflash_length_head_backward -- loss and head gradients for one round.
+ *   accept_len [B] int32   A_b from adaflash_verify (clamped to [0, L_b]).
+ *   verify_len [B] int32   L_b, the verify length used (clamped to [1, k]).
+ *   loss [B] fp32 out      (a_hat - A/L)^2 per request.
+ *   dW1 [H', H], db1 [H'], dw2 [H'], db2 [1]  fp32 out: gradients of the SUM
+ *                          of the losses over the batch (overwritten).
+ * The forward pass is recomputed (same arithmetic as the forward entry
+ * point).  Returns ADAFLASH_OK or a negative adaflash_status.
+ */
+ADAFLASH_API int adaflash_length_head_backward(const void* hidden, const void* W1, const float* b1,
+                                  const float* w2, float b2, int B, int k, int H, int Hp,
+                                  const int32_t* accept_len, const int32_t* verify_len, float* loss,
+                                  float* dW1, float* db1, float* dw2, float* db2, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

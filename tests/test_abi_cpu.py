@@ -113,3 +113,55 @@ def test_opd_rejects_bad_arguments(lib):
     assert call(ro=None) == -1
     assert call(wsb=0) == -2
     assert call(k=100) == -1
+
+
+# ------------------------------------------------------------- length head
+
+def test_length_head_workspace_bytes(lib):
+    f = lib.adaflash_length_head_workspace_bytes
+    f.restype = ctypes.c_size_t
+    assert f(128, 16, 4096, 256) > 0
+    assert f(0, 16, 4096, 256) > 0
+    assert f(4, 16, 4096 + 8, 256) == 0     # H not a multiple of 16
+    assert f(4, 16, 8, 256) == 0            # H < 16
+    assert f(4, 0, 64, 8) == 0
+    assert f(4, 65, 64, 8) == 0
+    assert f(4, 16, 64, 0) == 0
+    assert f(4, 16, 64, 8193) == 0
+    assert f(256, 16, 4096, 256) > f(128, 16, 4096, 256)
+
+
+FAKE_ALIGNED = 0x10000
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(H=24), -1), (dict(k=0), -1), (dict(Hp=0), -1), (dict(gamma=0.0), -1), (dict(gamma=float("inf")), -1),
+    (dict(h=None), -1), (dict(h=FAKE_ALIGNED + 2), -1), (dict(W1=FAKE_ALIGNED + 8), -1),
+    (dict(ws=None), -2), (dict(wsb=16), -2), (dict(b2=float("nan")), -1), (dict(a_hat=None, k_hat=None), -1),
+])
+def test_length_head_forward_rejects_bad_arguments(lib, kw, code):
+    a = dict(h=FAKE_ALIGNED, W1=FAKE_ALIGNED, b1=FAKE_ALIGNED, w2=FAKE_ALIGNED, b2=0.0, B=4, k=16, H=64, Hp=8,
+             gamma=1.0, a_hat=FAKE_ALIGNED, k_hat=FAKE_ALIGNED, ws=FAKE_ALIGNED, wsb=1 << 30)
+    a.update(kw)
+    f = lib.adaflash_length_head_forward
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    f.restype = i32
+    f.argtypes = [vp, vp, vp, vp, f32, i32, i32, i32, i32, f32, vp, vp, vp, sz, vp]
+    rc = f(a["h"], a["W1"], a["b1"], a["w2"], a["b2"], a["B"], a["k"], a["H"], a["Hp"], a["gamma"], a["a_hat"],
+           a["k_hat"], a["ws"], a["wsb"], None)
+    assert rc == code
+    lib.adaflash_last_error.restype = ctypes.c_char_p
+    assert lib.adaflash_last_error()
+
+
+def test_length_head_backward_rejects_bad_arguments(lib):
+    f = lib.adaflash_length_head_backward
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    f.restype = i32
+    f.argtypes = [vp, vp, vp, vp, f32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    P = FAKE_ALIGNED
+    # Missing gradient outputs, missing accept lengths, bad sizes: rejected before any launch.
+    assert f(P, P, P, P, 0.0, 4, 16, 64, 8, P, P, P, None, P, P, P, P, 1 << 30, None) == -1
+    assert f(P, P, P, P, 0.0, 4, 16, 64, 8, None, P, P, P, P, P, P, P, 1 << 30, None) == -1
+    assert f(P, P, P, P, 0.0, 4, 16, 40, 8, P, P, P, P, P, P, P, P, 1 << 30, None) == -1
+    assert f(P, P, P, P, 0.0, 4, 16, 64, 8, P, P, P, P, P, P, P, P, 16, None) == -2

@@ -212,3 +212,32 @@ def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
     u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
     return u.astype(np.uint16)
+
+
+# ------------------------------------------------------------- length head
+
+@dataclass
+class LengthHeadBatch:
+    hidden: np.ndarray      # [B, k, H] bf16 bits
+    W1: np.ndarray          # [Hp, H] bf16 bits
+    b1: np.ndarray          # [Hp] float32
+    w2: np.ndarray          # [Hp] float32
+    b2: float
+    accept_len: np.ndarray  # [B] int32, A_b in [0, L_b]
+    verify_len: np.ndarray  # [B] int32, L_b in [1, k]
+
+
+def length_head_inputs(B: int, k: int = 16, H: int = 4096, Hp: int = 256, seed: int = SEED_BASE + 21
+                       ) -> LengthHeadBatch:
+    """Synthetic hidden states and head weights for the adaptive length head:
+    h ~ N(0, 1) and W1 ~ N(0, 1/H) (so the projection is about N(0, 1)), both
+    rounded to bf16; b1 ~ N(0, 0.1^2), w2 ~ N(0, 4/Hp), b2 = 0.3; verify
+    lengths U{1..k} and accept lengths U{0..L} (numpy's seeded generator)."""
+    rng = np.random.default_rng(seed)
+    hidden = f32_to_bf16_bits(rng.standard_normal((B, k, H), dtype=np.float32))
+    W1 = f32_to_bf16_bits((rng.standard_normal((Hp, H)) / np.sqrt(H)).astype(np.float32))
+    b1 = (0.1 * rng.standard_normal(Hp)).astype(np.float32)
+    w2 = (2.0 / np.sqrt(Hp) * rng.standard_normal(Hp)).astype(np.float32)
+    vl = rng.integers(1, k + 1, size=B).astype(np.int32)
+    al = np.array([rng.integers(0, L + 1) for L in vl], dtype=np.int32)
+    return LengthHeadBatch(hidden=hidden, W1=W1, b1=b1, w2=w2, b2=0.3, accept_len=al, verify_len=vl)
