@@ -66,12 +66,15 @@ hipError_t launch(const LaunchArgs& a);
 
 // Adaptive length head (adaflash_length_head.hip).
 struct LhWorkspace {
-  float* z1;         // [B*k, Hp] projection before bias and SiLU
+  float* z1;         // [S, B*k, Hp] split-K slices of the projection
+  float* zsum;       // [B*k, Hp] their sum
   float* hbar;       // [B, Hp] pooled vectors (backward)
   float* ds;         // [B] d loss / d logit (backward)
   uint16_t* dzh;     // [Hp, Mp] dZ1^T, bf16 high part (backward)
   uint16_t* dzl;     // [Hp, Mp] dZ1^T, bf16 remainder (backward)
   float* db1_part;   // [ceil(B*k/64), Hp] per-tile sums for db1 (backward)
+  uint16_t* hT;      // [H, Mp] transposed hidden states (backward)
+  float* dw_part;    // [S, Hp, H] split-K partial sums of dW1 (backward)
 };
 
 size_t lh_workspace_layout(int B, int k, int H, int Hp, char* base, LhWorkspace* ws);

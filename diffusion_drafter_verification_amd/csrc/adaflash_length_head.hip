@@ -42,36 +42,101 @@ __device__ __forceinline__ float sigmoidf_(float x) { return 1.f / (1.f + __expf
 // accumulator register r of lane l is D[8 (r / 4) + 4 (l / 32) + r % 4][l % 32].
 __device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
-// C[M x N] (fp32, row stride ldc) = A[M x K] . B[N x K]^T, A and B bf16 with
-// row strides lda, ldb (elements), K a multiple of 16, rows 16-byte aligned.
-__global__ __launch_bounds__(kLhThreads) void lh_gemm_tn(const uint16_t* __restrict__ A, int lda,
-                                                          const uint16_t* __restrict__ Bm, int ldb,
-                                                          float* __restrict__ C, int ldc, int M, int N, int K) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // Row tiles along x (up to 2^24 rows), column tiles along y.
-  const int m0 = blockIdx.x * kTile + 32 * (wave >> 1);
-  const int n0 = blockIdx.y * kTile + 32 * (wave & 1);
-  const int ra = m0 + (lane & 31), rb = n0 + (lane & 31);
-  const int ko = 8 * (lane >> 5);
-  const bool va = ra < M, vb = rb < N;
-  const uint16_t* pa = A + (size_t)(va ? ra : 0) * lda + ko;
-  const uint16_t* pb = Bm + (size_t)(vb ? rb : 0) * ldb + ko;
-  f32x16_t acc = {};
+// Split-K product: slice z = blockIdx.z of the reduction, C_z[M x N] (fp32,
+// row stride N, slice stride M N) = A[M x K_z] . B[N x K_z]^T with A (and,
+// with TWO_A, A + A2) and B bf16, rows of stride lda / ldb elements, K a
+// multiple of 16, rows 16-byte aligned.  The workgroup stages 64-wide steps
+// of the reduction through LDS (each row's 128 bytes read by eight adjacent
+// threads), then every wave multiplies its 32 x 32 tile from LDS.
+constexpr int kKs = 64;           // reduction step staged per round
+constexpr int kLdsRow = kKs + 8;  // bf16 per LDS row (16 bytes of padding)
+
+template <bool TWO_A>
+__global__ __launch_bounds__(kLhThreads) void lh_gemm_tn(const uint16_t* __restrict__ A, const uint16_t* __restrict__ A2,
+                                                          int lda, const uint16_t* __restrict__ Bm, int ldb,
+                                                          float* __restrict__ C, int M, int N, int K, int kslice) {
+  __shared__ __attribute__((aligned(16))) uint16_t sa[TWO_A ? 2 : 1][kTile * kLdsRow];
+  __shared__ __attribute__((aligned(16))) uint16_t sb[kTile * kLdsRow];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // Row tiles along x (up to 2^24 rows), column tiles along y, slices along z.
+  const int mt0 = blockIdx.x * kTile, nt0 = blockIdx.y * kTile;
+  const int kb = blockIdx.z * kslice;
+  const int ke = min(K, kb + kslice);
+  // Staging: thread t moves 16 bytes of rows t / 8 and t / 8 + 32, chunk t % 8.
+  const int lr = tid >> 3, lc = (tid & 7) * 8;
   const u32x4_t zero = {0u, 0u, 0u, 0u};
-#pragma unroll 4
-  for (int k0 = 0; k0 < K; k0 += 16) {
-    const u32x4_t a = va ? *(const u32x4_t*)(pa + k0) : zero;
-    const u32x4_t b = vb ? *(const u32x4_t*)(pb + k0) : zero;
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
-                                                  acc, 0, 0, 0);
+  f32x16_t acc = {};
+  const int wr = 32 * (wave >> 1), wc = 32 * (wave & 1);
+  const int ko = 8 * (lane >> 5);
+  for (int k0 = kb; k0 < ke; k0 += kKs) {
+    u32x4_t ga[2], ga2[2], gb[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = lr + 32 * h;
+      const int kk = k0 + lc;
+      const bool okk = kk < ke;
+      const int ra = mt0 + r, rb = nt0 + r;
+      ga[h] = (ra < M && okk) ? *(const u32x4_t*)(A + (size_t)ra * lda + kk) : zero;
+      if constexpr (TWO_A) ga2[h] = (ra < M && okk) ? *(const u32x4_t*)(A2 + (size_t)ra * lda + kk) : zero;
+      gb[h] = (rb < N && okk) ? *(const u32x4_t*)(Bm + (size_t)rb * ldb + kk) : zero;
+    }
+    __syncthreads();  // the previous round's fragments are consumed
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = lr + 32 * h;
+      *(u32x4_t*)&sa[0][r * kLdsRow + lc] = ga[h];
+      if constexpr (TWO_A) *(u32x4_t*)&sa[1][r * kLdsRow + lc] = ga2[h];
+      *(u32x4_t*)&sb[r * kLdsRow + lc] = gb[h];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < kKs / 16; ++t) {
+      const int kc = 16 * t + ko;
+      const u32x4_t a = *(const u32x4_t*)&sa[0][(wr + (lane & 31)) * kLdsRow + kc];
+      const u32x4_t b = *(const u32x4_t*)&sb[(wc + (lane & 31)) * kLdsRow + kc];
+      const bf16x8_t bb = __builtin_bit_cast(bf16x8_t, b);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), bb, acc, 0, 0, 0);
+      if constexpr (TWO_A) {
+        const u32x4_t a2 = *(const u32x4_t*)&sa[1][(wr + (lane & 31)) * kLdsRow + kc];
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a2), bb, acc, 0, 0, 0);
+      }
+    }
   }
-  const int col = n0 + (lane & 31);
+  float* Cz = C + (size_t)blockIdx.z * M * N;
+  const int col = nt0 + wc + (lane & 31);
   if (col < N) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int row = m0 + acc_row(r, lane);
-      if (row < M) C[(size_t)row * ldc + col] = acc[r];
+      const int row = mt0 + wr + acc_row(r, lane);
+      if (row < M) Cz[(size_t)row * N + col] = acc[r];
     }
+  }
+}
+
+// out[i] = sum over the S slices of part[s][i], in slice order.
+__global__ __launch_bounds__(kLhThreads) void lh_sum_slices(const float* __restrict__ part, int S, size_t n,
+                                                             float* __restrict__ out) {
+  for (size_t i = (size_t)blockIdx.x * kLhThreads + threadIdx.x; i < n; i += (size_t)gridDim.x * kLhThreads) {
+    float a = 0.f;
+    for (int z = 0; z < S; ++z) a += part[(size_t)z * n + i];
+    out[i] = a;
+  }
+}
+
+// hT [H x Mp] = h^T (bf16), zero for m >= M, through a 64 x 64 LDS tile.
+__global__ __launch_bounds__(kLhThreads) void lh_transpose(const uint16_t* __restrict__ h, int M, int H, int Mp,
+                                                            uint16_t* __restrict__ hT) {
+  __shared__ uint16_t t[kTile][kTile + 2];
+  const int m0 = blockIdx.x * kTile, c0 = blockIdx.y * kTile;
+  const int tc = threadIdx.x & 63, tr = threadIdx.x >> 6;
+  for (int rr = tr; rr < kTile; rr += 4) {
+    const int m = m0 + rr, c = c0 + tc;
+    t[rr][tc] = (m < M && c < H) ? h[(size_t)m * H + c] : (uint16_t)0;
+  }
+  __syncthreads();
+  for (int cc = tr; cc < kTile; cc += 4) {
+    const int c = c0 + cc, m = m0 + tc;
+    if (c < H && m < Mp) hT[(size_t)c * Mp + m] = t[tc][cc];
   }
 }
 
@@ -102,6 +167,7 @@ __global__ __launch_bounds__(kLhThreads) void lh_pool(const float* __restrict__ 
   for (int n = threadIdx.x; n < Hp; n += kLhThreads) {
     const float bias = b1[n];
     float acc = 0.f;
+#pragma unroll 8
     for (int i = 0; i < k; ++i) {
       const float z = Z1[((size_t)b * k + i) * Hp + n] + bias;
       acc += z * sigmoidf_(z);
@@ -185,9 +251,11 @@ __global__ __launch_bounds__(kLhThreads) void lh_small_grads(const float* __rest
   __shared__ float red[4];
   for (int n = threadIdx.x; n < Hp; n += kLhThreads) {
     float a = 0.f;
+#pragma unroll 8
     for (int t = 0; t < ntiles; ++t) a += db1_part[(size_t)t * Hp + n];
     db1[n] = a;
     float w = 0.f;
+#pragma unroll 8
     for (int b = 0; b < B; ++b) w = fmaf(ds[b], hbar[(size_t)b * Hp + n], w);
     dw2[n] = w;
   }
@@ -197,45 +265,21 @@ __global__ __launch_bounds__(kLhThreads) void lh_small_grads(const float* __rest
   if (threadIdx.x == 0) *db2 = tot;
 }
 
-// dW1 [H' x H] = (dzh + dzl) [H' x Mp] . h [M x H]: the reduction runs over
-// the M rows of h; lane l gathers h[8 (l / 32) + 0..7 + m0][col] with 2-byte
-// loads.
-__global__ __launch_bounds__(kLhThreads) void lh_gemm_dw(const uint16_t* __restrict__ dzh,
-                                                          const uint16_t* __restrict__ dzl, int Mp,
-                                                          const uint16_t* __restrict__ h, int M, int H,
-                                                          float* __restrict__ dW1, int Hp) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r0 = blockIdx.y * kTile + 32 * (wave >> 1);  // rows of dW1 (n)
-  const int c0 = blockIdx.x * kTile + 32 * (wave & 1);   // columns of dW1 (h feature)
-  const int ra = r0 + (lane & 31), col = c0 + (lane & 31);
-  const int ko = 8 * (lane >> 5);
-  const bool va = ra < Hp, vc = col < H;
-  const uint16_t* pah = dzh + (size_t)(va ? ra : 0) * Mp + ko;
-  const uint16_t* pal = dzl + (size_t)(va ? ra : 0) * Mp + ko;
-  const uint16_t* pb = h + (vc ? col : 0);
-  f32x16_t acc = {};
-  const u32x4_t zero = {0u, 0u, 0u, 0u};
-  for (int k0 = 0; k0 < Mp; k0 += 16) {
-    const u32x4_t ah = va ? *(const u32x4_t*)(pah + k0) : zero;
-    const u32x4_t al = va ? *(const u32x4_t*)(pal + k0) : zero;
-    uint32_t g[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int m = k0 + ko + t;
-      g[t] = (vc && m < M) ? (uint32_t)pb[(size_t)m * H] : 0u;
-    }
-    const u32x4_t bv = {g[0] | (g[1] << 16), g[2] | (g[3] << 16), g[4] | (g[5] << 16), g[6] | (g[7] << 16)};
-    const bf16x8_t bb = __builtin_bit_cast(bf16x8_t, bv);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ah), bb, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, al), bb, acc, 0, 0, 0);
-  }
-  if (vc) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = r0 + acc_row(r, lane);
-      if (row < Hp) dW1[(size_t)row * H + col] = acc[r];
-    }
-  }
+// Split of a reduction of length K for a product with `tiles` output tiles:
+// enough slices for about 1024 workgroups, each slice a multiple of 16 and at
+// least 256 long.
+struct Split {
+  int S, kslice;
+};
+Split split_k(int K, long long tiles) {
+  if (tiles < 1) tiles = 1;  // (an empty product)
+  long long want = (1024 + tiles - 1) / tiles;
+  long long maxs = K / 256 > 0 ? K / 256 : 1;
+  int S = (int)(want < 1 ? 1 : (want > maxs ? maxs : want));
+  int ks = (K + S - 1) / S;
+  ks = ks < 16 ? 16 : (ks + 15) & ~15;
+  S = K > 0 ? (K + ks - 1) / ks : 1;
+  return {S, ks};
 }
 
 }  // namespace
@@ -244,27 +288,34 @@ size_t lh_workspace_layout(int B, int k, int H, int Hp, char* base, LhWorkspace*
   const size_t M = (size_t)B * k;
   const size_t Mp = (M + 15) & ~size_t(15);
   const size_t ntiles = (M + kTile - 1) / kTile;
+  const Split sf = split_k(H, (long long)ntiles * ((Hp + kTile - 1) / kTile));
+  const Split sb = split_k((int)Mp, (long long)((Hp + kTile - 1) / kTile) * ((H + kTile - 1) / kTile));
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t at = off;
     off = (off + bytes + 255) & ~size_t(255);
     return base ? base + at : nullptr;
   };
-  char* z1 = take(sizeof(float) * M * Hp);
+  char* z1 = take(sizeof(float) * sf.S * M * Hp);
+  char* zsum = take(sizeof(float) * M * Hp);
   char* hbar = take(sizeof(float) * (size_t)B * Hp);
   char* ds = take(sizeof(float) * (size_t)B);
   char* dzh = take(sizeof(uint16_t) * Mp * Hp);
   char* dzl = take(sizeof(uint16_t) * Mp * Hp);
   char* part = take(sizeof(float) * ntiles * Hp);
+  char* hT = take(sizeof(uint16_t) * (size_t)H * Mp);
+  char* dwp = take(sizeof(float) * sb.S * (size_t)Hp * H);
   if (ws) {
     ws->z1 = (float*)z1;
+    ws->zsum = (float*)zsum;
     ws->hbar = (float*)hbar;
     ws->ds = (float*)ds;
     ws->dzh = (uint16_t*)dzh;
     ws->dzl = (uint16_t*)dzl;
     ws->db1_part = (float*)part;
+    ws->hT = (uint16_t*)hT;
+    ws->dw_part = (float*)dwp;
   }
-  (void)H;
   return off;
 }
 
@@ -272,30 +323,48 @@ hipError_t lh_launch(const LhArgs& a) {
   const int M = a.B * a.k;
   const int Mp = (M + 15) & ~15;
   if (M == 0) return hipSuccess;
-  const dim3 g1((M + kTile - 1) / kTile, (a.Hp + kTile - 1) / kTile);
-  hipLaunchKernelGGL(lh_gemm_tn, g1, dim3(kLhThreads), 0, a.stream, a.h, a.H, a.W1, a.H, a.ws.z1, a.Hp, M, a.Hp,
-                     a.H);
+  const int mt = (M + kTile - 1) / kTile, nt = (a.Hp + kTile - 1) / kTile;
+  const Split sf = split_k(a.H, (long long)mt * nt);
+  const bool bwd = a.accept_len != nullptr;
+  hipLaunchKernelGGL((lh_gemm_tn<false>), dim3(mt, nt, sf.S), dim3(kLhThreads), 0, a.stream, a.h,
+                     (const uint16_t*)nullptr, a.H, a.W1, a.H, a.ws.z1, M, a.Hp, a.H, sf.kslice);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const bool bwd = a.accept_len != nullptr;
-  hipLaunchKernelGGL(lh_pool, dim3(a.B), dim3(kLhThreads), 0, a.stream, a.ws.z1, a.Hp, a.k, a.b1, a.w2, a.b2,
-                     a.gamma, a.a_hat, a.k_hat, a.accept_len, a.verify_len, a.loss, bwd ? a.ws.hbar : nullptr,
-                     a.ws.ds);
+  // The split-K slices summed in slice order (the pooling kernel then reads
+  // one value per entry).
+  const size_t nz = (size_t)M * a.Hp;
+  const int zblocks = (int)((nz + kLhThreads - 1) / kLhThreads < 2048 ? (nz + kLhThreads - 1) / kLhThreads : 2048);
+  hipLaunchKernelGGL(lh_sum_slices, dim3(zblocks), dim3(kLhThreads), 0, a.stream, a.ws.z1, sf.S, nz, a.ws.zsum);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(lh_pool, dim3(a.B), dim3(kLhThreads), 0, a.stream, a.ws.zsum, a.Hp, a.k,
+                     a.b1, a.w2, a.b2, a.gamma, a.a_hat, a.k_hat, a.accept_len, a.verify_len, a.loss,
+                     bwd ? a.ws.hbar : nullptr, a.ws.ds);
   e = hipGetLastError();
   if (e != hipSuccess || !bwd) return e;
   const int ntiles = (M + kTile - 1) / kTile;
-  const dim3 g2((Mp + kTile - 1) / kTile, (a.Hp + kTile - 1) / kTile);
-  hipLaunchKernelGGL(lh_dz, g2, dim3(kLhThreads), 0, a.stream, a.ws.z1, M, a.Hp, a.k, Mp, a.b1, a.w2, a.ws.ds,
-                     a.ws.dzh, a.ws.dzl, a.ws.db1_part);
+  hipLaunchKernelGGL(lh_dz, dim3((Mp + kTile - 1) / kTile, nt), dim3(kLhThreads), 0, a.stream, a.ws.zsum, M, a.Hp,
+                     a.k, Mp, a.b1, a.w2, a.ws.ds, a.ws.dzh, a.ws.dzl, a.ws.db1_part);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(lh_small_grads, dim3(1), dim3(kLhThreads), 0, a.stream, a.ws.db1_part, ntiles, a.Hp, a.B,
                      a.ws.ds, a.ws.hbar, a.db1, a.dw2, a.db2);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 g3((a.H + kTile - 1) / kTile, (a.Hp + kTile - 1) / kTile);
-  hipLaunchKernelGGL(lh_gemm_dw, g3, dim3(kLhThreads), 0, a.stream, a.ws.dzh, a.ws.dzl, Mp, a.h, M, a.H, a.dW1,
-                     a.Hp);
+  hipLaunchKernelGGL(lh_transpose, dim3((Mp + kTile - 1) / kTile, (a.H + kTile - 1) / kTile), dim3(kLhThreads), 0,
+                     a.stream, a.h, M, a.H, Mp, a.ws.hT);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // dW1 [H' x H] = (dZ1^T high + remainder) [H' x Mp] . (h^T)^T, reduction over Mp.
+  const int rt = nt, ct = (a.H + kTile - 1) / kTile;
+  const Split sb = split_k(Mp, (long long)rt * ct);
+  hipLaunchKernelGGL((lh_gemm_tn<true>), dim3(rt, ct, sb.S), dim3(kLhThreads), 0, a.stream, a.ws.dzh, a.ws.dzl, Mp,
+                     a.ws.hT, Mp, a.ws.dw_part, a.Hp, a.H, Mp, sb.kslice);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t n = (size_t)a.Hp * a.H;
+  const int blocks = (int)((n + kLhThreads - 1) / kLhThreads < 2048 ? (n + kLhThreads - 1) / kLhThreads : 2048);
+  hipLaunchKernelGGL(lh_sum_slices, dim3(blocks), dim3(kLhThreads), 0, a.stream, a.ws.dw_part, sb.S, n, a.dW1);
   return hipGetLastError();
 }
 
