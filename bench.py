@@ -38,7 +38,7 @@ def parse():
     ap.add_argument("--sets", type=int, default=2, help="input sets rotated between calls")
     ap.add_argument("--clip", type=float, default=10.0)
     ap.add_argument("--lam", type=float, default=1.0)
-    ap.add_argument("--mode", choices=["fused", "verify", "opd"], default="fused")
+    ap.add_argument("--mode", choices=["fused", "verify", "opd", "lengthhead"], default="fused")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-probe", action="store_true",
@@ -122,6 +122,91 @@ def cpu_baseline(batch, mode, clip, lam, budget_s):
                       f"{done} repetitions in {el:.1f} s, {threads} threads"}
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak, AMD published
+
+
+def bench_length_head(args):
+    """Adaptive length head, B=128 requests, k=16 positions, H=4096 (hidden
+    size of an 8B-class target), H'=256: one step = the forward (accept rate,
+    verify length) plus the backward (loss and head gradients) of a round.
+    Synthetic hidden states and weights; two input sets rotated."""
+    import numpy as np
+    import torch
+    import diffusion_drafter_verification_amd as ada
+    import workloads as W
+    B, k, H, Hp = 128, 16, 4096, 256
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    sets = [W.length_head_inputs(B, k, H, Hp, seed=W.SEED_BASE + 21 + s) for s in range(args.sets)]
+    d = []
+    for lb in sets:
+        d.append({"h": torch.from_numpy(lb.hidden.view(np.int16)).view(torch.bfloat16).to(dev),
+                  "W1": torch.from_numpy(lb.W1.view(np.int16)).view(torch.bfloat16).to(dev),
+                  "b1": torch.from_numpy(lb.b1).to(dev), "w2": torch.from_numpy(lb.w2).to(dev), "b2": lb.b2,
+                  "al": torch.from_numpy(lb.accept_len).to(dev), "vl": torch.from_numpy(lb.verify_len).to(dev)})
+    ws = ada.length_head_workspace(B, k, H, Hp, dev)
+    a_hat = torch.empty(B, dtype=torch.float32, device=dev)
+    k_hat = torch.empty(B, dtype=torch.int32, device=dev)
+    loss = torch.empty(B, dtype=torch.float32, device=dev)
+    dW1 = torch.empty(Hp, H, dtype=torch.float32, device=dev)
+    db1 = torch.empty(Hp, dtype=torch.float32, device=dev)
+    dw2 = torch.empty(Hp, dtype=torch.float32, device=dev)
+    db2 = torch.empty(1, dtype=torch.float32, device=dev)
+
+    def call(x):
+        ada.adaflash_length_head_forward(x["h"], x["W1"], x["b1"], x["w2"], x["b2"], 1.0, a_hat, k_hat, ws, stream)
+        ada.adaflash_length_head_backward(x["h"], x["W1"], x["b1"], x["w2"], x["b2"], x["al"], x["vl"], loss, dW1,
+                                          db1, dw2, db2, ws, stream)
+
+    for i in range(args.warmup):
+        call(d[i % len(d)])
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        call(d[i % len(d)])
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    durs = np.array([s_.elapsed_time(e) for s_, e in zip(starts, ends)]) * 1e-3
+    avg = float(durs.mean())
+    # Matrix-core work per step: the projection in the forward and again in
+    # the backward, and the weight gradient as two products (bf16 high part
+    # and remainder of dZ1): 2 M H' H each, M = B k.
+    flops = 4 * 2.0 * B * k * Hp * H
+    achieved = flops / avg / 1e12
+    res = {
+        "metric": "length-head forward+backward requests/sec (B=128, k=16, H=4096, H'=256)",
+        "value": B * args.steps / elapsed,
+        "unit": "requests/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": elapsed / args.steps * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "adaptive length head: B=128, k=16, H=4096, H'=256, bf16 hidden states and W1, "
+                               "fp32 accumulation, one forward + one backward per step", "input_sets": args.sets},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None},
+        "kernel_ms_avg": avg * 1e3,
+    }
+    if not args.no_cpu:
+        from oracle import length_head as LH
+        lb = sets[0]
+        h = LH.bf16_to_f64(lb.hidden)
+        W1 = LH.bf16_to_f64(lb.W1)
+        n = 0
+        t1 = time.perf_counter()
+        while time.perf_counter() - t1 < min(args.cpu_seconds, 10.0) or n == 0:
+            LH.forward(h, W1, lb.b1, lb.w2, lb.b2, 1.0)
+            LH.loss_backward(h, W1, lb.b1, lb.w2, lb.b2, lb.accept_len, lb.verify_len)
+            n += 1
+        dt = time.perf_counter() - t1
+        res["cpu_baseline"] = {"value": B * n / dt, "unit": "requests/s", "cores": int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count()), "kind": "oracle",
+                               "sample": f"{n} full steps (B=128) of input set 0 in {dt:.1f} s, numpy float64"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -133,6 +218,9 @@ def main():
 
     if args.copy_probe:
         copy_probe()
+        return
+    if args.mode == "lengthhead":
+        bench_length_head(args)
         return
 
     import diffusion_drafter_verification_amd as ada
