@@ -62,6 +62,9 @@ def load_library() -> ctypes.CDLL:
         lib.adaflash_opd_loss_fwd_bwd.restype = i32
         lib.adaflash_opd_loss_fwd_bwd.argtypes = [i32, vp, vp, vp, i32, i32, i32, f32, f32, vp, vp,
                                                   vp, vp, vp, vp, sz, vp]
+        lib.adaflash_loss_variant_fwd_bwd.restype = i32
+        lib.adaflash_loss_variant_fwd_bwd.argtypes = [i32, vp, vp, vp, i32, i32, i32, i32, f32, f32, vp, vp, vp,
+                                                      vp, vp, sz, vp]
         lib.adaflash_length_head_workspace_bytes.restype = sz
         lib.adaflash_length_head_workspace_bytes.argtypes = [i32, i32, i32, i32]
         lib.adaflash_length_head_forward.restype = i32
@@ -186,6 +189,43 @@ def opd_loss_fwd_bwd(target: torch.Tensor, draft: torch.Tensor, verify_len: Opti
         ws = workspace(B, k, V, dev)
     adaflash_opd_loss_fwd_bwd(target, draft, verify_len, clip_c, lam, out["row_offsets"],
                               out["loss_ce"], out["loss_rkl"], out["grad"], out["status"], ws, stream)
+    return out
+
+
+# ----------------------------------------------------------- loss variants
+
+LOSS_VARIANTS = {"rkl": 1, "rkl_clip": 2, "mixture": 3, "fkl": 4, "wce": 5}
+
+
+def adaflash_loss_variant_fwd_bwd(target, draft, verify_len, variant, p1, p2, row_offsets, loss, grad_draft, status,
+                                  ws, stream=None) -> None:
+    """Direct binding of adaflash_loss_variant_fwd_bwd (see include/adaflash.h)."""
+    B, k1, V = target.shape
+    code = LOSS_VARIANTS[variant] if isinstance(variant, str) else int(variant)
+    rc = load_library().adaflash_loss_variant_fwd_bwd(
+        _dtype_code(target), _ptr(target), _ptr(draft), _ptr(verify_len), B, k1 - 1, V, code, float(p1),
+        float(p2), _ptr(row_offsets), _ptr(loss), _ptr(grad_draft), _ptr(status), _ptr(ws),
+        ws.numel() if ws is not None else 0, _stream(stream))
+    _check(rc)
+
+
+def loss_variant_fwd_bwd(target: torch.Tensor, draft: torch.Tensor, verify_len: Optional[torch.Tensor], variant,
+                         p1: float = 0.0, p2: float = 0.0, with_grad: bool = True, ws: Optional[torch.Tensor] = None,
+                         stream=None) -> dict:
+    """Allocates the outputs and calls adaflash_loss_variant_fwd_bwd."""
+    B, k1, V = target.shape
+    k = k1 - 1
+    dev = target.device
+    out = {
+        "row_offsets": torch.empty(B + 1, dtype=torch.int32, device=dev),
+        "status": torch.empty(1, dtype=torch.int32, device=dev),
+        "loss": torch.empty(B * k, dtype=torch.float32, device=dev),
+        "grad": torch.empty(B * k, V, dtype=target.dtype, device=dev) if with_grad else None,
+    }
+    if ws is None:
+        ws = workspace(B, k, V, dev)
+    adaflash_loss_variant_fwd_bwd(target, draft, verify_len, variant, p1, p2, out["row_offsets"], out["loss"],
+                                  out["grad"], out["status"], ws, stream)
     return out
 
 

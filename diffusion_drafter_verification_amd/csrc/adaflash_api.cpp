@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <limits>
 
 #include "../../include/adaflash.h"
 #include "adaflash_internal.h"
@@ -168,6 +169,56 @@ int adaflash_opd_loss_fwd_bwd(adaflash_dtype dtype, const void* target_logits,
   a.row_offsets = row_offsets;
   a.loss_ce = loss_ce;
   a.loss_rkl = loss_rkl;
+  a.grad = grad_draft;
+  a.status = status_flags;
+  a.stream = (hipStream_t)stream;
+  return run(a, workspace);
+}
+
+int adaflash_loss_variant_fwd_bwd(adaflash_dtype dtype, const void* target_logits, const void* draft_logits,
+                                  const int32_t* verify_len, int B, int k, int V, int variant, float p1, float p2,
+                                  int32_t* row_offsets, float* loss, void* grad_draft, int32_t* status_flags,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = common_checks(dtype, target_logits, draft_logits, B, k, V, row_offsets, workspace, workspace_bytes,
+                         true);
+  if (rc != ADAFLASH_OK) return rc;
+  LaunchArgs a{};
+  const float inf = std::numeric_limits<float>::infinity();
+  switch (variant) {
+    case ADAFLASH_LOSS_RKL:
+      a.a_ce = 0.f, a.lambda = 1.f, a.clip_c = inf;
+      break;
+    case ADAFLASH_LOSS_RKL_CLIP:
+      if (!(p1 > 0.f) || std::isinf(p1)) return fail(ADAFLASH_E_INVALID, "delta must be finite and > 0%s");
+      a.a_ce = 0.f, a.lambda = 1.f, a.clip_c = p1;
+      break;
+    case ADAFLASH_LOSS_MIXTURE:
+      if (!(p1 >= 0.f && p1 <= 1.f)) return fail(ADAFLASH_E_INVALID, "alpha must be in [0, 1]%s");
+      if (!(p2 > 0.f) || std::isinf(p2)) return fail(ADAFLASH_E_INVALID, "delta must be finite and > 0%s");
+      a.a_ce = p1, a.lambda = 1.f - p1, a.clip_c = p2;
+      break;
+    case ADAFLASH_LOSS_FKL:
+      a.a_ce = 0.f, a.lambda = 0.f, a.clip_c = inf, a.fkl = 1;
+      break;
+    case ADAFLASH_LOSS_WCE:
+      if (!(p1 > 0.f) || std::isinf(p1)) return fail(ADAFLASH_E_INVALID, "position decay must be finite and > 0%s");
+      a.a_ce = 1.f, a.lambda = 0.f, a.clip_c = inf, a.wdecay = p1;
+      break;
+    default:
+      return fail(ADAFLASH_E_INVALID, "unknown loss variant%s");
+  }
+  a.bf16 = dtype == ADAFLASH_BF16;
+  a.target = target_logits;
+  a.draft = draft_logits;
+  a.verify_len = verify_len;
+  a.B = B;
+  a.k = k;
+  a.V = V;
+  a.T = 1.f;
+  a.verify = 0;
+  a.opd = 1;
+  a.row_offsets = row_offsets;
+  a.loss_var = loss;
   a.grad = grad_draft;
   a.status = status_flags;
   a.stream = (hipStream_t)stream;

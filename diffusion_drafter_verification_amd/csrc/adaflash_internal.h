@@ -48,6 +48,10 @@ struct LaunchArgs {
   int verify;             // 1: verify the batch
   int opd;                // 1: supervision outputs requested
   float clip_c, lambda;
+  float a_ce = 1.f;       // weight of the hard-label term (loss variants)
+  float wdecay = 0.f;     // per-position weight exp(-i / wdecay); 0 = none
+  int fkl = 0;            // 1: forward KL(p || q) instead of the reverse KL
+  float* loss_var = nullptr;  // [N] combined per-row loss of a variant, or null
   int32_t* accept_len;
   int32_t* out_tokens;
   float* margins;

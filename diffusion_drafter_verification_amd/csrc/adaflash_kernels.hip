@@ -81,6 +81,11 @@ struct KParams {
   int B, k, V, G;
   float kT;  // log2(e) / T (0 in greedy mode)
   float clip_c, lambda;
+  // Supervision loss variants: weight of the hard-label term (1 for the
+  // default loss), per-position weight decay (0: none; else row i weighs
+  // exp(-i / wdecay)), and the combined per-row loss output (or null).
+  float a_ce, wdecay;
+  float* loss_var;
 };
 
 // ---------------------------------------------------------------- primitives
@@ -1111,6 +1116,7 @@ struct SupStats {
   // Derived row values: log2 normalisers of q and p, D = lse_q - lse_p, the
   // unclipped reverse KL, and the bound on the largest per-entry term.
   float lse_q2, lse_p2, D, KL, bound;
+  float fkl;  // forward KL(p || q) of the row (forward-KL variant only)
 };
 
 __device__ __forceinline__ void derive_sup(float Mp, float Mq, float Sp, float Sq, float Wsum, float BA,
@@ -1138,7 +1144,7 @@ __device__ __forceinline__ float accept_margin(float zpx, float zqx, float u, fl
 // hands the results to the other waves through fs.f; otherwise every wave
 // takes part.  CHUNK_X: the records carry no argmax; xstar is then the lowest
 // chunk whose maximum is the row maximum.
-template <bool SAMPLED, bool CHUNK_X>
+template <bool SAMPLED, bool CHUNK_X, bool FKL>
 __device__ SupStats combine_sup(const KParams& P, int r, FinShared& fs, float zpx, float zqx, float u) {
   const int tid = threadIdx.x;
   const int G = P.G;
@@ -1184,14 +1190,21 @@ __device__ SupStats combine_sup(const KParams& P, int r, FinShared& fs, float zp
     sq = pub_load(rec + 5);
     a = pub_load(rec + 6);
   };
-  float m[2], v[6], dv[5];
+  float m[2], v[6], dv[5], wpr = 0.f;
   if (G <= 64) {
     if (tid < 64) {
       float mp = neg_inf(), mq = neg_inf(), sp = 0.f, sq = 0.f, w = 0.f, a = neg_inf();
       int idx = kIntMax;
       if (tid < G) load(tid, mp, mq, sp, sq, w, a, idx);
       reduce(mp, mq, sp, sq, w, a, idx, tid < G, m, v, false);
+      float wp = 0.f;
+      if constexpr (FKL) {
+        if (tid < G && mp != neg_inf())
+          wp = pub_load(P.part1 + ((size_t)r * G + tid) * kRec1 + 7) * fexp2((mp - m[0]) * kLog2e);
+        wp = wave_reduce<OP_SUM>(wp);
+      }
       if (tid == 0) {
+        fs.f[14] = wp;
         fs.f[0] = m[0];
         fs.f[1] = m[1];
 #pragma unroll
@@ -1211,6 +1224,7 @@ __device__ SupStats combine_sup(const KParams& P, int r, FinShared& fs, float zp
     for (int q = 0; q < 6; ++q) v[q] = fs.f[2 + q];
 #pragma unroll
     for (int q = 0; q < 5; ++q) dv[q] = fs.f[9 + q];
+    wpr = fs.f[14];
   } else {
     float mp = neg_inf(), mq = neg_inf(), sp = 0.f, sq = 0.f, w = 0.f, a = neg_inf();
     int idx = kIntMax;
@@ -1218,6 +1232,14 @@ __device__ SupStats combine_sup(const KParams& P, int r, FinShared& fs, float zp
     reduce(mp, mq, sp, sq, w, a, idx, tid < G, m, v, true);
     if (SAMPLED && tid == 0) fs.f[8] = accept_margin(zpx, zqx, u, m[0], m[1], v[0], v[1]);
     derive_sup(m[0], m[1], v[0], v[1], v[2], v[3], dv);
+    if constexpr (FKL) {
+      float w1[1] = {0.f};
+      if (tid < G && mp != neg_inf())
+        w1[0] = pub_load(P.part1 + ((size_t)r * G + tid) * kRec1 + 7) * fexp2((mp - m[0]) * kLog2e);
+      const int o1[1] = {OP_SUM};
+      wg_reduce<1>(w1, o1, fs.red);
+      wpr = w1[0];
+    }
     __syncthreads();
   }
   SupStats s;
@@ -1235,30 +1257,34 @@ __device__ SupStats combine_sup(const KParams& P, int r, FinShared& fs, float zp
   s.D = uniform(dv[2]);
   s.KL = uniform(dv[3]);
   s.bound = uniform(dv[4]);
+  // Forward KL = sum p (log p - log q) = -E_p[z_q - z_p] + D.
+  s.fkl = FKL ? uniform(-wpr / s.Sp + s.D) : 0.f;
   return s;
 }
 
 // Gradient value of the exact path (q recomputed in fp32: clip decisions).
 __device__ __forceinline__ float grad_exact(float zq, float zp, float lse_q2, float D, float lam, float lamS,
-                                            float c) {
+                                            float c, float ace) {
   const float q = fexp2(fmaf(zq, kLog2e, -lse_q2));
   const float dd = (zq - zp) - D;
   const float f = q > 0.f ? q * dd : 0.f;
   const float sterm = f <= c ? f + q : 0.f;
-  return fmaf(-lamS, q, fmaf(lam, sterm, q));
+  return fmaf(-lamS, q, fmaf(lam, sterm, ace * q));
 }
 
 // Workgroups per CU: aligned bf16 chunks fit 80 VGPRs (six per CU), and the
 // fused sampled variant 72 (seven per CU; two values of the rarely taken
 // exact path spill, measured faster than six); fp32 chunks take twice the
 // registers and the element-wise loads of unaligned rows more.
-template <bool BF16, bool ALIGNED, int VMODE>
+template <bool BF16, bool ALIGNED, int VMODE, bool FKL>
 constexpr int sup_min_waves() {
-  return BF16 && ALIGNED ? (kElems <= 32 ? (VMODE == 2 ? 7 : 6) : 4) : 1;
+  return BF16 && ALIGNED ? (FKL ? 4 : (kElems <= 32 ? (VMODE == 2 ? 7 : 6) : 4)) : 1;
 }
 
-template <bool BF16, bool ALIGNED, int VMODE>
-__global__ __launch_bounds__(kThreads, (sup_min_waves<BF16, ALIGNED, VMODE>())) void sup_kernel(KParams P) {
+// FKL: the forward-KL variant (supervision only): pass 1 also sums
+// e^{z_p - m} (z_q - z_p) per chunk, the gradient adds q - p.
+template <bool BF16, bool ALIGNED, int VMODE, bool FKL = false>
+__global__ __launch_bounds__(kThreads, (sup_min_waves<BF16, ALIGNED, VMODE, FKL>())) void sup_kernel(KParams P) {
   constexpr bool SAMPLED = VMODE == 2, VERIFY = VMODE != 0;
   constexpr bool DEFER_X = VMODE != 1;  // argmax searched after the row barrier
   constexpr int VEC = Chunk<BF16>::VEC;
@@ -1349,7 +1375,7 @@ __global__ __launch_bounds__(kThreads, (sup_min_waves<BF16, ALIGNED, VMODE>())) 
     cand = entry_index<BF16>(v0, ce);
     if (cand >= V) cand = kIntMax;  // padding (a row of -inf only)
   }
-  float sp = 0.f, sq = 0.f, W = 0.f, Amax = neg_inf();
+  float sp = 0.f, sq = 0.f, W = 0.f, Amax = neg_inf(), Wp = 0.f;
   const float ap = uniform(Mw[0] == neg_inf() ? 0.f : -Mw[0] * kLog2e);
   const float aq = uniform(Mw[1] == neg_inf() ? 0.f : -Mw[1] * kLog2e);
   if (draft_row) {
@@ -1364,7 +1390,9 @@ __global__ __launch_bounds__(kThreads, (sup_min_waves<BF16, ALIGNED, VMODE>())) 
           const int e = s2 * VEC + u + t;
           const float zq = cq.get(e), zp = cp.get(e);
           const float ee = fexp2(fmaf(zq, kLog2e, aq));
-          sp += fexp2(fmaf(zp, kLog2e, ap));
+          const float ep = fexp2(fmaf(zp, kLog2e, ap));
+          sp += ep;
+          if constexpr (FKL) Wp = fmaf(ep, zq - zp, Wp);
           sq += ee;
           const float pr = ee * (zq - zp);
           W += pr;
@@ -1383,9 +1411,10 @@ __global__ __launch_bounds__(kThreads, (sup_min_waves<BF16, ALIGNED, VMODE>())) 
   {
     // Only thread 0 publishes the record; fs.red is next written after the
     // row barrier.
-    constexpr int NR = DEFER_X ? 4 : 5;
-    float v[5] = {sp, sq, W, Amax, __int_as_float(cand)};
-    const int ops[5] = {OP_SUM, OP_SUM, OP_SUM, OP_MAX, OP_MINI};
+    static_assert(!FKL || DEFER_X, "the forward-KL sum takes the argmax slot");
+    constexpr int NR = DEFER_X && !FKL ? 4 : 5;
+    float v[5] = {sp, sq, W, Amax, FKL ? Wp : __int_as_float(cand)};
+    const int ops[5] = {OP_SUM, OP_SUM, OP_SUM, OP_MAX, FKL ? OP_SUM : OP_MINI};
     wg_reduce_lead<NR>(reinterpret_cast<float(&)[NR]>(v), reinterpret_cast<const int(&)[NR]>(ops), fs.red);
     if (tid == 0) {
       float* rec = P.part1 + ((size_t)r * G + j) * kRec1;
@@ -1396,6 +1425,7 @@ __global__ __launch_bounds__(kThreads, (sup_min_waves<BF16, ALIGNED, VMODE>())) 
       pub_store(rec + 4, Mw[1]);
       pub_store(rec + 5, v[1]);
       pub_store(rec + 6, v[3]);
+      if (FKL) pub_store(rec + 7, v[4]);
     }
   }
   if (!draft_row) return;
@@ -1412,10 +1442,14 @@ __global__ __launch_bounds__(kThreads, (sup_min_waves<BF16, ALIGNED, VMODE>())) 
     const unsigned long long any = __ballot(rej);
     if (l == 0) fs.i[0] = any != 0ull;
   }
-  const SupStats st = combine_sup<SAMPLED, DEFER_X>(P, r, fs, zpx, zqx, u_acc);
+  const SupStats st = combine_sup<SAMPLED, DEFER_X, FKL>(P, r, fs, zpx, zqx, u_acc);
   const bool earlier_rejected = SAMPLED && fs.i[0] != 0;
   const float lse_q2 = st.lse_q2, lse_p2 = st.lse_p2, D = st.D, KL = st.KL;
-  const float c = P.clip_c, lam = P.lambda;
+  // Loss weights of this row: hard-label term ace, clipped reverse KL lam,
+  // forward KL afk, all scaled by the position weight (1 unless decaying).
+  const float wi = P.wdecay > 0.f ? uniform(fexp2(-(float)i * kLog2e / P.wdecay)) : 1.f;
+  const float c = P.clip_c, lam = uniform(wi * P.lambda), ace = uniform(wi * P.a_ce);
+  const float afk = FKL ? wi : 0.f;
   const bool fast = !st.nonfinite && st.bound <= 0.999f * c;
   // (A row maximum at the padding value means a row of -inf only.)
   const float pad = __uint_as_float(BF16 ? 0xff7f0000u : 0xff7fffffu);
@@ -1513,7 +1547,8 @@ __global__ __launch_bounds__(kThreads, (sup_min_waves<BF16, ALIGNED, VMODE>())) 
   if (fast) {
     // g = q (1 + lambda (dz - D - KL)) = q (lambda dz + c1), with q = e s the
     // cached pass-1 exponential e = exp(z_q - m) scaled by s = exp(m - lse_q).
-    const float c1 = fmaf(-lam, D, 1.f - lam * KL);
+    // (plus, for the forward KL, afk (q - p): afk joins c1 and afk p is subtracted)
+    const float c1 = FKL ? fmaf(-lam, D, ace - lam * KL) + afk : fmaf(-lam, D, ace - lam * KL);
     const float sc = uniform(fexp2(-aq - lse_q2));
     const float lsc = uniform(lam * sc), csc = uniform(c1 * sc);
     // The residual sweep shares the gradient's unpacked logits; its q is
@@ -1538,11 +1573,12 @@ __global__ __launch_bounds__(kThreads, (sup_min_waves<BF16, ALIGNED, VMODE>())) 
           const float zq = cq.get(e), zp = cp.get(e);
           float q = 0.f;
           if (!ECACHE || decltype(with_res)::value) q = fexp2(fmaf(zq, kLog2e, -lse_q2));
+          const float pterm = FKL ? -afk * fexp2(fmaf(zp, kLog2e, -lse_p2)) : 0.f;
           if constexpr (ECACHE) {
             const float dz = decltype(with_res)::value ? zq - zp : dz8[u];
-            g[u] = fma_f16(hw[u / 2], u & 1, fmaf(lsc, dz, csc), 0.f);
+            g[u] = fma_f16(hw[u / 2], u & 1, fmaf(lsc, dz, csc), pterm);
           } else {
-            g[u] = q * fmaf(lam, zq - zp, c1);
+            g[u] = fmaf(q, fmaf(lam, zq - zp, c1), pterm);
           }
           if constexpr (decltype(with_res)::value)
             Zpart += fmaxf(0.f, fexp2(fmaf(zp, kLog2e, -lse_p2)) - q);
@@ -1553,12 +1589,14 @@ __global__ __launch_bounds__(kThreads, (sup_min_waves<BF16, ALIGNED, VMODE>())) 
     if (need_res) sweep(std::true_type{});
     else if (P.grad) sweep(std::false_type{});
     if (xs_here) {
+      // (z_p at x* is the row maximum)
+      const float pstar = FKL ? -afk * fexp2(st.Mp * kLog2e - lse_p2) : 0.f;
       if constexpr (ECACHE) {
         const int xs_slot = xo / (kThreads * VEC), xs_u = xo % VEC;
         const uint32_t w = ecache[((size_t)xs_slot * kThreads + tid) * 4 + xs_u / 2];
-        gstar = fma_f16(w, xs_u & 1, fmaf(lsc, zqs - st.Mp, csc), 0.f) - 1.f;
+        gstar = fma_f16(w, xs_u & 1, fmaf(lsc, zqs - st.Mp, csc), pstar) - ace;
       } else {
-        gstar = fexp2(fmaf(zqs, kLog2e, -lse_q2)) * fmaf(lam, zqs - st.Mp, c1) - 1.f;
+        gstar = fmaf(fexp2(fmaf(zqs, kLog2e, -lse_q2)), fmaf(lam, zqs - st.Mp, c1), pstar) - ace;
       }
     }
   } else {
@@ -1606,14 +1644,16 @@ __global__ __launch_bounds__(kThreads, (sup_min_waves<BF16, ALIGNED, VMODE>())) 
 #pragma unroll
         for (int u = 0; u < VEC; ++u) {
           const int e = s2 * VEC + u;
-          g[u] = grad_exact(cq.get(e), cp.get(e), lse_q2, D, lam, lamS, c);
+          g[u] = grad_exact(cq.get(e), cp.get(e), lse_q2, D, lam, lamS, c, ace);
+          if constexpr (FKL) g[u] -= afk * fexp2(fmaf(cp.get(e), kLog2e, -lse_p2));
           // Rarely taken path: limit the interleaving (and registers) here.
           if (u & 1) __builtin_amdgcn_sched_barrier(0);
         }
         store_slot(s2, g);
       }
     }
-    gstar = grad_exact(zqs, st.Mp, lse_q2, D, lam, lamS, c) - 1.f;
+    gstar = grad_exact(zqs, st.Mp, lse_q2, D, lam, lamS, c, ace) - ace;
+    if constexpr (FKL) gstar -= afk * fexp2(st.Mp * kLog2e - lse_p2);
   }
   if (fast && need_res) {
     // The residual mass of this chunk goes to the finaliser.
@@ -1628,6 +1668,7 @@ __global__ __launch_bounds__(kThreads, (sup_min_waves<BF16, ALIGNED, VMODE>())) 
     if (P.grad) store_one(xs, gstar);
     if (P.loss_ce) P.loss_ce[n] = lse_q2 * kLn2 - zqs;
     if (P.loss_rkl) P.loss_rkl[n] = Rrow;
+    if (P.loss_var) P.loss_var[n] = wi * (P.a_ce * (lse_q2 * kLn2 - zqs) + P.lambda * Rrow + (FKL ? st.fkl : 0.f));
   }
 }
 
@@ -1917,9 +1958,9 @@ hipError_t launch_rows(const KParams& p, int grid, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <bool BF16, bool ALIGNED, int VMODE>
+template <bool BF16, bool ALIGNED, int VMODE, bool FKL = false>
 hipError_t launch_sup(const KParams& p, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((sup_kernel<BF16, ALIGNED, VMODE>), dim3(grid), dim3(kThreads), 0, st, p);
+  hipLaunchKernelGGL((sup_kernel<BF16, ALIGNED, VMODE, FKL>), dim3(grid), dim3(kThreads), 0, st, p);
   return hipGetLastError();
 }
 
@@ -1930,9 +1971,10 @@ hipError_t launch_final(const KParams& p, hipStream_t st) {
 }
 
 template <bool BF16, bool ALIGNED>
-hipError_t dispatch_mode(const KParams& p, int grid, int opd, int vmode, bool t1, hipStream_t st) {
+hipError_t dispatch_mode(const KParams& p, int grid, int opd, int vmode, bool t1, bool fkl, hipStream_t st) {
   hipError_t e;
-  if (opd && vmode == 0) e = launch_sup<BF16, ALIGNED, 0>(p, grid, st);
+  if (opd && vmode == 0 && fkl) e = launch_sup<BF16, ALIGNED, 0, true>(p, grid, st);
+  else if (opd && vmode == 0) e = launch_sup<BF16, ALIGNED, 0>(p, grid, st);
   else if (opd && vmode == 1) e = launch_sup<BF16, ALIGNED, 1>(p, grid, st);
   else if (opd && vmode == 2 && t1) e = launch_sup<BF16, ALIGNED, 2>(p, grid, st);
   else if (opd) e = launch_rows<BF16, ALIGNED, true, 2, false>(p, grid, st);
@@ -1987,6 +2029,9 @@ hipError_t launch(const LaunchArgs& a) {
   p.kT = a.T > 0.f ? kLog2e / a.T : 0.f;
   p.clip_c = a.clip_c;
   p.lambda = a.lambda;
+  p.a_ce = a.a_ce;
+  p.wdecay = a.wdecay;
+  p.loss_var = a.loss_var;
 
   const int vmode = a.verify ? (a.T > 0.f ? 2 : 1) : 0;
   const int rows_max = a.B * (a.k + bonus);
@@ -1998,11 +2043,11 @@ hipError_t launch(const LaunchArgs& a) {
                        (a.grad == nullptr || ((uintptr_t)a.grad & 15) == 0);
   const bool t1 = a.T == 1.0f;
   if (a.bf16) {
-    if (aligned) return dispatch_mode<true, true>(p, (int)grid, a.opd, vmode, t1, a.stream);
-    return dispatch_mode<true, false>(p, (int)grid, a.opd, vmode, t1, a.stream);
+    if (aligned) return dispatch_mode<true, true>(p, (int)grid, a.opd, vmode, t1, a.fkl != 0, a.stream);
+    return dispatch_mode<true, false>(p, (int)grid, a.opd, vmode, t1, a.fkl != 0, a.stream);
   }
-  if (aligned) return dispatch_mode<false, true>(p, (int)grid, a.opd, vmode, t1, a.stream);
-  return dispatch_mode<false, false>(p, (int)grid, a.opd, vmode, t1, a.stream);
+  if (aligned) return dispatch_mode<false, true>(p, (int)grid, a.opd, vmode, t1, a.fkl != 0, a.stream);
+  return dispatch_mode<false, false>(p, (int)grid, a.opd, vmode, t1, a.fkl != 0, a.stream);
 }
 
 }  // namespace adaflash

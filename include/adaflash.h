@@ -160,6 +160,49 @@ ADAFLASH_API int adaflash_opd_loss_fwd_bwd(adaflash_dtype dtype, const void* tar
                               void* stream);
 
 /*
+ * Supervision loss variants the pages compare, on the same fused row pass as
+ * adaflash_opd_loss_fwd_bwd (temperature 1; p = softmax(z_p), q = softmax(z_q),
+ * x* = argmax z_p, lowest index on ties; CE = -log q(x*); R_c = sum_v
+ * min(q log(q/p), c); FKL = sum_v p log(p/q)):
+ *   ADAFLASH_LOSS_RKL       R_inf: plain reverse KL (AdaFlash review (EN),
+ *                           ablation Table 2, first row)
+ *   ADAFLASH_LOSS_RKL_CLIP  R_delta, p1 = delta > 0 (Table 2, second row;
+ *                           "Entry-Wise Divergence Clipping, Derived")
+ *   ADAFLASH_LOSS_MIXTURE   alpha CE + (1 - alpha) R_delta, p1 = alpha in
+ *                           [0, 1], p2 = delta > 0 (Table 2, third row;
+ *                           AdaFlash review (ZH) section 2.1: alpha = 0.8,
+ *                           delta = 0.01)
+ *   ADAFLASH_LOSS_FKL       FKL: forward KL, the OSD baseline's objective
+ *                           (AdaFlash review (EN), "Forward KL vs. Reverse KL")
+ *   ADAFLASH_LOSS_WCE       exp(-i / p1) CE for draft position i (DFlash
+ *                           reading notes, section 7.3, eq. 12; p1 = 7 at
+ *                           block size 16)
+ */
+typedef enum {
+  ADAFLASH_LOSS_RKL = 1,
+  ADAFLASH_LOSS_RKL_CLIP = 2,
+  ADAFLASH_LOSS_MIXTURE = 3,
+  ADAFLASH_LOSS_FKL = 4,
+  ADAFLASH_LOSS_WCE = 5
+} adaflash_loss_variant;
+
+/*
+ * adaflash_loss_variant_fwd_bwd -- one loss variant and its gradient with
+ * respect to the draft logits for the verified rows (i < L_b) of a batch.
+ *   target_logits, draft_logits, verify_len, B, k, V, row_offsets,
+ *   status_flags, workspace, stream   as in adaflash_opd_loss_fwd_bwd.
+ *   variant, p1, p2                   see adaflash_loss_variant.
+ *   loss          [N]    out or NULL  the variant's per-row loss.
+ *   grad_draft    [N, V] out or NULL  its gradient in the logits' dtype.
+ * Returns ADAFLASH_OK or a negative adaflash_status.
+ */
+ADAFLASH_API int adaflash_loss_variant_fwd_bwd(adaflash_dtype dtype, const void* target_logits,
+                                  const void* draft_logits, const int32_t* verify_len, int B, int k,
+                                  int V, int variant, float p1, float p2, int32_t* row_offsets,
+                                  float* loss, void* grad_draft, int32_t* status_flags, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/*
  * Adaptive length head: the step before verification (it produces the verify
  * lengths) and after it (it learns from the accept lengths).  AdaFlash review
  * (ZH), section 2.2 "Adaptive Length Head", and AdaFlash review (EN),

@@ -165,3 +165,19 @@ def test_length_head_backward_rejects_bad_arguments(lib):
     assert f(P, P, P, P, 0.0, 4, 16, 64, 8, None, P, P, P, P, P, P, P, 1 << 30, None) == -1
     assert f(P, P, P, P, 0.0, 4, 16, 40, 8, P, P, P, P, P, P, P, P, 1 << 30, None) == -1
     assert f(P, P, P, P, 0.0, 4, 16, 64, 8, P, P, P, P, P, P, P, P, 16, None) == -2
+
+
+# ----------------------------------------------------------- loss variants
+
+@pytest.mark.parametrize("variant,p1,p2,code", [
+    (0, 0.0, 0.0, -1), (6, 0.0, 0.0, -1), (2, 0.0, 0.0, -1), (2, float("inf"), 0.0, -1),
+    (3, 1.5, 0.01, -1), (3, 0.8, 0.0, -1), (5, 0.0, 0.0, -1), (5, float("nan"), 0.0, -1),
+])
+def test_loss_variant_rejects_bad_arguments(lib, variant, p1, p2, code):
+    f = lib.adaflash_loss_variant_fwd_bwd
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    f.restype = i32
+    f.argtypes = [i32, vp, vp, vp, i32, i32, i32, i32, f32, f32, vp, vp, vp, vp, vp, sz, vp]
+    P = 0x10000
+    rc = f(1, P, P, None, 4, 16, 64, variant, p1, p2, P, P, P, None, P, 1 << 30, None)
+    assert rc == code
