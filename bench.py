@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--clip", type=float, default=10.0)
     ap.add_argument("--lam", type=float, default=1.0)
     ap.add_argument("--mode", choices=["fused", "verify", "opd", "lengthhead"], default="fused")
+    ap.add_argument("--variant", choices=["rkl", "rkl_clip", "mixture", "fkl", "wce"], default=None,
+                    help="with --mode opd: a supervision loss variant (pages' defaults: delta 0.01, "
+                         "alpha 0.8, position decay 7)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-probe", action="store_true",
@@ -254,8 +257,15 @@ def main():
     grad = torch.empty(B * k, V, dtype=torch.bfloat16, device=dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
 
+    vparams = {"rkl": (0.0, 0.0), "rkl_clip": (0.01, 0.0), "mixture": (0.8, 0.01), "fkl": (0.0, 0.0),
+               "wce": (7.0, 0.0)}
+
     def call(ds):
-        if args.mode == "opd":
+        if args.mode == "opd" and args.variant:
+            p1, p2 = vparams[args.variant]
+            ada.adaflash_loss_variant_fwd_bwd(ds["t"], ds["d"], ds["vl"], args.variant, p1, p2, ro, ce, grad,
+                                              status, ws, stream)
+        elif args.mode == "opd":
             ada.adaflash_opd_loss_fwd_bwd(ds["t"], ds["d"], ds["vl"], args.clip, args.lam, ro, ce, rk, grad,
                                           status, ws, stream)
         else:
@@ -315,8 +325,9 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": ("c128 fused verify+supervision: B=128, k=16, V=151936, bf16 logits, "
-                         "verify_len~U{1..16}, sigma_b~U{0.3,1,2}, T=1, c=%g, lambda=%g, mode=%s"
-                         % (args.clip, args.lam, args.mode)),
+                         "verify_len~U{1..16}, sigma_b~U{0.3,1,2}, T=1, c=%g, lambda=%g, mode=%s%s"
+                         % (args.clip, args.lam, args.mode,
+                            (", variant=%s" % args.variant) if args.variant else "")),
             "B": B, "k": k, "V": V, "input_sets": args.sets,
         },
         "roofline": {
@@ -332,7 +343,7 @@ def main():
         "algorithmic_bytes_per_call": bytes_total / args.steps,
         "verified_positions_per_call": positions / args.steps,
     }
-    if not args.no_cpu:
+    if not args.no_cpu and not args.variant:
         res["cpu_baseline"] = cpu_baseline(sets[0], args.mode, args.clip, args.lam, args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
