@@ -38,7 +38,7 @@ def parse():
     ap.add_argument("--sets", type=int, default=2, help="input sets rotated between calls")
     ap.add_argument("--clip", type=float, default=10.0)
     ap.add_argument("--lam", type=float, default=1.0)
-    ap.add_argument("--mode", choices=["fused", "verify", "opd", "lengthhead"], default="fused")
+    ap.add_argument("--mode", choices=["fused", "verify", "opd", "lengthhead", "admission"], default="fused")
     ap.add_argument("--variant", choices=["rkl", "rkl_clip", "mixture", "fkl", "wce"], default=None,
                     help="with --mode opd: a supervision loss variant (pages' defaults: delta 0.01, "
                          "alpha 0.8, position decay 7)")
@@ -210,6 +210,57 @@ def bench_length_head(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_admission(args):
+    """Host-side admission controller: seeded traffic (Poisson arrivals of
+    mean 40 per round, requests of 1..64 rounds, k_hat ~ U{1..16}, budget
+    2048 verify tokens, beta 0.2) for `steps` x 100 rounds; time per round
+    (propose + commit + finish) of the native controller, the Python oracle
+    timed beside it.  No GPU work."""
+    import numpy as np
+    import diffusion_drafter_verification_amd as ada
+    from oracle.admission import Admission as Ref
+
+    def run(ctl, rounds, seed):
+        rng = np.random.default_rng(seed)
+        remaining, nid, served = {}, 0, 0
+        t = 0.0
+        for _ in range(rounds):
+            n = int(rng.poisson(40.0))
+            ids = list(range(nid, nid + n))
+            nid += n
+            for r in ids:
+                remaining[r] = int(rng.integers(1, 65))
+            k = rng.integers(1, 17, size=4096).astype(np.int32)
+            t0 = time.perf_counter()
+            ctl.enqueue(ids)
+            b = ctl.propose()
+            out = ctl.commit(k[:len(b)])
+            fin = [r for r in out if remaining[r] == 1]
+            ctl.finish(fin)
+            t += time.perf_counter() - t0
+            for r in out:
+                remaining[r] -= 1
+            served += len(out)
+        return t, served
+
+    rounds = max(1, args.steps) * 100
+    tn, sn = run(ada.Admission(0.2, 64.0, 2048), rounds, 11)
+    tr, sr = run(Ref(0.2, 64.0, 2048), rounds, 11)
+    assert sn == sr
+    res = {
+        "metric": "admission-controller rounds/sec (host)", "value": rounds / tn, "unit": "rounds/s",
+        "n_gpus": 0, "steps": rounds, "warmup": 0, "ms_per_step": tn / rounds * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int64", "data": "synthetic",
+        "config": {"workload": "EMA admission, beta=0.2, budget 2048 verify tokens, Poisson(40) arrivals, "
+                               "1..64 rounds per request, k_hat~U{1..16}"},
+        "roofline": None,
+        "requests_verified_per_round": sn / rounds,
+        "cpu_baseline": {"value": rounds / tr, "unit": "rounds/s", "cores": 1, "kind": "oracle",
+                         "sample": f"the same {rounds} rounds with the Python oracle"},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -224,6 +275,9 @@ def main():
         return
     if args.mode == "lengthhead":
         bench_length_head(args)
+        return
+    if args.mode == "admission":
+        bench_admission(args)
         return
 
     import diffusion_drafter_verification_amd as ada

@@ -65,6 +65,23 @@ def load_library() -> ctypes.CDLL:
         lib.adaflash_loss_variant_fwd_bwd.restype = i32
         lib.adaflash_loss_variant_fwd_bwd.argtypes = [i32, vp, vp, vp, i32, i32, i32, i32, f32, f32, vp, vp, vp,
                                                       vp, vp, sz, vp]
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        lib.adaflash_admission_create.restype = vp
+        lib.adaflash_admission_create.argtypes = [ctypes.c_double, ctypes.c_double, ctypes.c_int64]
+        lib.adaflash_admission_destroy.restype = None
+        lib.adaflash_admission_destroy.argtypes = [vp]
+        lib.adaflash_admission_enqueue.restype = i32
+        lib.adaflash_admission_enqueue.argtypes = [vp, i64p, i32]
+        lib.adaflash_admission_propose.restype = i32
+        lib.adaflash_admission_propose.argtypes = [vp, i64p, i32]
+        lib.adaflash_admission_commit.restype = i32
+        lib.adaflash_admission_commit.argtypes = [vp, ctypes.POINTER(ctypes.c_int32), i32, i64p]
+        lib.adaflash_admission_finish.restype = i32
+        lib.adaflash_admission_finish.argtypes = [vp, i64p, i32]
+        lib.adaflash_admission_estimate.restype = ctypes.c_double
+        lib.adaflash_admission_estimate.argtypes = [vp]
+        lib.adaflash_admission_pending.restype = i32
+        lib.adaflash_admission_pending.argtypes = [vp]
         lib.adaflash_length_head_workspace_bytes.restype = sz
         lib.adaflash_length_head_workspace_bytes.argtypes = [i32, i32, i32, i32]
         lib.adaflash_length_head_forward.restype = i32
@@ -307,3 +324,61 @@ def length_head_backward(hidden: torch.Tensor, W1: torch.Tensor, b1: torch.Tenso
     adaflash_length_head_backward(hidden, W1, b1, w2, b2, accept_len, verify_len, out["loss"], out["dW1"],
                                   out["db1"], out["dw2"], out["db2"], ws, stream)
     return out
+
+
+# -------------------------------------------------------- admission control
+
+
+class Admission:
+    """Host-side admission controller (binding of adaflash_admission_*)."""
+
+    def __init__(self, beta: float, n_hat0: float, budget_tokens: int):
+        import numpy as np
+        self._np = np
+        self._lib = load_library()
+        self._h = self._lib.adaflash_admission_create(float(beta), float(n_hat0), int(budget_tokens))
+        if not self._h:
+            raise ValueError("need 0 < beta <= 1, n_hat0 >= 0, budget_tokens >= 1")
+        self._buf = np.empty(1024, dtype=np.int64)
+
+    def __del__(self):
+        if getattr(self, "_h", None):
+            self._lib.adaflash_admission_destroy(self._h)
+            self._h = None
+
+    def _i64(self, a):
+        a = self._np.ascontiguousarray(a, dtype=self._np.int64)
+        return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+
+    def enqueue(self, ids):
+        a, p = self._i64(ids)
+        _check(self._lib.adaflash_admission_enqueue(self._h, p, len(a)))
+
+    def propose(self):
+        while True:
+            n = self._lib.adaflash_admission_propose(self._h, self._buf.ctypes.data_as(
+                ctypes.POINTER(ctypes.c_int64)), len(self._buf))
+            if n >= 0:
+                return self._buf[:n].tolist()
+            self._buf = self._np.empty(2 * len(self._buf), dtype=self._np.int64)
+
+    def commit(self, k_hat):
+        k = self._np.ascontiguousarray(k_hat, dtype=self._np.int32)
+        out = self._np.empty(max(1, len(k)), dtype=self._np.int64)
+        m = self._lib.adaflash_admission_commit(self._h, k.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), len(k),
+                                                out.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)))
+        if m < 0:
+            _check(m)
+        return out[:m].tolist()
+
+    def finish(self, done_ids):
+        a, p = self._i64(done_ids)
+        _check(self._lib.adaflash_admission_finish(self._h, p, len(a)))
+
+    @property
+    def n_hat(self) -> float:
+        return float(self._lib.adaflash_admission_estimate(self._h))
+
+    @property
+    def pending(self) -> int:
+        return int(self._lib.adaflash_admission_pending(self._h))

@@ -254,6 +254,40 @@ ADAFLASH_API int adaflash_length_head_backward(const void* hidden, const void* W
                                   float* dW1, float* db1, float* dw2, float* db2, void* workspace,
                                   size_t workspace_bytes, void* stream);
 
+/*
+ * Verification-batch admission controller (host only; no GPU call).
+ * AdaFlash review (ZH), section 2.3, and AdaFlash review (EN), "Adaptive
+ * request scheduling for variable verification lengths": with per-request
+ * verify lengths the verify batch is packed to sum_i k_hat_i tokens, so the
+ * scheduler smooths the number of requests a round actually advanced,
+ * N_hat <- (1 - beta) N_hat + beta N, admits up to that many next round, and
+ * returns requests that still overflow the budget to the pending queue.
+ * One round:
+ *   n = adaflash_admission_propose(h, ids, cap)   running requests, then
+ *       pending ones in arrival order until the batch holds
+ *       max(1, floor(N_hat + 0.5)); the caller computes k_hat for them
+ *       (adaflash_length_head_forward);
+ *   m = adaflash_admission_commit(h, k_hat, n, ids)   while sum k_hat exceeds
+ *       budget_tokens (and m > 1) the most recently placed request goes back
+ *       to the front of the pending queue, order kept; N = m updates N_hat;
+ *       ids[0..m) is the batch to verify;
+ *   adaflash_admission_finish(h, done, nd)   after verification, drops the
+ *       requests that completed.
+ * Request ids are the caller's (int64); host pointers; the handle is not
+ * thread-safe.  Functions return ADAFLASH_OK / a count, or ADAFLASH_E_INVALID
+ * (nothing changed) on a NULL handle, a negative count, a too small `cap`, or
+ * a k_hat count different from the proposed batch.
+ */
+ADAFLASH_API void* adaflash_admission_create(double beta, double n_hat0, int64_t budget_tokens);  /* NULL if
+                                      beta not in (0, 1], n_hat0 < 0 or not finite, budget < 1 */
+ADAFLASH_API void adaflash_admission_destroy(void* h);
+ADAFLASH_API int adaflash_admission_enqueue(void* h, const int64_t* ids, int n);
+ADAFLASH_API int adaflash_admission_propose(void* h, int64_t* out_ids, int cap);
+ADAFLASH_API int adaflash_admission_commit(void* h, const int32_t* k_hat, int n, int64_t* out_ids);
+ADAFLASH_API int adaflash_admission_finish(void* h, const int64_t* done_ids, int n);
+ADAFLASH_API double adaflash_admission_estimate(const void* h);   /* N_hat (NaN for NULL) */
+ADAFLASH_API int adaflash_admission_pending(const void* h);       /* pending queue length */
+
 #ifdef __cplusplus
 }
 #endif
