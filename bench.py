@@ -42,6 +42,10 @@ def parse():
     ap.add_argument("--variant", choices=["rkl", "rkl_clip", "mixture", "fkl", "wce"], default=None,
                     help="with --mode opd: a supervision loss variant (pages' defaults: delta 0.01, "
                          "alpha 0.8, position decay 7)")
+    ap.add_argument("--layout", choices=["padded", "packed"], default="padded",
+                    help="logits layout: padded [B, k+1, V] or packed [sum(L_b+1), V]")
+    ap.add_argument("--workload", choices=["c128", "c32", "single"], default="c128",
+                    help="batch shape (default: the headline B=128 configuration)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-probe", action="store_true",
@@ -81,12 +85,12 @@ def copy_probe():
     print(json.dumps({"copy_probe_bytes": n, "calls": 5}))
 
 
-def measured_traffic(mode):
+def measured_traffic(mode, default_shape=True):
     """HBM bytes per launch of the fused kernel from the committed rocprofv3
     counter summary, or None when the kernel source changed since then."""
     import hashlib
     import re
-    if mode != "fused" or not os.path.exists(TRAFFIC_PROFILE):
+    if mode != "fused" or not default_shape or not os.path.exists(TRAFFIC_PROFILE):
         return None
     m = re.search(r"```json\n(.*?)\n```", open(TRAFFIC_PROFILE).read(), re.S)
     if not m:
@@ -283,8 +287,12 @@ def main():
     import diffusion_drafter_verification_amd as ada
     import workloads as W
 
-    wl = W.WORKLOADS[4]
+    wl = W.WORKLOADS[{"single": 2, "c32": 3, "c128": 4}[args.workload]]
     B, k, V = wl.B, wl.k, wl.V
+    packed = args.layout == "packed"
+    if packed and args.variant:
+        print("the loss variants take the padded layout", file=sys.stderr)
+        sys.exit(2)
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
 
@@ -294,9 +302,14 @@ def main():
         sets.append(bt)
     dsets = []
     for bt in sets:
+        tgt, drf = bt.target, bt.draft
+        if packed:  # the verify pass's own layout: only the real rows, request after request
+            L = np.clip(bt.verify_len, 1, k)
+            tgt = np.concatenate([bt.target[b, :L[b] + 1] for b in range(B)])
+            drf = np.concatenate([bt.draft[b, :L[b]] for b in range(B)])
         dsets.append({
-            "t": torch.from_numpy(bt.target.view(np.int16)).view(torch.bfloat16).to(dev),
-            "d": torch.from_numpy(bt.draft.view(np.int16)).view(torch.bfloat16).to(dev),
+            "t": torch.from_numpy(np.ascontiguousarray(tgt).view(np.int16)).view(torch.bfloat16).to(dev),
+            "d": torch.from_numpy(np.ascontiguousarray(drf).view(np.int16)).view(torch.bfloat16).to(dev),
             "tok": torch.from_numpy(bt.tokens).to(dev),
             "vl": torch.from_numpy(bt.verify_len).to(dev),
             "u": torch.from_numpy(bt.uniforms).to(dev),
@@ -319,14 +332,18 @@ def main():
             p1, p2 = vparams[args.variant]
             ada.adaflash_loss_variant_fwd_bwd(ds["t"], ds["d"], ds["vl"], args.variant, p1, p2, ro, ce, grad,
                                               status, ws, stream)
+        elif args.mode == "opd" and packed:
+            ada.adaflash_opd_loss_fwd_bwd_packed(ds["t"], ds["d"], ds["vl"], k, args.clip, args.lam, ro, ce, rk,
+                                                 grad, status, ws, stream)
         elif args.mode == "opd":
             ada.adaflash_opd_loss_fwd_bwd(ds["t"], ds["d"], ds["vl"], args.clip, args.lam, ro, ce, rk, grad,
                                           status, ws, stream)
         else:
             fused = args.mode == "fused"
-            ada.adaflash_verify(ds["t"], ds["d"], ds["tok"], ds["vl"], ds["u"], 1.0, acc, outt, mg, args.clip,
-                                args.lam, ro, ce if fused else None, rk if fused else None,
-                                grad if fused else None, status, ws, stream)
+            fn = ada.adaflash_verify_packed if packed else ada.adaflash_verify
+            fn(ds["t"], ds["d"], ds["tok"], ds["vl"], ds["u"], 1.0, acc, outt, mg, args.clip,
+               args.lam, ro, ce if fused else None, rk if fused else None,
+               grad if fused else None, status, ws, stream)
 
     # accept lengths per set (for the bonus-row byte count)
     accs = []
@@ -378,10 +395,11 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": ("c128 fused verify+supervision: B=128, k=16, V=151936, bf16 logits, "
-                         "verify_len~U{1..16}, sigma_b~U{0.3,1,2}, T=1, c=%g, lambda=%g, mode=%s%s"
-                         % (args.clip, args.lam, args.mode,
-                            (", variant=%s" % args.variant) if args.variant else "")),
+            "workload": ("%s fused verify+supervision: B=%d, k=%d, V=%d, bf16 logits, "
+                         "verify_len%s, sigma_b~U{0.3,1,2}, T=1, c=%g, lambda=%g, mode=%s%s, layout=%s"
+                         % (args.workload, B, k, V, ("~U{1..%d}" % k) if wl.ragged else ("=%d" % k),
+                            args.clip, args.lam, args.mode,
+                            (", variant=%s" % args.variant) if args.variant else "", args.layout)),
             "B": B, "k": k, "V": V, "input_sets": args.sets,
         },
         "roofline": {
@@ -390,7 +408,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": measured_traffic(args.mode),
+            "traffic": measured_traffic(args.mode, args.workload == "c128" and not packed),
         },
         "kernel_ms_avg": avg_dur * 1e3,
         "kernel_ms_p10_p50_p90": [float(np.percentile(durs, q) * 1e3) for q in (10, 50, 90)],

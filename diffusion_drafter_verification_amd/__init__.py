@@ -9,6 +9,8 @@ the library is missing or the tensors are not on the GPU, calls raise.
 Entry points (same names as the C ABI):
   adaflash_verify(...)            speculative verification, optional fused supervision
   adaflash_opd_loss_fwd_bwd(...)  supervision only
+  adaflash_verify_packed(...), adaflash_opd_loss_fwd_bwd_packed(...)
+                                  the same on logits packed request after request
   adaflash_workspace_bytes(B, k, V)
 Convenience wrappers allocating the outputs: ``verify`` and ``opd_loss_fwd_bwd``.
 """
@@ -62,6 +64,10 @@ def load_library() -> ctypes.CDLL:
         lib.adaflash_opd_loss_fwd_bwd.restype = i32
         lib.adaflash_opd_loss_fwd_bwd.argtypes = [i32, vp, vp, vp, i32, i32, i32, f32, f32, vp, vp,
                                                   vp, vp, vp, vp, sz, vp]
+        lib.adaflash_verify_packed.restype = i32
+        lib.adaflash_verify_packed.argtypes = lib.adaflash_verify.argtypes
+        lib.adaflash_opd_loss_fwd_bwd_packed.restype = i32
+        lib.adaflash_opd_loss_fwd_bwd_packed.argtypes = lib.adaflash_opd_loss_fwd_bwd.argtypes
         lib.adaflash_loss_variant_fwd_bwd.restype = i32
         lib.adaflash_loss_variant_fwd_bwd.argtypes = [i32, vp, vp, vp, i32, i32, i32, i32, f32, f32, vp, vp, vp,
                                                       vp, vp, sz, vp]
@@ -158,6 +164,34 @@ def adaflash_opd_loss_fwd_bwd(target, draft, verify_len, clip_c, lam, row_offset
     _check(rc)
 
 
+def adaflash_verify_packed(target, draft, tokens, verify_len, uniforms, T, accept_len, out_tokens, margins,
+                           clip_c, lam, row_offsets, loss_ce, loss_rkl, grad_draft, status, ws,
+                           stream=None) -> None:
+    """Direct binding of adaflash_verify_packed: target [sum(L_b+1), V], draft
+    [sum L_b, V]; B and k come from tokens [B, k]."""
+    B, k = tokens.shape
+    V = target.shape[-1]
+    rc = load_library().adaflash_verify_packed(
+        _dtype_code(target), _ptr(target), _ptr(draft), _ptr(tokens), _ptr(verify_len), _ptr(uniforms),
+        B, k, V, float(T), _ptr(accept_len), _ptr(out_tokens), _ptr(margins), float(clip_c),
+        float(lam), _ptr(row_offsets), _ptr(loss_ce), _ptr(loss_rkl), _ptr(grad_draft), _ptr(status),
+        _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream))
+    _check(rc)
+
+
+def adaflash_opd_loss_fwd_bwd_packed(target, draft, verify_len, k, clip_c, lam, row_offsets, loss_ce,
+                                     loss_rkl, grad_draft, status, ws, stream=None) -> None:
+    """Direct binding of adaflash_opd_loss_fwd_bwd_packed: target
+    [sum(L_b+1), V], draft [sum L_b, V]; B from verify_len [B]."""
+    B = verify_len.shape[0]
+    V = target.shape[-1]
+    rc = load_library().adaflash_opd_loss_fwd_bwd_packed(
+        _dtype_code(target), _ptr(target), _ptr(draft), _ptr(verify_len), B, int(k), V, float(clip_c),
+        float(lam), _ptr(row_offsets), _ptr(loss_ce), _ptr(loss_rkl), _ptr(grad_draft), _ptr(status),
+        _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream))
+    _check(rc)
+
+
 def verify(target: torch.Tensor, draft: Optional[torch.Tensor], tokens: torch.Tensor,
            verify_len: torch.Tensor, uniforms: Optional[torch.Tensor], T: float,
            opd: bool = False, clip_c: float = 10.0, lam: float = 1.0, margins: bool = True,
@@ -206,6 +240,58 @@ def opd_loss_fwd_bwd(target: torch.Tensor, draft: torch.Tensor, verify_len: Opti
         ws = workspace(B, k, V, dev)
     adaflash_opd_loss_fwd_bwd(target, draft, verify_len, clip_c, lam, out["row_offsets"],
                               out["loss_ce"], out["loss_rkl"], out["grad"], out["status"], ws, stream)
+    return out
+
+
+def verify_packed(target: torch.Tensor, draft: Optional[torch.Tensor], tokens: torch.Tensor,
+                  verify_len: torch.Tensor, uniforms: Optional[torch.Tensor], T: float,
+                  opd: bool = False, clip_c: float = 10.0, lam: float = 1.0, margins: bool = True,
+                  ws: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """As ``verify`` on packed logits (target [sum(L_b+1), V], draft
+    [sum L_b, V]); the gradient has one row per draft row."""
+    B, k = tokens.shape
+    V = target.shape[-1]
+    dev = target.device
+    out = {
+        "accept_len": torch.empty(B, dtype=torch.int32, device=dev),
+        "out_tokens": torch.empty(B, k + 1, dtype=torch.int32, device=dev),
+        "margins": torch.empty(B, k + 1, dtype=torch.float32, device=dev) if margins else None,
+        "row_offsets": torch.empty(B + 1, dtype=torch.int32, device=dev),
+        "status": torch.empty(1, dtype=torch.int32, device=dev),
+        "loss_ce": None, "loss_rkl": None, "grad": None,
+    }
+    if opd:
+        n = draft.shape[0]
+        out["loss_ce"] = torch.empty(max(n, 1), dtype=torch.float32, device=dev)
+        out["loss_rkl"] = torch.empty(max(n, 1), dtype=torch.float32, device=dev)
+        out["grad"] = torch.empty(max(n, 1), V, dtype=target.dtype, device=dev)
+    if ws is None:
+        ws = workspace(B, k, V, dev)
+    adaflash_verify_packed(target, draft, tokens, verify_len, uniforms, T, out["accept_len"],
+                           out["out_tokens"], out["margins"], clip_c, lam, out["row_offsets"], out["loss_ce"],
+                           out["loss_rkl"], out["grad"], out["status"], ws, stream)
+    return out
+
+
+def opd_loss_fwd_bwd_packed(target: torch.Tensor, draft: torch.Tensor, verify_len: torch.Tensor, k: int,
+                            clip_c: float = 10.0, lam: float = 1.0, with_grad: bool = True,
+                            ws: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """As ``opd_loss_fwd_bwd`` on packed logits."""
+    B = verify_len.shape[0]
+    V = target.shape[-1]
+    dev = target.device
+    n = max(draft.shape[0], 1)
+    out = {
+        "row_offsets": torch.empty(B + 1, dtype=torch.int32, device=dev),
+        "status": torch.empty(1, dtype=torch.int32, device=dev),
+        "loss_ce": torch.empty(n, dtype=torch.float32, device=dev),
+        "loss_rkl": torch.empty(n, dtype=torch.float32, device=dev),
+        "grad": torch.empty(n, V, dtype=target.dtype, device=dev) if with_grad else None,
+    }
+    if ws is None:
+        ws = workspace(B, k, V, dev)
+    adaflash_opd_loss_fwd_bwd_packed(target, draft, verify_len, k, clip_c, lam, out["row_offsets"],
+                                     out["loss_ce"], out["loss_rkl"], out["grad"], out["status"], ws, stream)
     return out
 
 

@@ -95,12 +95,12 @@ static int run(LaunchArgs& a, void* workspace) {
   return ADAFLASH_OK;
 }
 
-int adaflash_verify(adaflash_dtype dtype, const void* target_logits, const void* draft_logits,
-                    const int32_t* draft_tokens, const int32_t* verify_len, const float* uniforms,
-                    int B, int k, int V, float T, int32_t* accept_len, int32_t* out_tokens,
-                    float* margins, float clip_c, float lambda, int32_t* row_offsets,
-                    float* loss_ce, float* loss_rkl, void* grad_draft, int32_t* status_flags,
-                    void* workspace, size_t workspace_bytes, void* stream) {
+static int verify_impl(int packed, adaflash_dtype dtype, const void* target_logits, const void* draft_logits,
+                       const int32_t* draft_tokens, const int32_t* verify_len, const float* uniforms,
+                       int B, int k, int V, float T, int32_t* accept_len, int32_t* out_tokens,
+                       float* margins, float clip_c, float lambda, int32_t* row_offsets,
+                       float* loss_ce, float* loss_rkl, void* grad_draft, int32_t* status_flags,
+                       void* workspace, size_t workspace_bytes, void* stream) {
   const bool opd = loss_ce || loss_rkl || grad_draft;
   if (!(T >= 0.f) || std::isinf(T)) return fail(ADAFLASH_E_INVALID, "T must be finite and >= 0%s");
   const bool need_draft = T > 0.f || opd;
@@ -126,6 +126,7 @@ int adaflash_verify(adaflash_dtype dtype, const void* target_logits, const void*
   a.V = V;
   a.T = T;
   a.verify = 1;
+  a.packed = packed;
   a.opd = opd ? 1 : 0;
   a.clip_c = clip_c;
   a.lambda = lambda;
@@ -141,12 +142,12 @@ int adaflash_verify(adaflash_dtype dtype, const void* target_logits, const void*
   return run(a, workspace);
 }
 
-int adaflash_opd_loss_fwd_bwd(adaflash_dtype dtype, const void* target_logits,
-                              const void* draft_logits, const int32_t* verify_len, int B, int k,
-                              int V, float clip_c, float lambda, int32_t* row_offsets,
-                              float* loss_ce, float* loss_rkl, void* grad_draft,
-                              int32_t* status_flags, void* workspace, size_t workspace_bytes,
-                              void* stream) {
+static int opd_impl(int packed, adaflash_dtype dtype, const void* target_logits,
+                    const void* draft_logits, const int32_t* verify_len, int B, int k,
+                    int V, float clip_c, float lambda, int32_t* row_offsets,
+                    float* loss_ce, float* loss_rkl, void* grad_draft,
+                    int32_t* status_flags, void* workspace, size_t workspace_bytes,
+                    void* stream) {
   int rc = common_checks(dtype, target_logits, draft_logits, B, k, V, row_offsets, workspace,
                          workspace_bytes, true);
   if (rc != ADAFLASH_OK) return rc;
@@ -163,6 +164,7 @@ int adaflash_opd_loss_fwd_bwd(adaflash_dtype dtype, const void* target_logits,
   a.V = V;
   a.T = 1.f;
   a.verify = 0;
+  a.packed = packed;
   a.opd = 1;
   a.clip_c = clip_c;
   a.lambda = lambda;
@@ -173,6 +175,48 @@ int adaflash_opd_loss_fwd_bwd(adaflash_dtype dtype, const void* target_logits,
   a.status = status_flags;
   a.stream = (hipStream_t)stream;
   return run(a, workspace);
+}
+
+int adaflash_verify(adaflash_dtype dtype, const void* target_logits, const void* draft_logits,
+                    const int32_t* draft_tokens, const int32_t* verify_len, const float* uniforms,
+                    int B, int k, int V, float T, int32_t* accept_len, int32_t* out_tokens,
+                    float* margins, float clip_c, float lambda, int32_t* row_offsets,
+                    float* loss_ce, float* loss_rkl, void* grad_draft, int32_t* status_flags,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  return verify_impl(0, dtype, target_logits, draft_logits, draft_tokens, verify_len, uniforms, B, k, V, T,
+                     accept_len, out_tokens, margins, clip_c, lambda, row_offsets, loss_ce, loss_rkl, grad_draft,
+                     status_flags, workspace, workspace_bytes, stream);
+}
+
+int adaflash_verify_packed(adaflash_dtype dtype, const void* target_logits, const void* draft_logits,
+                           const int32_t* draft_tokens, const int32_t* verify_len, const float* uniforms,
+                           int B, int k, int V, float T, int32_t* accept_len, int32_t* out_tokens,
+                           float* margins, float clip_c, float lambda, int32_t* row_offsets,
+                           float* loss_ce, float* loss_rkl, void* grad_draft, int32_t* status_flags,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  return verify_impl(1, dtype, target_logits, draft_logits, draft_tokens, verify_len, uniforms, B, k, V, T,
+                     accept_len, out_tokens, margins, clip_c, lambda, row_offsets, loss_ce, loss_rkl, grad_draft,
+                     status_flags, workspace, workspace_bytes, stream);
+}
+
+int adaflash_opd_loss_fwd_bwd(adaflash_dtype dtype, const void* target_logits,
+                              const void* draft_logits, const int32_t* verify_len, int B, int k,
+                              int V, float clip_c, float lambda, int32_t* row_offsets,
+                              float* loss_ce, float* loss_rkl, void* grad_draft,
+                              int32_t* status_flags, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  return opd_impl(0, dtype, target_logits, draft_logits, verify_len, B, k, V, clip_c, lambda, row_offsets,
+                  loss_ce, loss_rkl, grad_draft, status_flags, workspace, workspace_bytes, stream);
+}
+
+int adaflash_opd_loss_fwd_bwd_packed(adaflash_dtype dtype, const void* target_logits,
+                                     const void* draft_logits, const int32_t* verify_len, int B, int k,
+                                     int V, float clip_c, float lambda, int32_t* row_offsets,
+                                     float* loss_ce, float* loss_rkl, void* grad_draft,
+                                     int32_t* status_flags, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+  return opd_impl(1, dtype, target_logits, draft_logits, verify_len, B, k, V, clip_c, lambda, row_offsets,
+                  loss_ce, loss_rkl, grad_draft, status_flags, workspace, workspace_bytes, stream);
 }
 
 int adaflash_loss_variant_fwd_bwd(adaflash_dtype dtype, const void* target_logits, const void* draft_logits,

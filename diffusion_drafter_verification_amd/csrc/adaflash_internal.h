@@ -38,8 +38,8 @@ size_t workspace_layout(int B, int k, int V, char* base, Workspace* ws);
 
 struct LaunchArgs {
   int bf16;               // 1: bf16 logits, 0: fp32
-  const void* target;     // [B, k+1, V]
-  const void* draft;      // [B, k, V] (may be null for greedy verify without supervision)
+  const void* target;     // [B, k+1, V] (packed: [sum(L_b+1), V])
+  const void* draft;      // [B, k, V] (packed: [sum L_b, V]; may be null for greedy verify without supervision)
   const int32_t* tokens;  // [B, k] (verify only)
   const int32_t* verify_len;  // [B] or null (= k)
   const float* uniforms;  // [B, k+1] (sampled verify only)
@@ -52,6 +52,7 @@ struct LaunchArgs {
   float wdecay = 0.f;     // per-position weight exp(-i / wdecay); 0 = none
   int fkl = 0;            // 1: forward KL(p || q) instead of the reverse KL
   float* loss_var = nullptr;  // [N] combined per-row loss of a variant, or null
+  int packed = 0;         // 1: target [sum(L_b+1), V], draft [sum L_b, V] (rows in request order)
   int32_t* accept_len;
   int32_t* out_tokens;
   float* margins;

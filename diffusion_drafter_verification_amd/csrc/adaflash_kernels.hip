@@ -86,6 +86,9 @@ struct KParams {
   // exp(-i / wdecay)), and the combined per-row loss output (or null).
   float a_ce, wdecay;
   float* loss_var;
+  // Logit layout: 0 = padded [B, k+1, V] / [B, k, V]; 1 = packed
+  // [sum (L_b + 1), V] / [sum L_b, V] (rows located through row_offsets).
+  int packed;
 };
 
 // ---------------------------------------------------------------- primitives
@@ -463,6 +466,27 @@ __device__ __forceinline__ float sload_logit(const void* row, int v) {
   }
 }
 
+// Logit rows of request b, position i, in either layout.  The packed row
+// of target position i is row_offsets[b] + b + i (L_b + 1 rows per request),
+// of draft position i row_offsets[b] + i; row_offsets is the pack kernel's
+// prefix sum of the clamped verify lengths.
+__device__ __forceinline__ size_t target_row_index(const KParams& P, int b, int i) {
+  return P.packed ? (size_t)(int)sload_u32(P.row_offsets + b) + b + i : (size_t)b * (P.k + 1) + i;
+}
+__device__ __forceinline__ size_t draft_row_index(const KParams& P, int b, int i) {
+  return P.packed ? (size_t)(int)sload_u32(P.row_offsets + b) + i : (size_t)b * P.k + i;
+}
+template <bool BF16>
+__device__ __forceinline__ const void* target_row_ptr(const KParams& P, int b, int i) {
+  const size_t row = target_row_index(P, b, i);
+  return BF16 ? (const void*)((const uint16_t*)P.target + row * P.V) : (const void*)((const float*)P.target + row * P.V);
+}
+template <bool BF16>
+__device__ __forceinline__ const void* draft_row_ptr(const KParams& P, int b, int i) {
+  const size_t row = draft_row_index(P, b, i);
+  return BF16 ? (const void*)((const uint16_t*)P.draft + row * P.V) : (const void*)((const float*)P.draft + row * P.V);
+}
+
 // Two values rounded to bf16 (nearest even) and packed: one v_cvt_pk_bf16_f32.
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -624,6 +648,7 @@ __device__ void finalize_request(const KParams& P, int b, FinShared& fs) {
   const int k = P.k, V = P.V, G = P.G;
   const int tid = threadIdx.x;
   const int L = P.Lc[b];
+  if (L < 0) return;  // packed rows unusable (see pack_kernel)
   const int r0 = b * (k + 1);  // row slot of position 0
   int A = L, token = 0;
   float sample_margin = __int_as_float(0x7fc00000);
@@ -711,10 +736,8 @@ __device__ void finalize_request(const KParams& P, int b, FinShared& fs) {
 
     // Scan chunk jc in index order: per-entry masses, one prefix sum over
     // (slot, thread, entry), the lowest index whose running sum passes thr.
-    const void* trow = BF16 ? (const void*)((const uint16_t*)P.target + (size_t)rs * V)
-                            : (const void*)((const float*)P.target + (size_t)rs * V);
-    const void* drow = BF16 ? (const void*)((const uint16_t*)P.draft + ((size_t)b * k + A) * V)
-                            : (const void*)((const float*)P.draft + ((size_t)b * k + A) * V);
+    const void* trow = target_row_ptr<BF16>(P, b, A);
+    const void* drow = draft_row_ptr<BF16>(P, b, A);
     const int v0 = jc * kChunk;
     Chunk<BF16> cp, cq;
     load_chunk<BF16, ALIGNED>(cp, trow, v0, V);
@@ -845,19 +868,16 @@ __global__ __launch_bounds__(kThreads) void row_kernel(KParams P) {
   const int j = (int)blockIdx.x - s_ * G;
   const int b = s_ / (k + 1), i = s_ - b * (k + 1);
   const int L = P.Lc[b];
-  if (i > L || (!VERIFY && i == L)) return;
+  if (L < 0 || i > L || (!VERIFY && i == L)) return;
   const int r = s_;
-  const int rid = r;
   const bool draft_row = i < L;
   const bool need_q = draft_row && (OPD || SAMPLED);
   const int v0 = j * kChunk;
 
-  const void* trow = BF16 ? (const void*)((const uint16_t*)P.target + (size_t)rid * V)
-                          : (const void*)((const float*)P.target + (size_t)rid * V);
+  const void* trow = target_row_ptr<BF16>(P, b, i);
   const void* drow = nullptr;
   if (need_q)
-    drow = BF16 ? (const void*)((const uint16_t*)P.draft + ((size_t)b * k + i) * V)
-                : (const void*)((const float*)P.draft + ((size_t)b * k + i) * V);
+    drow = draft_row_ptr<BF16>(P, b, i);
 
   // ---- phase 1: load the chunk, chunk maxima, argmax, sums of exponentials.
   Chunk<BF16> cp, cq;
@@ -1319,18 +1339,17 @@ __global__ __launch_bounds__(kThreads, (sup_min_waves<BF16, ALIGNED, VMODE, FKL>
     i = -1;
   }
   const int L = P.Lc[b];
+  if (L < 0) return;
   if (i < 0) i = L;
   else if (i >= L) return;
   const int r = b * (k + 1) + i;
   const bool draft_row = i < L;
   const int v0 = j * kChunk;
 
-  const void* trow = BF16 ? (const void*)((const uint16_t*)P.target + (size_t)r * V)
-                          : (const void*)((const float*)P.target + (size_t)r * V);
+  const void* trow = target_row_ptr<BF16>(P, b, i);
   const void* drow = nullptr;
   if (draft_row)
-    drow = BF16 ? (const void*)((const uint16_t*)P.draft + ((size_t)b * k + i) * V)
-                : (const void*)((const float*)P.draft + ((size_t)b * k + i) * V);
+    drow = draft_row_ptr<BF16>(P, b, i);
 
   // ---- pass 1
   Chunk<BF16> cp, cq;
@@ -1693,17 +1712,15 @@ __global__ __launch_bounds__(kThreads) void vstat_kernel(KParams P) {
   const int j = (int)blockIdx.x - s_ * G;
   const int b = s_ / (k + 1), i = s_ - b * (k + 1);
   const int L = P.Lc[b];
-  if (i > L) return;
+  if (L < 0 || i > L) return;
   const int r = s_;
   const bool draft_row = i < L;
   const int v0 = j * kChunk;
-  const void* trow = BF16 ? (const void*)((const uint16_t*)P.target + (size_t)r * V)
-                          : (const void*)((const float*)P.target + (size_t)r * V);
+  const void* trow = target_row_ptr<BF16>(P, b, i);
   Chunk<BF16> cp, cq;
   load_chunk<BF16, ALIGNED>(cp, trow, v0, V);
   if (draft_row) {
-    const void* drow = BF16 ? (const void*)((const uint16_t*)P.draft + ((size_t)b * k + i) * V)
-                            : (const void*)((const float*)P.draft + ((size_t)b * k + i) * V);
+    const void* drow = draft_row_ptr<BF16>(P, b, i);
     load_chunk<BF16, ALIGNED>(cq, drow, v0, V);
   }
   float m[2] = {chunk_max<BF16>(cp), draft_row ? chunk_max<BF16>(cq) : neg_inf()};
@@ -1785,6 +1802,7 @@ __global__ __launch_bounds__(kThreads) void vres_kernel(KParams P) {
   const int h = (int)blockIdx.x - b * GH;  // chunks kResChunks*h ...
   const int j = h;                         // (workgroup h == 0 writes the row flags)
   const int L = P.Lc[b];
+  if (L < 0) return;
   const int r0 = b * (k + 1);
   const int grp = tid >> 4, l16 = tid & 15;  // 16 groups of 16 lanes
   for (int i0 = 0; i0 < L; i0 += kThreads / 16) {
@@ -1813,10 +1831,8 @@ __global__ __launch_bounds__(kThreads) void vres_kernel(KParams P) {
         if (j == 0) flag(P.status, ADAFLASH_FLAG_BAD_TOKEN);
         x = x < 0 ? 0 : V - 1;
       }
-      const void* trow = BF16 ? (const void*)((const uint16_t*)P.target + (size_t)r * V)
-                              : (const void*)((const float*)P.target + (size_t)r * V);
-      const void* drow = BF16 ? (const void*)((const uint16_t*)P.draft + ((size_t)b * k + i) * V)
-                              : (const void*)((const float*)P.draft + ((size_t)b * k + i) * V);
+      const void* trow = target_row_ptr<BF16>(P, b, i);
+      const void* drow = draft_row_ptr<BF16>(P, b, i);
       const float zpx = load_logit<BF16>(trow, x), zqx = load_logit<BF16>(drow, x);
       const float px = fexp2((zpx - RMp) * P.kT) / SpT;
       const float qx = fexp2((zqx - RMq) * P.kT) / SqT;
@@ -1844,10 +1860,8 @@ __global__ __launch_bounds__(kThreads) void vres_kernel(KParams P) {
   if (A >= L) return;  // every draft accepted: the bonus draw needs no residual
 
   const int rA = r0 + A;
-  const void* trow = BF16 ? (const void*)((const uint16_t*)P.target + (size_t)rA * V)
-                          : (const void*)((const float*)P.target + (size_t)rA * V);
-  const void* drow = BF16 ? (const void*)((const uint16_t*)P.draft + ((size_t)b * k + A) * V)
-                          : (const void*)((const float*)P.draft + ((size_t)b * k + A) * V);
+  const void* trow = target_row_ptr<BF16>(P, b, A);
+  const void* drow = draft_row_ptr<BF16>(P, b, A);
   // All chunks' loads first, then the arithmetic.
   Chunk<BF16> cp[kResChunks], cq[kResChunks];
 #pragma unroll
@@ -1901,7 +1915,7 @@ __global__ __launch_bounds__(kThreads) void final_kernel(KParams P) {
 // row offsets (prefix sum: a scan inside each wave, then across the 16
 // waves), clears the arrival counters, marks every row's accept flag as not
 // yet known, and initialises the status word.
-__global__ __launch_bounds__(1024) void pack_kernel(const int32_t* verify_len, int B, int k,
+__global__ __launch_bounds__(1024) void pack_kernel(const int32_t* verify_len, int B, int k, int packed,
                                                      int32_t* row_offsets, Workspace ws, int32_t* status) {
   __shared__ int s_wave[16];
   __shared__ int s_flags;
@@ -1946,6 +1960,11 @@ __global__ __launch_bounds__(1024) void pack_kernel(const int32_t* verify_len, i
     carry += tot;
     __syncthreads();
   }
+  // Packed logits are located through the caller's own lengths: with one of
+  // them out of range the rows cannot be found, so every request is marked
+  // unusable (Lc = -1) and the row kernels read nothing.
+  if (packed && s_flags)
+    for (int b = tid; b < B; b += 1024) ws.Lc[b] = -1;
   if (tid == 0) {
     row_offsets[B] = carry;
     if (status) *status = s_flags;
@@ -1999,7 +2018,7 @@ hipError_t dispatch_mode(const KParams& p, int grid, int opd, int vmode, bool t1
 
 hipError_t launch(const LaunchArgs& a) {
   const int bonus = a.verify ? 1 : 0;
-  hipLaunchKernelGGL(pack_kernel, dim3(1), dim3(1024), 0, a.stream, a.verify_len, a.B, a.k,
+  hipLaunchKernelGGL(pack_kernel, dim3(1), dim3(1024), 0, a.stream, a.verify_len, a.B, a.k, a.packed,
                      a.row_offsets, a.ws, a.status);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.B == 0) return e;
@@ -2032,6 +2051,7 @@ hipError_t launch(const LaunchArgs& a) {
   p.a_ce = a.a_ce;
   p.wdecay = a.wdecay;
   p.loss_var = a.loss_var;
+  p.packed = a.packed;
 
   const int vmode = a.verify ? (a.T > 0.f ? 2 : 1) : 0;
   const int rows_max = a.B * (a.k + bonus);

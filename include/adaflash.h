@@ -160,6 +160,46 @@ ADAFLASH_API int adaflash_opd_loss_fwd_bwd(adaflash_dtype dtype, const void* tar
                               void* stream);
 
 /*
+ * Packed-logits forms of adaflash_verify and adaflash_opd_loss_fwd_bwd.
+ *
+ * AdaFlash review (ZH), section 2.3, and AdaFlash review (EN), "Adaptive
+ * request scheduling for variable verification lengths": the target's verify
+ * pass runs over only the real verify tokens of each request, sum_b k_hat_b
+ * positions instead of B x k, so its logits arrive packed request after
+ * request.  These entry points read them in place, with no scatter into the
+ * padded [B, k+1, V] form:
+ *
+ *   target_logits [sum_b (L_b + 1), V]  request b's rows i = 0..L_b (the last
+ *                              one is its bonus row) start at row
+ *                              row_offsets[b] + b.  (For the supervision-only
+ *                              form the bonus rows are present but not read.)
+ *   draft_logits  [sum_b L_b, V]  request b's rows i = 0..L_b-1 start at row
+ *                              row_offsets[b] -- the same order as the packed
+ *                              supervision outputs.
+ *
+ * Every other argument, output and error is as in the padded form (draft
+ * tokens, uniforms and margins stay [B, k] / [B, k+1]).  L_b must lie in
+ * [1, k]: the packed rows are found through the lengths themselves, so when
+ * one of them is outside that range (ADAFLASH_FLAG_BAD_VERIFY_LEN) no logits
+ * row is read and the outputs other than row_offsets and status_flags are
+ * left unwritten.  verify_len == NULL (supervision only) means L_b = k.
+ * The workspace is the padded form's (adaflash_workspace_bytes).
+ */
+ADAFLASH_API int adaflash_verify_packed(adaflash_dtype dtype, const void* target_logits, const void* draft_logits,
+                    const int32_t* draft_tokens, const int32_t* verify_len, const float* uniforms,
+                    int B, int k, int V, float T, int32_t* accept_len, int32_t* out_tokens,
+                    float* margins, float clip_c, float lambda, int32_t* row_offsets,
+                    float* loss_ce, float* loss_rkl, void* grad_draft, int32_t* status_flags,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+ADAFLASH_API int adaflash_opd_loss_fwd_bwd_packed(adaflash_dtype dtype, const void* target_logits,
+                              const void* draft_logits, const int32_t* verify_len, int B, int k,
+                              int V, float clip_c, float lambda, int32_t* row_offsets,
+                              float* loss_ce, float* loss_rkl, void* grad_draft,
+                              int32_t* status_flags, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
  * Supervision loss variants the pages compare, on the same fused row pass as
  * adaflash_opd_loss_fwd_bwd (temperature 1; p = softmax(z_p), q = softmax(z_q),
  * x* = argmax z_p, lowest index on ties; CE = -log q(x*); R_c = sum_v
