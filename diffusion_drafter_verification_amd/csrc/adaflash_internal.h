@@ -25,7 +25,8 @@ constexpr int kRec1 = 8, kRec2 = 4, kRowRec = 4;
 
 // Device scratch carved out of the caller's workspace.
 struct Workspace {
-  int32_t* Lc;       // [B]    clamped verify lengths
+  int32_t* Lc;       // [B+1]  clamped verify lengths; Lc[B] = rows in use N (0: none usable)
+  int32_t* rowmap;   // [B*k]  packed draft row n -> 64 b + i (request b, position i)
   int32_t* rowcnt;   // [B*(k+1)*kCounterStride] per-row arrival counters (zeroed per call)
   float* part1;      // [B*(k+1)*G*kRec1] per-chunk row statistics
   float* part2;      // [B*(k+1)*G*kRec2] per-chunk supervision / residual partials
