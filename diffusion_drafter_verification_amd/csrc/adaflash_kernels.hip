@@ -1351,7 +1351,10 @@ __device__ __forceinline__ float grad_exact(float zq, float zp, float lse_q2, fl
 // Workgroups per CU: aligned bf16 chunks fit 80 VGPRs (six per CU), and the
 // fused sampled variant 72 (seven per CU; two values of the rarely taken
 // exact path spill, measured faster than six); fp32 chunks take twice the
-// registers and the element-wise loads of unaligned rows more.
+// registers and the element-wise loads of unaligned rows more.  (Eight per
+// CU, 64 VGPRs, was 4% faster for supervision alone but spills chunk words
+// of the exact path and left some gradient slots of that path unwritten now
+// and then; it is not used.)
 template <bool BF16, bool ALIGNED, int VMODE, bool FKL>
 constexpr int sup_min_waves() {
   return BF16 && ALIGNED ? (FKL ? 4 : (kElems <= 32 ? (VMODE == 2 ? 7 : 6) : 4)) : 1;
