@@ -64,6 +64,10 @@ def load_library() -> ctypes.CDLL:
         lib.adaflash_opd_loss_fwd_bwd.restype = i32
         lib.adaflash_opd_loss_fwd_bwd.argtypes = [i32, vp, vp, vp, i32, i32, i32, f32, f32, vp, vp,
                                                   vp, vp, vp, vp, sz, vp]
+        lib.adaflash_timing_enable.restype = i32
+        lib.adaflash_timing_enable.argtypes = [i32]
+        lib.adaflash_timing_read.restype = i32
+        lib.adaflash_timing_read.argtypes = [ctypes.POINTER(ctypes.c_float), i32]
         lib.adaflash_verify_packed.restype = i32
         lib.adaflash_verify_packed.argtypes = lib.adaflash_verify.argtypes
         lib.adaflash_opd_loss_fwd_bwd_packed.restype = i32
@@ -127,6 +131,21 @@ def _stream(stream) -> int:
 def _check(rc: int):
     if rc != 0:
         raise AdaflashError(rc, load_library().adaflash_last_error().decode())
+
+
+def adaflash_timing_enable(max_records: int) -> None:
+    """Direct binding of adaflash_timing_enable (benchmark hook)."""
+    _check(load_library().adaflash_timing_enable(int(max_records)))
+
+
+def adaflash_timing_read(cap: int) -> list:
+    """Direct binding of adaflash_timing_read: the recorded dominant-kernel
+    durations in milliseconds."""
+    buf = (ctypes.c_float * max(int(cap), 1))()
+    n = load_library().adaflash_timing_read(buf, int(cap))
+    if n < 0:
+        _check(n)
+    return [float(buf[i]) for i in range(n)]
 
 
 def adaflash_workspace_bytes(B: int, k: int, V: int) -> int:

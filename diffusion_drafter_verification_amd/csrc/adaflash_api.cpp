@@ -66,6 +66,19 @@ extern "C" {
 
 int adaflash_version(void) { return 100; }
 
+int adaflash_timing_enable(int max_records) {
+  if (max_records < 0 || max_records > (1 << 20)) return fail(ADAFLASH_E_INVALID, "max_records out of range%s");
+  if (timing_enable(max_records) != 0) return fail(ADAFLASH_E_HIP, "hipEventCreate failed%s");
+  return ADAFLASH_OK;
+}
+
+int adaflash_timing_read(float* ms, int cap) {
+  if (cap < 0 || (cap > 0 && !ms)) return fail(ADAFLASH_E_INVALID, "bad output buffer%s");
+  const int n = timing_read(ms, cap);
+  if (n < 0) return fail(ADAFLASH_E_HIP, "event query failed%s");
+  return n;
+}
+
 const char* adaflash_last_error(void) { return g_err; }
 
 size_t adaflash_workspace_bytes(int B, int k, int V) {

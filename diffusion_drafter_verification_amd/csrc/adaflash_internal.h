@@ -70,6 +70,10 @@ struct LaunchArgs {
 // launch error.
 hipError_t launch(const LaunchArgs& a);
 
+// Measurement hook (adaflash_timing_enable / adaflash_timing_read).
+int timing_enable(int cap);
+int timing_read(float* ms, int cap);
+
 // Adaptive length head (adaflash_length_head.hip).
 struct LhWorkspace {
   float* z1;         // [S, B*k, Hp] split-K slices of the projection
