@@ -100,6 +100,12 @@ def load_library() -> ctypes.CDLL:
         lib.adaflash_length_head_backward.restype = i32
         lib.adaflash_length_head_backward.argtypes = [vp, vp, vp, vp, f32, i32, i32, i32, i32, vp, vp, vp,
                                                       vp, vp, vp, vp, vp, sz, vp]
+        lib.adaflash_length_head_forward_cached.restype = i32
+        lib.adaflash_length_head_forward_cached.argtypes = (lib.adaflash_length_head_forward.argtypes[:12] + [vp]
+                                                            + lib.adaflash_length_head_forward.argtypes[12:])
+        lib.adaflash_length_head_backward_cached.restype = i32
+        lib.adaflash_length_head_backward_cached.argtypes = (lib.adaflash_length_head_backward.argtypes[:16] + [vp]
+                                                             + lib.adaflash_length_head_backward.argtypes[16:])
         _lib = lib
     return _lib
 
@@ -377,45 +383,63 @@ def _f32(t: torch.Tensor) -> torch.Tensor:
     return t
 
 
-def adaflash_length_head_forward(hidden, W1, b1, w2, b2, gamma, a_hat, k_hat, ws, stream=None) -> None:
-    """Direct binding of adaflash_length_head_forward (see include/adaflash.h)."""
+def adaflash_length_head_forward(hidden, W1, b1, w2, b2, gamma, a_hat, k_hat, ws, stream=None,
+                                 z1_cache=None) -> None:
+    """Direct binding of adaflash_length_head_forward, or of
+    adaflash_length_head_forward_cached when z1_cache ([B k, H'] fp32) is given."""
     B, k, H = hidden.shape
     Hp = W1.shape[0]
-    rc = load_library().adaflash_length_head_forward(
-        _ptr(_bf16(hidden)), _ptr(_bf16(W1)), _ptr(_f32(b1)), _ptr(_f32(w2)), float(b2), B, k, H, Hp,
-        float(gamma), _ptr(a_hat), _ptr(k_hat), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream))
+    lib = load_library()
+    head = (_ptr(_bf16(hidden)), _ptr(_bf16(W1)), _ptr(_f32(b1)), _ptr(_f32(w2)), float(b2), B, k, H, Hp,
+            float(gamma), _ptr(a_hat), _ptr(k_hat))
+    tail = (_ptr(ws), ws.numel() if ws is not None else 0, _stream(stream))
+    if z1_cache is None:
+        rc = lib.adaflash_length_head_forward(*head, *tail)
+    else:
+        rc = lib.adaflash_length_head_forward_cached(*head, _ptr(z1_cache), *tail)
     _check(rc)
 
 
 def adaflash_length_head_backward(hidden, W1, b1, w2, b2, accept_len, verify_len, loss, dW1, db1, dw2, db2, ws,
-                                  stream=None) -> None:
-    """Direct binding of adaflash_length_head_backward (see include/adaflash.h)."""
+                                  stream=None, z1_cache=None) -> None:
+    """Direct binding of adaflash_length_head_backward, or of
+    adaflash_length_head_backward_cached when z1_cache (the forward's) is given."""
     B, k, H = hidden.shape
     Hp = W1.shape[0]
-    rc = load_library().adaflash_length_head_backward(
-        _ptr(_bf16(hidden)), _ptr(_bf16(W1)), _ptr(_f32(b1)), _ptr(_f32(w2)), float(b2), B, k, H, Hp,
-        _ptr(accept_len), _ptr(verify_len), _ptr(loss), _ptr(dW1), _ptr(db1), _ptr(dw2), _ptr(db2), _ptr(ws),
-        ws.numel() if ws is not None else 0, _stream(stream))
+    lib = load_library()
+    head = (_ptr(_bf16(hidden)), _ptr(_bf16(W1)), _ptr(_f32(b1)), _ptr(_f32(w2)), float(b2), B, k, H, Hp,
+            _ptr(accept_len), _ptr(verify_len), _ptr(loss), _ptr(dW1), _ptr(db1), _ptr(dw2), _ptr(db2))
+    tail = (_ptr(ws), ws.numel() if ws is not None else 0, _stream(stream))
+    if z1_cache is None:
+        rc = lib.adaflash_length_head_backward(*head, *tail)
+    else:
+        rc = lib.adaflash_length_head_backward_cached(*head, _ptr(z1_cache), *tail)
     _check(rc)
 
 
 def length_head_forward(hidden: torch.Tensor, W1: torch.Tensor, b1: torch.Tensor, w2: torch.Tensor, b2: float,
-                        gamma: float = 1.0, ws: Optional[torch.Tensor] = None, stream=None) -> dict:
-    """Allocates the outputs and calls adaflash_length_head_forward."""
+                        gamma: float = 1.0, ws: Optional[torch.Tensor] = None, stream=None,
+                        keep_projection: bool = False) -> dict:
+    """Allocates the outputs and calls adaflash_length_head_forward; with
+    keep_projection, out["z1"] holds the projection for the backward."""
     B, k, H = hidden.shape
     dev = hidden.device
     out = {"a_hat": torch.empty(B, dtype=torch.float32, device=dev),
            "k_hat": torch.empty(B, dtype=torch.int32, device=dev)}
+    if keep_projection:
+        out["z1"] = torch.empty(B * k, W1.shape[0], dtype=torch.float32, device=dev)
     if ws is None:
         ws = length_head_workspace(B, k, H, W1.shape[0], dev)
-    adaflash_length_head_forward(hidden, W1, b1, w2, b2, gamma, out["a_hat"], out["k_hat"], ws, stream)
+    adaflash_length_head_forward(hidden, W1, b1, w2, b2, gamma, out["a_hat"], out["k_hat"], ws, stream,
+                                 z1_cache=out.get("z1"))
     return out
 
 
 def length_head_backward(hidden: torch.Tensor, W1: torch.Tensor, b1: torch.Tensor, w2: torch.Tensor, b2: float,
                          accept_len: torch.Tensor, verify_len: torch.Tensor, ws: Optional[torch.Tensor] = None,
-                         stream=None) -> dict:
-    """Allocates the outputs and calls adaflash_length_head_backward."""
+                         stream=None, z1: Optional[torch.Tensor] = None) -> dict:
+    """Allocates the outputs and calls adaflash_length_head_backward (with z1,
+    the forward's kept projection, instead of recomputing it)."""
     B, k, H = hidden.shape
     Hp = W1.shape[0]
     dev = hidden.device
@@ -427,7 +451,7 @@ def length_head_backward(hidden: torch.Tensor, W1: torch.Tensor, b1: torch.Tenso
     if ws is None:
         ws = length_head_workspace(B, k, H, Hp, dev)
     adaflash_length_head_backward(hidden, W1, b1, w2, b2, accept_len, verify_len, out["loss"], out["dW1"],
-                                  out["db1"], out["dw2"], out["db2"], ws, stream)
+                                  out["db1"], out["dw2"], out["db2"], ws, stream, z1_cache=z1)
     return out
 
 

@@ -309,9 +309,9 @@ static int lh_checks(const void* h, const void* W1, const float* b1, const float
   return ADAFLASH_OK;
 }
 
-int adaflash_length_head_forward(const void* hidden, const void* W1, const float* b1, const float* w2, float b2,
-                                 int B, int k, int H, int Hp, float gamma, float* a_hat, int32_t* k_hat,
-                                 void* workspace, size_t workspace_bytes, void* stream) {
+static int lh_forward(const void* hidden, const void* W1, const float* b1, const float* w2, float b2, int B, int k,
+                      int H, int Hp, float gamma, float* a_hat, int32_t* k_hat, float* z1_cache, void* workspace,
+                      size_t workspace_bytes, void* stream) {
   int rc = lh_checks(hidden, W1, b1, w2, b2, B, k, H, Hp, workspace, workspace_bytes);
   if (rc != ADAFLASH_OK) return rc;
   if (!(gamma > 0.f) || std::isinf(gamma)) return fail(ADAFLASH_E_INVALID, "gamma must be finite and > 0%s");
@@ -329,6 +329,7 @@ int adaflash_length_head_forward(const void* hidden, const void* W1, const float
   a.Hp = Hp;
   a.a_hat = a_hat;
   a.k_hat = k_hat;
+  a.z1_out = z1_cache;
   a.stream = (hipStream_t)stream;
   lh_workspace_layout(B, k, H, Hp, (char*)workspace, &a.ws);
   const hipError_t e = lh_launch(a);
@@ -337,10 +338,10 @@ int adaflash_length_head_forward(const void* hidden, const void* W1, const float
   return ADAFLASH_OK;
 }
 
-int adaflash_length_head_backward(const void* hidden, const void* W1, const float* b1, const float* w2, float b2,
-                                  int B, int k, int H, int Hp, const int32_t* accept_len,
-                                  const int32_t* verify_len, float* loss, float* dW1, float* db1, float* dw2,
-                                  float* db2, void* workspace, size_t workspace_bytes, void* stream) {
+static int lh_backward(const void* hidden, const void* W1, const float* b1, const float* w2, float b2, int B,
+                       int k, int H, int Hp, const int32_t* accept_len, const int32_t* verify_len, float* loss,
+                       float* dW1, float* db1, float* dw2, float* db2, const float* z1_cache, void* workspace,
+                       size_t workspace_bytes, void* stream) {
   int rc = lh_checks(hidden, W1, b1, w2, b2, B, k, H, Hp, workspace, workspace_bytes);
   if (rc != ADAFLASH_OK) return rc;
   if (!dW1 || !db1 || !dw2 || !db2) return fail(ADAFLASH_E_INVALID, "dW1, db1, dw2 and db2 must not be NULL%s");
@@ -364,12 +365,47 @@ int adaflash_length_head_backward(const void* hidden, const void* W1, const floa
   a.db1 = db1;
   a.dw2 = dw2;
   a.db2 = db2;
+  a.z1_in = z1_cache;
   a.stream = (hipStream_t)stream;
   lh_workspace_layout(B, k, H, Hp, (char*)workspace, &a.ws);
   const hipError_t e = lh_launch(a);
   if (e != hipSuccess) return fail(ADAFLASH_E_HIP, "HIP launch failed: %s", hipGetErrorString(e));
   g_err[0] = 0;
   return ADAFLASH_OK;
+}
+
+int adaflash_length_head_forward(const void* hidden, const void* W1, const float* b1, const float* w2, float b2,
+                                 int B, int k, int H, int Hp, float gamma, float* a_hat, int32_t* k_hat,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  return lh_forward(hidden, W1, b1, w2, b2, B, k, H, Hp, gamma, a_hat, k_hat, nullptr, workspace, workspace_bytes,
+                    stream);
+}
+
+int adaflash_length_head_forward_cached(const void* hidden, const void* W1, const float* b1, const float* w2,
+                                        float b2, int B, int k, int H, int Hp, float gamma, float* a_hat,
+                                        int32_t* k_hat, float* z1_cache, void* workspace, size_t workspace_bytes,
+                                        void* stream) {
+  if (B > 0 && !z1_cache) return fail(ADAFLASH_E_INVALID, "z1_cache must not be NULL%s");
+  return lh_forward(hidden, W1, b1, w2, b2, B, k, H, Hp, gamma, a_hat, k_hat, z1_cache, workspace,
+                    workspace_bytes, stream);
+}
+
+int adaflash_length_head_backward(const void* hidden, const void* W1, const float* b1, const float* w2, float b2,
+                                  int B, int k, int H, int Hp, const int32_t* accept_len,
+                                  const int32_t* verify_len, float* loss, float* dW1, float* db1, float* dw2,
+                                  float* db2, void* workspace, size_t workspace_bytes, void* stream) {
+  return lh_backward(hidden, W1, b1, w2, b2, B, k, H, Hp, accept_len, verify_len, loss, dW1, db1, dw2, db2, nullptr,
+                     workspace, workspace_bytes, stream);
+}
+
+int adaflash_length_head_backward_cached(const void* hidden, const void* W1, const float* b1, const float* w2,
+                                         float b2, int B, int k, int H, int Hp, const int32_t* accept_len,
+                                         const int32_t* verify_len, float* loss, float* dW1, float* db1,
+                                         float* dw2, float* db2, const float* z1_cache, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+  if (B > 0 && !z1_cache) return fail(ADAFLASH_E_INVALID, "z1_cache must not be NULL%s");
+  return lh_backward(hidden, W1, b1, w2, b2, B, k, H, Hp, accept_len, verify_len, loss, dW1, db1, dw2, db2,
+                     z1_cache, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -105,6 +105,8 @@ struct LhArgs {
   float* db1;          // [Hp]
   float* dw2;          // [Hp]
   float* db2;          // [1]
+  float* z1_out = nullptr;        // forward: [B*k, Hp] projection h W1^T kept for the backward
+  const float* z1_in = nullptr;   // backward: that projection, instead of recomputing it
   LhWorkspace ws;
   hipStream_t stream;
 };

@@ -68,8 +68,10 @@ __global__ __launch_bounds__(kLhThreads) void lh_gemm_tn(const uint16_t* __restr
   f32x16_t acc = {};
   const int wr = 32 * (wave >> 1), wc = 32 * (wave & 1);
   const int ko = 8 * (lane >> 5);
-  for (int k0 = kb; k0 < ke; k0 += kKs) {
-    u32x4_t ga[2], ga2[2], gb[2];
+  // The next round's operands are loaded into registers while the matrix
+  // cores work on the current one (the loads' latency is hidden).
+  u32x4_t ga[2], ga2[2], gb[2];
+  auto fetch = [&](int k0) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int r = lr + 32 * h;
@@ -80,6 +82,9 @@ __global__ __launch_bounds__(kLhThreads) void lh_gemm_tn(const uint16_t* __restr
       if constexpr (TWO_A) ga2[h] = (ra < M && okk) ? *(const u32x4_t*)(A2 + (size_t)ra * lda + kk) : zero;
       gb[h] = (rb < N && okk) ? *(const u32x4_t*)(Bm + (size_t)rb * ldb + kk) : zero;
     }
+  };
+  if (kb < ke) fetch(kb);
+  for (int k0 = kb; k0 < ke; k0 += kKs) {
     __syncthreads();  // the previous round's fragments are consumed
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -89,6 +94,7 @@ __global__ __launch_bounds__(kLhThreads) void lh_gemm_tn(const uint16_t* __restr
       *(u32x4_t*)&sb[r * kLdsRow + lc] = gb[h];
     }
     __syncthreads();
+    if (k0 + kKs < ke) fetch(k0 + kKs);
 #pragma unroll
     for (int t = 0; t < kKs / 16; ++t) {
       const int kc = 16 * t + ko;
@@ -113,30 +119,68 @@ __global__ __launch_bounds__(kLhThreads) void lh_gemm_tn(const uint16_t* __restr
   }
 }
 
-// out[i] = sum over the S slices of part[s][i], in slice order.
+// out[i] = sum over the S slices of part[s][i], in slice order.  VEC: four
+// consecutive entries per thread with 16-byte loads and stores (n a multiple
+// of 4, out 16-byte aligned).
+template <bool VEC>
 __global__ __launch_bounds__(kLhThreads) void lh_sum_slices(const float* __restrict__ part, int S, size_t n,
                                                              float* __restrict__ out) {
-  for (size_t i = (size_t)blockIdx.x * kLhThreads + threadIdx.x; i < n; i += (size_t)gridDim.x * kLhThreads) {
-    float a = 0.f;
-    for (int z = 0; z < S; ++z) a += part[(size_t)z * n + i];
-    out[i] = a;
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  if constexpr (VEC) {
+    const size_t n4 = n / 4;
+    for (size_t i = (size_t)blockIdx.x * kLhThreads + threadIdx.x; i < n4; i += (size_t)gridDim.x * kLhThreads) {
+      f32x4_t a = {0.f, 0.f, 0.f, 0.f};
+      for (int z = 0; z < S; ++z) a += *(const f32x4_t*)(part + (size_t)z * n + 4 * i);
+      *(f32x4_t*)(out + 4 * i) = a;
+    }
+  } else {
+    for (size_t i = (size_t)blockIdx.x * kLhThreads + threadIdx.x; i < n; i += (size_t)gridDim.x * kLhThreads) {
+      float a = 0.f;
+      for (int z = 0; z < S; ++z) a += part[(size_t)z * n + i];
+      out[i] = a;
+    }
   }
 }
 
+hipError_t sum_slices(const float* part, int S, size_t n, float* out, hipStream_t st) {
+  const bool vec = n % 4 == 0 && ((uintptr_t)out & 15) == 0;
+  const size_t units = vec ? n / 4 : n;
+  const int blocks = (int)((units + kLhThreads - 1) / kLhThreads < 2048 ? (units + kLhThreads - 1) / kLhThreads : 2048);
+  if (blocks == 0) return hipSuccess;
+  if (vec) hipLaunchKernelGGL((lh_sum_slices<true>), dim3(blocks), dim3(kLhThreads), 0, st, part, S, n, out);
+  else hipLaunchKernelGGL((lh_sum_slices<false>), dim3(blocks), dim3(kLhThreads), 0, st, part, S, n, out);
+  return hipGetLastError();
+}
+
 // hT [H x Mp] = h^T (bf16), zero for m >= M, through a 64 x 64 LDS tile.
+// Rows of h are read and rows of hT written 16 bytes (eight entries) per
+// thread; H is a multiple of 8 and Mp of 16, h 16-byte aligned.  The LDS
+// rows are 66 entries long (33 words), so that the column reads of eight
+// rows eight apart fall in different banks.
 __global__ __launch_bounds__(kLhThreads) void lh_transpose(const uint16_t* __restrict__ h, int M, int H, int Mp,
                                                             uint16_t* __restrict__ hT) {
-  __shared__ uint16_t t[kTile][kTile + 2];
+  __shared__ __attribute__((aligned(16))) uint16_t t[kTile][kTile + 2];
   const int m0 = blockIdx.x * kTile, c0 = blockIdx.y * kTile;
-  const int tc = threadIdx.x & 63, tr = threadIdx.x >> 6;
-  for (int rr = tr; rr < kTile; rr += 4) {
-    const int m = m0 + rr, c = c0 + tc;
-    t[rr][tc] = (m < M && c < H) ? h[(size_t)m * H + c] : (uint16_t)0;
+  const int r8 = threadIdx.x >> 3, e8 = (threadIdx.x & 7) * 8;
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int r = r8 + 32 * hh, m = m0 + r, c = c0 + e8;
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (m < M && c < H) v = *(const u32x4_t*)(h + (size_t)m * H + c);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) *(uint32_t*)&t[r][e8 + 2 * w] = v[w];
   }
   __syncthreads();
-  for (int cc = tr; cc < kTile; cc += 4) {
-    const int c = c0 + cc, m = m0 + tc;
-    if (c < H && m < Mp) hT[(size_t)c * Mp + m] = t[tc][cc];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int cc = r8 + 32 * hh, c = c0 + cc, m = m0 + e8;
+    if (c < H && m < Mp) {
+      u32x4_t v;
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        v[w] = (uint32_t)t[e8 + 2 * w][cc] | ((uint32_t)t[e8 + 2 * w + 1][cc] << 16);
+      *(u32x4_t*)(hT + (size_t)c * Mp + m) = v;
+    }
   }
 }
 
@@ -212,6 +256,7 @@ __global__ __launch_bounds__(kLhThreads) void lh_dz(const float* __restrict__ Z1
   const int n = n0 + tc;
   const float invk = 1.f / (float)k;
   float colsum = 0.f;
+#pragma unroll
   for (int rr = tr; rr < kTile; rr += 4) {
     const int m = m0 + rr;
     float v = 0.f;
@@ -230,6 +275,7 @@ __global__ __launch_bounds__(kLhThreads) void lh_dz(const float* __restrict__ Z1
   __syncthreads();
   if (tr == 0 && n < Hp) db1_part[(size_t)blockIdx.x * Hp + n] = (cs[0][tc] + cs[1][tc]) + (cs[2][tc] + cs[3][tc]);
   // Transposed write: row n of dZ1^T, 64 consecutive m.
+#pragma unroll
   for (int cc = tr; cc < kTile; cc += 4) {
     const int nn = n0 + cc, m = m0 + tc;
     if (nn < Hp && m < Mp) {
@@ -242,27 +288,38 @@ __global__ __launch_bounds__(kLhThreads) void lh_dz(const float* __restrict__ Z1
   }
 }
 
-// db1 = sum of the tile partials, dw2 = sum_b ds[b] hbar[b], db2 = sum_b ds[b]
-// (all in a fixed order), one workgroup.
+// db1 = sum of the tile partials, dw2 = sum_b ds[b] hbar[b], db2 = sum_b
+// ds[b], all in a fixed order.  Workgroup x takes 64 columns; wave w sums the
+// tiles and requests congruent to w mod 4, and the four partials are added
+// in wave order.  Workgroup 0 also forms db2.
 __global__ __launch_bounds__(kLhThreads) void lh_small_grads(const float* __restrict__ db1_part, int ntiles, int Hp,
                                                               int B, const float* __restrict__ ds,
                                                               const float* __restrict__ hbar, float* __restrict__ db1,
                                                               float* __restrict__ dw2, float* __restrict__ db2) {
   __shared__ float red[4];
-  for (int n = threadIdx.x; n < Hp; n += kLhThreads) {
-    float a = 0.f;
-#pragma unroll 8
-    for (int t = 0; t < ntiles; ++t) a += db1_part[(size_t)t * Hp + n];
-    db1[n] = a;
-    float w = 0.f;
-#pragma unroll 8
-    for (int b = 0; b < B; ++b) w = fmaf(ds[b], hbar[(size_t)b * Hp + n], w);
-    dw2[n] = w;
+  __shared__ float pa[4][64], pw[4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = blockIdx.x * 64 + lane;
+  float a = 0.f, w = 0.f;
+  if (n < Hp) {
+#pragma unroll 4
+    for (int t = wave; t < ntiles; t += 4) a += db1_part[(size_t)t * Hp + n];
+#pragma unroll 4
+    for (int b = wave; b < B; b += 4) w = fmaf(ds[b], hbar[(size_t)b * Hp + n], w);
   }
-  float part = 0.f;
-  for (int b = threadIdx.x; b < B; b += kLhThreads) part += ds[b];
-  const float tot = lh_block_sum(part, red);
-  if (threadIdx.x == 0) *db2 = tot;
+  pa[wave][lane] = a;
+  pw[wave][lane] = w;
+  __syncthreads();
+  if (wave == 0 && n < Hp) {
+    db1[n] = (pa[0][lane] + pa[1][lane]) + (pa[2][lane] + pa[3][lane]);
+    dw2[n] = (pw[0][lane] + pw[1][lane]) + (pw[2][lane] + pw[3][lane]);
+  }
+  if (blockIdx.x == 0) {
+    float part = 0.f;
+    for (int b = threadIdx.x; b < B; b += kLhThreads) part += ds[b];
+    const float tot = lh_block_sum(part, red);
+    if (threadIdx.x == 0) *db2 = tot;
+  }
 }
 
 // Split of a reduction of length K for a product with `tiles` output tiles:
@@ -326,28 +383,32 @@ hipError_t lh_launch(const LhArgs& a) {
   const int mt = (M + kTile - 1) / kTile, nt = (a.Hp + kTile - 1) / kTile;
   const Split sf = split_k(a.H, (long long)mt * nt);
   const bool bwd = a.accept_len != nullptr;
-  hipLaunchKernelGGL((lh_gemm_tn<false>), dim3(mt, nt, sf.S), dim3(kLhThreads), 0, a.stream, a.h,
-                     (const uint16_t*)nullptr, a.H, a.W1, a.H, a.ws.z1, M, a.Hp, a.H, sf.kslice);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  // The split-K slices summed in slice order (the pooling kernel then reads
-  // one value per entry).
-  const size_t nz = (size_t)M * a.Hp;
-  const int zblocks = (int)((nz + kLhThreads - 1) / kLhThreads < 2048 ? (nz + kLhThreads - 1) / kLhThreads : 2048);
-  hipLaunchKernelGGL(lh_sum_slices, dim3(zblocks), dim3(kLhThreads), 0, a.stream, a.ws.z1, sf.S, nz, a.ws.zsum);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(lh_pool, dim3(a.B), dim3(kLhThreads), 0, a.stream, a.ws.zsum, a.Hp, a.k,
+  hipError_t e = hipSuccess;
+  // The projection Z1 = h W1^T: from the caller's copy of the forward's, or
+  // computed (split-K slices summed in slice order, so that the pooling
+  // kernel reads one value per entry).
+  const float* z1 = a.z1_in;
+  if (!z1) {
+    float* zdst = a.z1_out ? a.z1_out : a.ws.zsum;
+    hipLaunchKernelGGL((lh_gemm_tn<false>), dim3(mt, nt, sf.S), dim3(kLhThreads), 0, a.stream, a.h,
+                       (const uint16_t*)nullptr, a.H, a.W1, a.H, a.ws.z1, M, a.Hp, a.H, sf.kslice);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = sum_slices(a.ws.z1, sf.S, (size_t)M * a.Hp, zdst, a.stream);
+    if (e != hipSuccess) return e;
+    z1 = zdst;
+  }
+  hipLaunchKernelGGL(lh_pool, dim3(a.B), dim3(kLhThreads), 0, a.stream, z1, a.Hp, a.k,
                      a.b1, a.w2, a.b2, a.gamma, a.a_hat, a.k_hat, a.accept_len, a.verify_len, a.loss,
                      bwd ? a.ws.hbar : nullptr, a.ws.ds);
   e = hipGetLastError();
   if (e != hipSuccess || !bwd) return e;
   const int ntiles = (M + kTile - 1) / kTile;
-  hipLaunchKernelGGL(lh_dz, dim3((Mp + kTile - 1) / kTile, nt), dim3(kLhThreads), 0, a.stream, a.ws.zsum, M, a.Hp,
+  hipLaunchKernelGGL(lh_dz, dim3((Mp + kTile - 1) / kTile, nt), dim3(kLhThreads), 0, a.stream, z1, M, a.Hp,
                      a.k, Mp, a.b1, a.w2, a.ws.ds, a.ws.dzh, a.ws.dzl, a.ws.db1_part);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(lh_small_grads, dim3(1), dim3(kLhThreads), 0, a.stream, a.ws.db1_part, ntiles, a.Hp, a.B,
+  hipLaunchKernelGGL(lh_small_grads, dim3((a.Hp + 63) / 64), dim3(kLhThreads), 0, a.stream, a.ws.db1_part, ntiles, a.Hp, a.B,
                      a.ws.ds, a.ws.hbar, a.db1, a.dw2, a.db2);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -362,10 +423,7 @@ hipError_t lh_launch(const LhArgs& a) {
                      a.ws.hT, Mp, a.ws.dw_part, a.Hp, a.H, Mp, sb.kslice);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t n = (size_t)a.Hp * a.H;
-  const int blocks = (int)((n + kLhThreads - 1) / kLhThreads < 2048 ? (n + kLhThreads - 1) / kLhThreads : 2048);
-  hipLaunchKernelGGL(lh_sum_slices, dim3(blocks), dim3(kLhThreads), 0, a.stream, a.ws.dw_part, sb.S, n, a.dW1);
-  return hipGetLastError();
+  return sum_slices(a.ws.dw_part, sb.S, (size_t)a.Hp * a.H, a.dW1, a.stream);
 }
 
 }  // namespace adaflash

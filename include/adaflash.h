@@ -309,6 +309,31 @@ ADAFLASH_API int adaflash_length_head_backward(const void* hidden, const void* W
                                   size_t workspace_bytes, void* stream);
 
 /*
+ * The same two calls with the projection kept between them.  In a serving
+ * round the forward runs before verification and the backward after it, on
+ * the same hidden states and weights; the backward then needs the forward's
+ * projection again.
+ *   z1_cache [B k, H'] fp32   forward: out, the projection h W1^T (before
+ *                             the bias); backward: in, that same array
+ *                             (not recomputed).  Caller-owned device memory;
+ *                             must not be NULL when B > 0.  The backward's
+ *                             results equal those of
+ *                             adaflash_length_head_backward only if z1_cache
+ *                             holds the forward's output for the same hidden
+ *                             states and W1.
+ * Every other argument is as in the plain forms above.
+ */
+ADAFLASH_API int adaflash_length_head_forward_cached(const void* hidden, const void* W1, const float* b1,
+                                 const float* w2, float b2, int B, int k, int H, int Hp, float gamma,
+                                 float* a_hat, int32_t* k_hat, float* z1_cache, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+ADAFLASH_API int adaflash_length_head_backward_cached(const void* hidden, const void* W1, const float* b1,
+                                  const float* w2, float b2, int B, int k, int H, int Hp,
+                                  const int32_t* accept_len, const int32_t* verify_len, float* loss,
+                                  float* dW1, float* db1, float* dw2, float* db2, const float* z1_cache,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Verification-batch admission controller (host only; no GPU call).
  * AdaFlash review (ZH), section 2.3, and AdaFlash review (EN), "Adaptive
  * request scheduling for variable verification lengths": with per-request

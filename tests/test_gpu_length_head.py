@@ -94,3 +94,32 @@ def test_length_head_empty_batch():
     out = ada.length_head_forward(h, W1, b1, b1, 0.0)
     torch.cuda.synchronize()
     assert out["a_hat"].numel() == 0 and out["k_hat"].numel() == 0
+
+
+@pytest.mark.parametrize("B", [128, 7])
+def test_cached_projection_equals_recomputed(B):
+    """The forward's kept projection fed to the backward gives the same
+    outputs, bit for bit, as the backward that recomputes it; the forward's
+    own outputs do not change either; and the kept projection matches the
+    oracle's h W1^T."""
+    import torch
+    import diffusion_drafter_verification_amd as ada
+    lb = W.length_head_inputs(B)
+    h = _dev(lb.hidden.view(np.int16), torch.bfloat16)
+    W1 = _dev(lb.W1.view(np.int16), torch.bfloat16)
+    b1, w2 = _dev(lb.b1), _dev(lb.w2)
+    A, L = _dev(lb.accept_len), _dev(lb.verify_len)
+    f0 = ada.length_head_forward(h, W1, b1, w2, lb.b2, 1.0)
+    f1 = ada.length_head_forward(h, W1, b1, w2, lb.b2, 1.0, keep_projection=True)
+    g0 = ada.length_head_backward(h, W1, b1, w2, lb.b2, A, L)
+    g1 = ada.length_head_backward(h, W1, b1, w2, lb.b2, A, L, z1=f1["z1"])
+    torch.cuda.synchronize()
+    for key in ("a_hat", "k_hat"):
+        assert torch.equal(f0[key], f1[key]), key
+    for key in ("loss", "dW1", "db1", "dw2", "db2"):
+        assert torch.equal(g0[key], g1[key]), key
+    hh = LH.bf16_to_f64(lb.hidden).reshape(B * lb.hidden.shape[1], -1)
+    ref = hh @ LH.bf16_to_f64(lb.W1).T
+    z = f1["z1"].double().cpu().numpy()
+    scale = np.abs(hh) @ np.abs(LH.bf16_to_f64(lb.W1)).T
+    assert np.all(np.abs(z - ref) <= 1e-4 * scale + 1e-9)
