@@ -82,7 +82,7 @@ struct LhWorkspace {
   float* ds;         // [B] d loss / d logit (backward)
   uint16_t* dzh;     // [Hp, Mp] dZ1^T, bf16 high part (backward)
   uint16_t* dzl;     // [Hp, Mp] dZ1^T, bf16 remainder (backward)
-  float* db1_part;   // [ceil(B*k/64), Hp] per-tile sums for db1 (backward)
+  float* db1_part;   // [B, Hp] per-request column sums of dZ1 (for db1)
   uint16_t* hT;      // [H, Mp] transposed hidden states (backward)
   float* dw_part;    // [S, Hp, H] split-K partial sums of dW1 (backward)
 };

@@ -197,14 +197,21 @@ __device__ float lh_block_sum(float v, float* red) {
 
 // One workgroup per request: bias, SiLU, mean over the k positions, second
 // layer, sigmoid, verify length; with accept_len given also the label, the
-// loss and d loss / d s, and the pooled vector kept for the weight gradient.
+// loss and d loss / d s, the pooled vector kept for the weight gradient, and
+// this request's rows of dZ1 = ds w2 / k SiLU'(z1), written transposed
+// (dZ1^T, [H' x Mp]) as a bf16 high part and remainder, with its column sums
+// for db1 ([B][H']).  The workgroup of the last request also zeroes the
+// padding columns m in [M, Mp).
 __global__ __launch_bounds__(kLhThreads) void lh_pool(const float* __restrict__ Z1, int Hp, int k,
                                                        const float* __restrict__ b1, const float* __restrict__ w2,
                                                        float b2, float gamma, float* __restrict__ a_hat,
                                                        int32_t* __restrict__ k_hat, const int32_t* __restrict__ accept_len,
                                                        const int32_t* __restrict__ verify_len, float* __restrict__ loss,
-                                                       float* __restrict__ hbar, float* __restrict__ ds) {
+                                                       float* __restrict__ hbar, float* __restrict__ ds, int M, int Mp,
+                                                       uint16_t* __restrict__ dzh, uint16_t* __restrict__ dzl,
+                                                       float* __restrict__ db1_part) {
   __shared__ float red[4];
+  __shared__ float sh_ds;
   const int b = blockIdx.x;
   const float invk = 1.f / (float)k;
   float part = 0.f;
@@ -238,60 +245,67 @@ __global__ __launch_bounds__(kLhThreads) void lh_pool(const float* __restrict__ 
       const float d = a - astar;
       loss[b] = d * d;
       ds[b] = 2.f * d * a * (1.f - a);
+      sh_ds = ds[b];
     }
+  }
+  if (!accept_len) return;
+  __syncthreads();
+  const float dsb = sh_ds;
+  const size_t m0 = (size_t)b * k;
+  // 16-byte stores of a row segment when it is aligned (k a multiple of 8).
+  const bool vec = (k & 7) == 0;
+  for (int n = threadIdx.x; n < Hp; n += kLhThreads) {
+    const float bias = b1[n];
+    const float wv = dsb * w2[n] * invk;
+    float colsum = 0.f;
+    uint16_t* rh = dzh + (size_t)n * Mp + m0;
+    uint16_t* rl = dzl + (size_t)n * Mp + m0;
+    for (int i0 = 0; i0 < k; i0 += 8) {
+      uint32_t ph[4], pl[4];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u;
+        float v = 0.f;
+        if (i < k) {
+          const float z = Z1[(m0 + i) * Hp + n] + bias;
+          const float sg = sigmoidf_(z);
+          v = wv * (sg * (1.f + z * (1.f - sg)));
+        }
+        colsum += v;
+        const __bf16 hi = (__bf16)v;
+        const __bf16 lo = (__bf16)(v - (float)hi);
+        const uint32_t hb = __builtin_bit_cast(uint16_t, hi), lb = __builtin_bit_cast(uint16_t, lo);
+        if (u & 1) {
+          ph[u >> 1] |= hb << 16;
+          pl[u >> 1] |= lb << 16;
+        } else {
+          ph[u >> 1] = hb;
+          pl[u >> 1] = lb;
+        }
+        if (!vec && i < k) {
+          rh[i] = (uint16_t)hb;
+          rl[i] = (uint16_t)lb;
+        }
+      }
+      if (vec) {
+        const u32x4_t vh = {ph[0], ph[1], ph[2], ph[3]}, vl = {pl[0], pl[1], pl[2], pl[3]};
+        *(u32x4_t*)(rh + i0) = vh;
+        *(u32x4_t*)(rl + i0) = vl;
+      }
+    }
+    db1_part[(size_t)b * Hp + n] = colsum;
+    if (b == (int)gridDim.x - 1)
+      for (int m = M; m < Mp; ++m) {
+        dzh[(size_t)n * Mp + m] = 0;
+        dzl[(size_t)n * Mp + m] = 0;
+      }
   }
 }
 
-// dZ1 = ds[b] w2[n] / k * SiLU'(z1) for a 64 x 64 tile of (row m, column n),
-// transposed through LDS and written as dZ1^T split into a bf16 high part and
-// a bf16 remainder ([H' x Mp], Mp = M rounded up to 16, zero past M).  Each
-// tile also writes its partial column sums for db1 ([ceil(M/64)][H']).
-__global__ __launch_bounds__(kLhThreads) void lh_dz(const float* __restrict__ Z1, int M, int Hp, int k, int Mp,
-                                                     const float* __restrict__ b1, const float* __restrict__ w2,
-                                                     const float* __restrict__ ds, uint16_t* __restrict__ dzh,
-                                                     uint16_t* __restrict__ dzl, float* __restrict__ db1_part) {
-  __shared__ float t[kTile][kTile + 1];
-  const int m0 = blockIdx.x * kTile, n0 = blockIdx.y * kTile;  // row tiles along x
-  const int tc = threadIdx.x & 63, tr = threadIdx.x >> 6;
-  const int n = n0 + tc;
-  const float invk = 1.f / (float)k;
-  float colsum = 0.f;
-#pragma unroll
-  for (int rr = tr; rr < kTile; rr += 4) {
-    const int m = m0 + rr;
-    float v = 0.f;
-    if (m < M && n < Hp) {
-      const float z = Z1[(size_t)m * Hp + n] + b1[n];
-      const float sg = sigmoidf_(z);
-      v = ds[m / k] * w2[n] * invk * (sg * (1.f + z * (1.f - sg)));
-    }
-    t[rr][tc] = v;
-    colsum += v;
-  }
-  __syncthreads();
-  // Partial db1: the four row groups' sums, added in a fixed order.
-  __shared__ float cs[4][kTile];
-  cs[tr][tc] = colsum;
-  __syncthreads();
-  if (tr == 0 && n < Hp) db1_part[(size_t)blockIdx.x * Hp + n] = (cs[0][tc] + cs[1][tc]) + (cs[2][tc] + cs[3][tc]);
-  // Transposed write: row n of dZ1^T, 64 consecutive m.
-#pragma unroll
-  for (int cc = tr; cc < kTile; cc += 4) {
-    const int nn = n0 + cc, m = m0 + tc;
-    if (nn < Hp && m < Mp) {
-      const float v = t[tc][cc];
-      const __bf16 hi = (__bf16)v;
-      const __bf16 lo = (__bf16)(v - (float)hi);
-      dzh[(size_t)nn * Mp + m] = __builtin_bit_cast(uint16_t, hi);
-      dzl[(size_t)nn * Mp + m] = __builtin_bit_cast(uint16_t, lo);
-    }
-  }
-}
-
-// db1 = sum of the tile partials, dw2 = sum_b ds[b] hbar[b], db2 = sum_b
-// ds[b], all in a fixed order.  Workgroup x takes 64 columns; wave w sums the
-// tiles and requests congruent to w mod 4, and the four partials are added
-// in wave order.  Workgroup 0 also forms db2.
+// db1 = sum of the per-request partials, dw2 = sum_b ds[b] hbar[b], db2 =
+// sum_b ds[b], all in a fixed order.  Workgroup x takes 64 columns; wave w
+// sums the partials and requests congruent to w mod 4, and the four partials
+// are added in wave order.  Workgroup 0 also forms db2.
 __global__ __launch_bounds__(kLhThreads) void lh_small_grads(const float* __restrict__ db1_part, int ntiles, int Hp,
                                                               int B, const float* __restrict__ ds,
                                                               const float* __restrict__ hbar, float* __restrict__ db1,
@@ -359,7 +373,7 @@ size_t lh_workspace_layout(int B, int k, int H, int Hp, char* base, LhWorkspace*
   char* ds = take(sizeof(float) * (size_t)B);
   char* dzh = take(sizeof(uint16_t) * Mp * Hp);
   char* dzl = take(sizeof(uint16_t) * Mp * Hp);
-  char* part = take(sizeof(float) * ntiles * Hp);
+  char* part = take(sizeof(float) * (size_t)B * Hp);
   char* hT = take(sizeof(uint16_t) * (size_t)H * Mp);
   char* dwp = take(sizeof(float) * sb.S * (size_t)Hp * H);
   if (ws) {
@@ -400,15 +414,10 @@ hipError_t lh_launch(const LhArgs& a) {
   }
   hipLaunchKernelGGL(lh_pool, dim3(a.B), dim3(kLhThreads), 0, a.stream, z1, a.Hp, a.k,
                      a.b1, a.w2, a.b2, a.gamma, a.a_hat, a.k_hat, a.accept_len, a.verify_len, a.loss,
-                     bwd ? a.ws.hbar : nullptr, a.ws.ds);
+                     bwd ? a.ws.hbar : nullptr, a.ws.ds, M, Mp, a.ws.dzh, a.ws.dzl, a.ws.db1_part);
   e = hipGetLastError();
   if (e != hipSuccess || !bwd) return e;
-  const int ntiles = (M + kTile - 1) / kTile;
-  hipLaunchKernelGGL(lh_dz, dim3((Mp + kTile - 1) / kTile, nt), dim3(kLhThreads), 0, a.stream, z1, M, a.Hp,
-                     a.k, Mp, a.b1, a.w2, a.ws.ds, a.ws.dzh, a.ws.dzl, a.ws.db1_part);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(lh_small_grads, dim3((a.Hp + 63) / 64), dim3(kLhThreads), 0, a.stream, a.ws.db1_part, ntiles, a.Hp, a.B,
+  hipLaunchKernelGGL(lh_small_grads, dim3((a.Hp + 63) / 64), dim3(kLhThreads), 0, a.stream, a.ws.db1_part, a.B, a.Hp, a.B,
                      a.ws.ds, a.ws.hbar, a.db1, a.dw2, a.db2);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
