@@ -41,7 +41,8 @@ def parse():
     ap.add_argument("--sets", type=int, default=2, help="input sets rotated between calls")
     ap.add_argument("--clip", type=float, default=10.0)
     ap.add_argument("--lam", type=float, default=1.0)
-    ap.add_argument("--mode", choices=["fused", "verify", "opd", "lengthhead", "admission"], default="fused")
+    ap.add_argument("--mode", choices=["fused", "verify", "greedy", "opd", "lengthhead", "admission"],
+                    default="fused")
     ap.add_argument("--variant", choices=["rkl", "rkl_clip", "mixture", "fkl", "wce"], default=None,
                     help="with --mode opd: a supervision loss variant (pages' defaults: delta 0.01, "
                          "alpha 0.8, position decay 7)")
@@ -67,7 +68,8 @@ def algorithmic_bytes(verify_len, accept_len, B, k, V, mode):
     if mode == "opd":
         return N * 3 * V * e + 8 * N + 4 * B
     bonus = int((accept_len == L).sum())
-    rd = 2 * N * V * e + bonus * V * e
+    # (greedy verification reads only the target rows)
+    rd = (1 if mode == "greedy" else 2) * N * V * e + bonus * V * e
     small = B * (4 * k + 4 * (k + 1) + 4) + B * (4 + 4 * (k + 1)) + B * 4 * (k + 1)
     total = rd + small
     if mode == "fused":
@@ -119,9 +121,11 @@ def cpu_baseline(batch, mode, clip, lam, budget_s):
     done = 0
     t0 = time.perf_counter()
     while True:
-        if mode != "opd":
+        if mode == "greedy":
+            oracle.verify(t, None, tok, vl, uni, T=0.0, nthreads=threads)
+        elif mode != "opd":
             oracle.verify(t, d, tok, vl, uni, T=1.0, nthreads=threads)
-        if mode != "verify":
+        if mode not in ("verify", "greedy"):
             oracle.opd(t, d, vl, clip, lam, with_grad=True, nthreads=threads)
         done += 1
         el = time.perf_counter() - t0
@@ -304,7 +308,8 @@ def main():
 
     sets = []
     for s in range(args.sets):
-        bt = W.generate(wl, round=s)
+        # (greedy verification: the drafts are the drafter's argmax tokens)
+        bt = W.generate(wl, round=s, T=0.0) if args.mode == "greedy" else W.generate(wl, round=s)
         sets.append(bt)
     dsets = []
     for bt in sets:
@@ -347,7 +352,8 @@ def main():
         else:
             fused = args.mode == "fused"
             fn = ada.adaflash_verify_packed if packed else ada.adaflash_verify
-            fn(ds["t"], ds["d"], ds["tok"], ds["vl"], ds["u"], 1.0, acc, outt, mg, args.clip,
+            fn(ds["t"], ds["d"], ds["tok"], ds["vl"], ds["u"], 0.0 if args.mode == "greedy" else 1.0, acc, outt, mg,
+               args.clip,
                args.lam, ro, ce if fused else None, rk if fused else None,
                grad if fused else None, status, ws, stream)
 
@@ -411,8 +417,9 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": ("%s fused verify+supervision: B=%d, k=%d, V=%d, bf16 logits, "
-                         "verify_len%s, sigma_b~U{0.3,1,2}, T=1, c=%g, lambda=%g, mode=%s%s, layout=%s"
+                         "verify_len%s, sigma_b~U{0.3,1,2}, T=%d, c=%g, lambda=%g, mode=%s%s, layout=%s"
                          % (args.workload, B, k, V, ("~U{1..%d}" % k) if wl.ragged else ("=%d" % k),
+                            0 if args.mode == "greedy" else 1,
                             args.clip, args.lam, args.mode,
                             (", variant=%s" % args.variant) if args.variant else "", args.layout)),
             "B": B, "k": k, "V": V, "input_sets": args.sets,
@@ -425,7 +432,8 @@ def main():
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": measured_traffic(args.mode, args.workload == "c128" and not packed),
         },
-        "dominant_kernel": {"fused": "sup_kernel", "opd": "sup_kernel", "verify": "vstat_kernel"}[args.mode],
+        "dominant_kernel": {"fused": "sup_kernel", "opd": "sup_kernel", "verify": "vstat_kernel",
+                            "greedy": "gstat_kernel"}[args.mode],
         "dominant_kernel_us_avg": kavg * 1e6,
         "kernel_ms_avg": avg_dur * 1e3,
         "kernel_ms_p10_p50_p90": [float(np.percentile(durs, q) * 1e3) for q in (10, 50, 90)],

@@ -1741,6 +1741,71 @@ __global__ __launch_bounds__(kThreads, (sup_min_waves<BF16, ALIGNED, VMODE, FKL>
   }
 }
 
+// ------------------------------------------ greedy verification (no OPD)
+
+// Greedy verification needs only every target row's maximum and its lowest
+// index.  One workgroup takes chunk j of kGRows consecutive rows of a request
+// (all their loads in flight together) and publishes one (max, argmax)
+// record per row, with two workgroup reductions for all its rows.  Rows
+// beyond the request's bonus row are skipped.
+constexpr int kGRows = 4;
+
+template <bool BF16, bool ALIGNED>
+__global__ __launch_bounds__(kThreads) void gstat_kernel(KParams P) {
+  __shared__ float red[kWaves * 2 * kGRows];
+  const int tid = threadIdx.x;
+  const int G = P.G, k = P.k, V = P.V;
+  const int NG = (k + kGRows) / kGRows;  // row groups per request (k + 1 rows)
+  const int q = (int)blockIdx.x / G;
+  const int j = (int)blockIdx.x - q * G;
+  const int b = q / NG, g = q - b * NG;
+  const int L = P.Lc[b];
+  if (L < 0) return;
+  const int i0 = g * kGRows;
+  if (i0 > L) return;
+  const int nr = min(kGRows, L + 1 - i0);  // rows i0 .. i0 + nr - 1 (uniform)
+  const int v0 = j * kChunk;
+  Chunk<BF16> c[kGRows];
+#pragma unroll
+  for (int t = 0; t < kGRows; ++t)
+    if (t < nr) load_chunk<BF16, ALIGNED>(c[t], target_row_ptr<BF16>(P, b, i0 + t), v0, V);
+  float m[kGRows];
+  int ops[kGRows];
+#pragma unroll
+  for (int t = 0; t < kGRows; ++t) {
+    m[t] = t < nr ? chunk_max<BF16>(c[t]) : neg_inf();
+    ops[t] = OP_MAX;
+  }
+  float M[kGRows];
+#pragma unroll
+  for (int t = 0; t < kGRows; ++t) M[t] = m[t];
+  wg_reduce<kGRows>(M, ops, red);
+  // Lowest index holding each row's chunk maximum (only lanes that hold it search).
+  float cand[kGRows];
+#pragma unroll
+  for (int t = 0; t < kGRows; ++t) {
+    int ci = kIntMax;
+    if (t < nr && m[t] == M[t]) {
+#pragma unroll
+      for (int e = kElems - 1; e >= 0; --e)
+        if (c[t].get(e) == M[t]) ci = entry_index<BF16>(v0, e);
+      if (ci >= V) ci = kIntMax;  // padding (a row of -inf only)
+    }
+    cand[t] = __int_as_float(ci);
+    ops[t] = OP_MINI;
+  }
+  wg_reduce_lead<kGRows>(cand, ops, red + kWaves * kGRows);
+  if (tid == 0) {
+#pragma unroll
+    for (int t = 0; t < kGRows; ++t) {
+      if (t >= nr) break;
+      float* rec = P.part1 + ((size_t)(b * (k + 1) + i0 + t) * G + j) * kRec1;
+      pub_store(rec + 0, M[t]);
+      pub_store(rec + 1, cand[t]);
+    }
+  }
+}
+
 // -------------------------------------------- sampled verification (no OPD)
 
 // Sampled verification without supervision needs the row statistics in one
@@ -2069,7 +2134,11 @@ hipError_t dispatch_mode(const KParams& p, int grid, int opd, int vmode, bool t1
   else if (opd && vmode == 1) e = launch_sup<BF16, ALIGNED, 1>(p, grid, st);
   else if (opd && vmode == 2 && t1) e = launch_sup<BF16, ALIGNED, 2>(p, grid, st);
   else if (opd) e = launch_rows<BF16, ALIGNED, true, 2, false>(p, grid, st);
-  else if (vmode == 1) e = launch_rows<BF16, ALIGNED, false, 1, false>(p, grid, st);
+  else if (vmode == 1) {
+    const int ng = (p.k + kGRows) / kGRows;
+    hipLaunchKernelGGL((gstat_kernel<BF16, ALIGNED>), dim3(p.B * ng * p.G), dim3(kThreads), 0, st, p);
+    e = hipGetLastError();
+  }
   else if (vmode == 2) {
     hipLaunchKernelGGL((vstat_kernel<BF16, ALIGNED>), dim3(grid), dim3(kThreads), 0, st, p);
     e = hipGetLastError();
