@@ -48,8 +48,9 @@ def parse():
                          "alpha 0.8, position decay 7)")
     ap.add_argument("--layout", choices=["padded", "packed"], default="padded",
                     help="logits layout: padded [B, k+1, V] or packed [sum(L_b+1), V]")
-    ap.add_argument("--workload", choices=["c128", "c32", "single"], default="c128",
-                    help="batch shape (default: the headline B=128 configuration)")
+    ap.add_argument("--workload", choices=["c128", "c32", "single", "replay"], default="c128",
+                    help="batch shape (default: the headline B=128 configuration; replay: 512 x 16 rows, "
+                         "supervision only)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-probe", action="store_true",
@@ -114,26 +115,37 @@ def cpu_baseline(batch, mode, clip, lam, budget_s):
     nreq = 8
     t = batch.target[:nreq]
     d = batch.draft[:nreq]
-    tok = batch.tokens[:nreq]
+    tok = batch.tokens[:nreq] if batch.tokens is not None else None
     vl = batch.verify_len[:nreq]
     uni = batch.uniforms[:nreq]
     positions = int(np.clip(vl, 1, t.shape[1] - 1).sum())
-    done = 0
-    t0 = time.perf_counter()
-    while True:
-        if mode == "greedy":
-            oracle.verify(t, None, tok, vl, uni, T=0.0, nthreads=threads)
-        elif mode != "opd":
-            oracle.verify(t, d, tok, vl, uni, T=1.0, nthreads=threads)
-        if mode not in ("verify", "greedy"):
-            oracle.opd(t, d, vl, clip, lam, with_grad=True, nthreads=threads)
-        done += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
+    def run(nthreads, budget):
+        done = 0
+        t0 = time.perf_counter()
+        while True:
+            if mode == "greedy":
+                oracle.verify(t, None, tok, vl, uni, T=0.0, nthreads=nthreads)
+            elif mode != "opd":
+                oracle.verify(t, d, tok, vl, uni, T=1.0, nthreads=nthreads)
+            if mode not in ("verify", "greedy"):
+                oracle.opd(t, d, vl, clip, lam, with_grad=True, nthreads=nthreads)
+            done += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                return done, el
+
+    done, el = run(threads, budget_s)
+    done1, el1 = run(1, budget_s / 3)  # one thread, to show the scaling
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": positions * done / el, "unit": "positions/s", "cores": threads, "kind": "oracle",
             "sample": f"{nreq} requests ({positions} verified positions) of input set 0, "
-                      f"{done} repetitions in {el:.1f} s, {threads} threads"}
+                      f"{done} repetitions in {el:.1f} s, {threads} threads",
+            "value_1_thread": positions * done1 / el1, "cpu_model": model}
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak, AMD published
@@ -297,7 +309,10 @@ def main():
     import diffusion_drafter_verification_amd as ada
     import workloads as W
 
-    wl = W.WORKLOADS[{"single": 2, "c32": 3, "c128": 4}[args.workload]]
+    wl = W.WORKLOADS[{"single": 2, "c32": 3, "c128": 4, "replay": 5}[args.workload]]
+    if args.workload == "replay" and args.mode != "opd":
+        print("the replay workload is supervision only (--mode opd)", file=sys.stderr)
+        sys.exit(2)
     B, k, V = wl.B, wl.k, wl.V
     packed = args.layout == "packed"
     if packed and args.variant:
@@ -309,7 +324,10 @@ def main():
     sets = []
     for s in range(args.sets):
         # (greedy verification: the drafts are the drafter's argmax tokens)
-        bt = W.generate(wl, round=s, T=0.0) if args.mode == "greedy" else W.generate(wl, round=s)
+        if args.mode == "greedy":
+            bt = W.generate(wl, round=s, T=0.0)
+        else:
+            bt = W.generate(wl, round=s, with_tokens=args.mode != "opd")
         sets.append(bt)
     dsets = []
     for bt in sets:
@@ -321,7 +339,8 @@ def main():
         dsets.append({
             "t": torch.from_numpy(np.ascontiguousarray(tgt).view(np.int16)).view(torch.bfloat16).to(dev),
             "d": torch.from_numpy(np.ascontiguousarray(drf).view(np.int16)).view(torch.bfloat16).to(dev),
-            "tok": torch.from_numpy(bt.tokens).to(dev),
+            "tok": (torch.from_numpy(bt.tokens) if bt.tokens is not None
+                    else torch.zeros(B, k, dtype=torch.int32)).to(dev),
             "vl": torch.from_numpy(bt.verify_len).to(dev),
             "u": torch.from_numpy(bt.uniforms).to(dev),
         })
