@@ -26,7 +26,8 @@
  *
  * Conventions shared by every entry point
  *  - All array arguments are DEVICE pointers owned by the caller; the library
- *    allocates nothing and keeps no state between calls.  Calls are enqueued
+ *    allocates nothing and keeps no state between calls (the measurement
+ *    hook adaflash_timing_enable aside, which owns its HIP events).  Calls are enqueued
  *    on `stream` (a hipStream_t; NULL = the null stream) and return without
  *    synchronising.  Concurrent calls must use distinct workspaces.
  *  - Logits are row-major, contiguous; `dtype` selects fp32 or bf16 (raw
@@ -38,7 +39,8 @@
  *    the error (thread-local string).
  *  - Data errors only the device can see are repaired and reported in
  *    *status_flags (see ADAFLASH_FLAG_*): verify lengths outside [1, k] are
- *    clamped, draft tokens outside [0, V) are clamped, non-finite row
+ *    clamped (the packed-logits forms instead read nothing, see below),
+ *    draft tokens outside [0, V) are clamped, non-finite row
  *    statistics are flagged.  Read the flags after synchronising the stream.
  *  - Sizes: 1 <= k <= 64, 1 <= V <= 2^20, 0 <= B and B * (k + 1) < 2^24.
  *    B == 0 is a valid empty call (row_offsets[0] is set to 0).
