@@ -1,4 +1,4 @@
-"""Seeded sweep of small configurations through the C ABI against the oracle:
+"""Seeded sweep of 96 small configurations through the C ABI against the oracle:
 vocabulary sizes around the 8192-entry chunk boundary (and 1, 7), bf16 and
 fp32 rows, draft lengths 1 to 16, ragged and full verify lengths, greedy and
 sampled temperatures, with and without fused supervision (clip thresholds on
@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 VS = [1, 7, 3000, 8191, 8192, 8193, 16384, 16385, 24577]
 
 
-def _cases(n=36, seed=2024):
+def _cases(n=96, seed=2024):
     rng = np.random.default_rng(seed)
     out = []
     for q in range(n):
