@@ -1349,16 +1349,15 @@ __device__ __forceinline__ float grad_exact(float zq, float zp, float lse_q2, fl
   return fmaf(-lamS, q, fmaf(lam, sterm, ace * q));
 }
 
-// Workgroups per CU: aligned bf16 chunks fit 80 VGPRs (six per CU), and the
-// fused sampled variant 72 (seven per CU; two values of the rarely taken
-// exact path spill, measured faster than six); fp32 chunks take twice the
-// registers and the element-wise loads of unaligned rows more.  (Eight per
-// CU, 64 VGPRs, was 4% faster for supervision alone but spills chunk words
-// of the exact path and left some gradient slots of that path unwritten now
-// and then; it is not used.)
+// Workgroups per CU: aligned bf16 chunks fit 64 VGPRs without spills (eight
+// per CU; the exact path reads its chunk again rather than holding it across
+// its second barrier, and a rejected row's residual mass has a loop of its
+// own), measured 5% faster than seven for supervision alone and 1-2% fused
+// with verification; fp32 chunks take twice the registers and the
+// element-wise loads of unaligned rows more.
 template <bool BF16, bool ALIGNED, int VMODE, bool FKL>
 constexpr int sup_min_waves() {
-  return BF16 && ALIGNED ? (FKL ? 4 : (kElems <= 32 ? (VMODE == 2 ? 7 : 6) : 4)) : 1;
+  return BF16 && ALIGNED ? (FKL ? 4 : (kElems <= 32 ? 8 : 4)) : 1;
 }
 
 // FKL: the forward-KL variant (supervision only): pass 1 also sums
@@ -1655,8 +1654,16 @@ __global__ __launch_bounds__(kThreads, (sup_min_waves<BF16, ALIGNED, VMODE, FKL>
         if (P.grad) store_slot(s2, g);
       }
     };
-    if (need_res) sweep(std::true_type{});
-    else if (P.grad) sweep(std::false_type{});
+    if (P.grad) sweep(std::false_type{});
+    if (need_res) {
+      // The residual mass of a rejected row, in a loop of its own (fewer
+      // live registers than folding it into the gradient sweep).
+#pragma unroll
+      for (int e = 0; e < kElems; ++e) {
+        const float q = fexp2(fmaf(cq.get(e), kLog2e, -lse_q2));
+        Zpart += fmaxf(0.f, fexp2(fmaf(cp.get(e), kLog2e, -lse_p2)) - q);
+      }
+    }
     if (xs_here) {
       // (z_p at x* is the row maximum)
       const float pstar = FKL ? -afk * fexp2(st.Mp * kLog2e - lse_p2) : 0.f;
@@ -1710,6 +1717,23 @@ __global__ __launch_bounds__(kThreads, (sup_min_waves<BF16, ALIGNED, VMODE, FKL>
 #pragma unroll
       for (int s2 = 0; s2 < NV; ++s2) {
         float g[VEC];
+        if constexpr (BF16 && ALIGNED) {
+          // The chunk's words are read again slot by slot (this path is
+          // rare), so that no chunk is held in registers across the second
+          // barrier: the kernel then fits 64 registers without spills.
+          const int idx0 = v0 + s2 * (kThreads * VEC) + tid * VEC;
+          const uint4 pad4 = make_uint4(0xff7fff7fu, 0xff7fff7fu, 0xff7fff7fu, 0xff7fff7fu);
+          const uint4 wp = idx0 < V ? *(const uint4*)((const uint16_t*)trow + idx0) : pad4;
+          const uint4 wq = idx0 < V ? *(const uint4*)((const uint16_t*)drow + idx0) : pad4;
+          cp.w[s2 * 4 + 0] = wp.x;
+          cp.w[s2 * 4 + 1] = wp.y;
+          cp.w[s2 * 4 + 2] = wp.z;
+          cp.w[s2 * 4 + 3] = wp.w;
+          cq.w[s2 * 4 + 0] = wq.x;
+          cq.w[s2 * 4 + 1] = wq.y;
+          cq.w[s2 * 4 + 2] = wq.z;
+          cq.w[s2 * 4 + 3] = wq.w;
+        }
 #pragma unroll
         for (int u = 0; u < VEC; ++u) {
           const int e = s2 * VEC + u;
