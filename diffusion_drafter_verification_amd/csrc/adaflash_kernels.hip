@@ -2145,7 +2145,8 @@ thread_local Timing t_timing;
 void timing_mark(hipStream_t st, int stop) {
   Timing& t = t_timing;
   if (t.used >= t.cap) return;
-  hipEventRecord(t.ev[2 * t.used + stop], st);
+  // (a failed record shows up as a failed read: adaflash_timing_read)
+  (void)hipEventRecord(t.ev[2 * t.used + stop], st);
   if (stop) ++t.used;
 }
 
@@ -2185,7 +2186,7 @@ hipError_t dispatch_mode(const KParams& p, int grid, int opd, int vmode, bool t1
 
 int timing_enable(int cap) {
   Timing& t = t_timing;
-  for (hipEvent_t e : t.ev) hipEventDestroy(e);
+  for (hipEvent_t e : t.ev) (void)hipEventDestroy(e);
   t.ev.clear();
   t.cap = t.used = 0;
   if (cap <= 0) return 0;
