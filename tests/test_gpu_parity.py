@@ -350,3 +350,17 @@ def test_replay_workload(seed_off):
     # every row's losses are finite and the gradient rows sum to ~0
     assert np.isfinite(g["loss_ce"]).all() and np.isfinite(g["loss_rkl"]).all()
     assert np.abs(g["grad"].sum(axis=1)).max() < 0.05
+
+
+@pytest.mark.parametrize("T", [1.0, 0.0])
+def test_c128_verify_only_workload(T):
+    """B=128, k=16, V=151936 bf16 verification without supervision (the
+    statistics and residual kernels at T=1, the greedy statistics kernel at
+    T=0, as bench.py --mode verify / --mode greedy time them): every
+    request's accept length, tokens and margins against the oracle, 3
+    rounds."""
+    wl = W.WORKLOADS[4]
+    say("c128 verify only", T)
+    for r in range(3):
+        bt = W.generate(wl, round=r, T=T) if T == 0 else W.generate(wl, round=r)
+        check_verify(bt, T)
