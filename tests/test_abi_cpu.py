@@ -181,3 +181,34 @@ def test_loss_variant_rejects_bad_arguments(lib, variant, p1, p2, code):
     P = 0x10000
     rc = f(1, P, P, None, 4, 16, 64, variant, p1, p2, P, P, P, None, P, 1 << 30, None)
     assert rc == code
+
+
+# ------------------------------------------- packed forms, cached head, timing
+
+def test_packed_and_cached_forms_reject_bad_arguments(lib):
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    P = FAKE_ALIGNED
+    f = lib.adaflash_opd_loss_fwd_bwd_packed
+    f.restype = i32
+    f.argtypes = [i32, vp, vp, vp, i32, i32, i32, f32, f32, vp, vp, vp, vp, vp, vp, sz, vp]
+    assert f(1, P, P, P, 4, 16, 1000, 0.0, 1.0, P, P, P, P, P, P, 1 << 30, None) == -1  # clip c <= 0
+    assert f(1, P, P, P, 4, 16, 1000, 1.0, 1.0, None, P, P, P, P, P, 1 << 30, None) == -1  # no row_offsets
+    g = lib.adaflash_length_head_forward_cached
+    g.restype = i32
+    g.argtypes = [vp, vp, vp, vp, f32, i32, i32, i32, i32, f32, vp, vp, vp, vp, sz, vp]
+    assert g(P, P, P, P, 0.0, 4, 16, 64, 8, 1.0, P, P, None, P, 1 << 30, None) == -1  # no z1 cache
+    h = lib.adaflash_length_head_backward_cached
+    h.restype = i32
+    h.argtypes = [vp, vp, vp, vp, f32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    assert h(P, P, P, P, 0.0, 4, 16, 64, 8, P, P, P, P, P, P, P, None, P, 1 << 30, None) == -1
+
+
+def test_timing_hook_argument_checks(lib):
+    lib.adaflash_timing_enable.restype = ctypes.c_int
+    lib.adaflash_timing_enable.argtypes = [ctypes.c_int]
+    lib.adaflash_timing_read.restype = ctypes.c_int
+    lib.adaflash_timing_read.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    assert lib.adaflash_timing_enable(-1) == -1
+    assert lib.adaflash_timing_enable(0) == 0  # disabling creates nothing
+    assert lib.adaflash_timing_read(None, 4) == -1
+    assert lib.adaflash_timing_read(None, 0) == 0  # nothing recorded
