@@ -28,7 +28,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published peak
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "sup_kernel_c128_fused_hbm_bytes.md")
+TRAFFIC_PROFILE = {"fused": os.path.join(ROOT, "profiles", "sup_kernel_c128_fused_hbm_bytes.md"),
+                   "verify": os.path.join(ROOT, "profiles", "vstat_kernel_c128_verify.md")}
 KERNEL_SOURCE = os.path.join(ROOT, "diffusion_drafter_verification_amd", "csrc", "adaflash_kernels.hip")
 METRIC = "verified draft positions/sec + achieved HBM GB/s (B=128, k=16, V=151936)"
 
@@ -37,7 +38,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--sets", type=int, default=2, help="input sets rotated between calls")
     ap.add_argument("--clip", type=float, default=10.0)
     ap.add_argument("--lam", type=float, default=1.0)
@@ -92,13 +93,15 @@ def copy_probe():
 
 
 def measured_traffic(mode, default_shape=True):
-    """HBM bytes per launch of the fused kernel from the committed rocprofv3
-    counter summary, or None when the kernel source changed since then."""
+    """HBM bytes per launch of the dominant kernel (fused or sampled verify
+    mode, default shape) from the committed rocprofv3 counter summary, or
+    None when the kernel source changed since then."""
     import hashlib
     import re
-    if mode != "fused" or not default_shape or not os.path.exists(TRAFFIC_PROFILE):
+    path = TRAFFIC_PROFILE.get(mode)
+    if path is None or not default_shape or not os.path.exists(path):
         return None
-    m = re.search(r"```json\n(.*?)\n```", open(TRAFFIC_PROFILE).read(), re.S)
+    m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
     if not m:
         return None
     rec = json.loads(m.group(1))
@@ -189,13 +192,18 @@ def bench_length_head(args):
     for i in range(args.warmup):
         call(d[i % len(d)])
     torch.cuda.synchronize()
+    # Events around each step first, then the timed steps with no event
+    # between them, bracketed by synchronisations.
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    t0 = time.perf_counter()
     for i in range(args.steps):
         starts[i].record(stream)
         call(d[i % len(d)])
         ends[i].record(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        call(d[i % len(d)])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     durs = np.array([s_.elapsed_time(e) for s_, e in zip(starts, ends)]) * 1e-3
@@ -390,21 +398,32 @@ def main():
         call(dsets[i % len(dsets)])
     torch.cuda.synchronize()
 
+    # Pass 1: events around each whole call (the per-call distribution).  It
+    # runs first so that the two passes below find the GPU's clocks settled
+    # even when few warm-up calls were asked for.
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    # HIP events around the dominant kernel of every timed call, recorded by
-    # the library on the call's stream.
-    ada.adaflash_timing_enable(args.steps)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for i in range(args.steps):
         starts[i].record(stream)
         call(dsets[i % len(dsets)])
         ends[i].record(stream)
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    # Pass 2: HIP events attached by the library to the dispatch of each
+    # call's dominant kernel (for the roofline).
+    ada.adaflash_timing_enable(args.steps)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        call(dsets[i % len(dsets)])
+    torch.cuda.synchronize()
     kdur = np.array(ada.adaflash_timing_read(args.steps)) * 1e-3  # seconds
     ada.adaflash_timing_enable(0)
+    # Pass 3, the timed steps: back-to-back calls with no event between
+    # them, bracketed by synchronisations (value and ms_per_step).
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        call(dsets[i % len(dsets)])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
     st = int(status.item())
     if st != 0:
         print(f"status flags {st} after the timed calls", file=sys.stderr)

@@ -38,6 +38,7 @@
 //     CE = lse_q - z_q[x*], grad = q - e_{x*} + lambda q (1_U (lq - lp + 1) - S).
 //   Exponentials use v_exp_f32 (2^x) on log2-scaled arguments.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -2115,16 +2116,36 @@ __global__ __launch_bounds__(1024) void pack_kernel(const int32_t* verify_len, i
   }
 }
 
+// Measurement hook: while enabled on the calling thread, each call launches
+// its dominant kernel (the first row kernel) with a pair of events attached
+// to that dispatch, which take the kernel's own start and end times, so that
+// a benchmark can time that kernel alone.
+struct Timing {
+  std::vector<hipEvent_t> ev;  // two per record
+  int cap = 0, used = 0;
+};
+thread_local Timing t_timing;
+
+template <typename K>
+hipError_t launch_dominant(K kernel, int grid, hipStream_t st, const KParams& p) {
+  Timing& t = t_timing;
+  if (t.used < t.cap) {
+    hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, st, t.ev[2 * t.used], t.ev[2 * t.used + 1], 0, p);
+    ++t.used;
+  } else {
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, st, p);
+  }
+  return hipGetLastError();
+}
+
 template <bool BF16, bool ALIGNED, bool OPD, int VMODE, bool T1>
 hipError_t launch_rows(const KParams& p, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((row_kernel<BF16, ALIGNED, OPD, VMODE, T1>), dim3(grid), dim3(kThreads), 0, st, p);
-  return hipGetLastError();
+  return launch_dominant(row_kernel<BF16, ALIGNED, OPD, VMODE, T1>, grid, st, p);
 }
 
 template <bool BF16, bool ALIGNED, int VMODE, bool FKL = false>
 hipError_t launch_sup(const KParams& p, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((sup_kernel<BF16, ALIGNED, VMODE, FKL>), dim3(grid), dim3(kThreads), 0, st, p);
-  return hipGetLastError();
+  return launch_dominant(sup_kernel<BF16, ALIGNED, VMODE, FKL>, grid, st, p);
 }
 
 template <bool BF16, bool ALIGNED, int VMODE>
@@ -2133,27 +2154,9 @@ hipError_t launch_final(const KParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Measurement hook: while enabled on the calling thread, each call records
-// a pair of events on its stream around its dominant kernel (the first row
-// kernel it launches), so that a benchmark can time that kernel alone.
-struct Timing {
-  std::vector<hipEvent_t> ev;  // two per record
-  int cap = 0, used = 0;
-};
-thread_local Timing t_timing;
-
-void timing_mark(hipStream_t st, int stop) {
-  Timing& t = t_timing;
-  if (t.used >= t.cap) return;
-  // (a failed record shows up as a failed read: adaflash_timing_read)
-  (void)hipEventRecord(t.ev[2 * t.used + stop], st);
-  if (stop) ++t.used;
-}
-
 template <bool BF16, bool ALIGNED>
 hipError_t dispatch_mode(const KParams& p, int grid, int opd, int vmode, bool t1, bool fkl, hipStream_t st) {
   hipError_t e;
-  timing_mark(st, 0);
   if (opd && vmode == 0 && fkl) e = launch_sup<BF16, ALIGNED, 0, true>(p, grid, st);
   else if (opd && vmode == 0) e = launch_sup<BF16, ALIGNED, 0>(p, grid, st);
   else if (opd && vmode == 1) e = launch_sup<BF16, ALIGNED, 1>(p, grid, st);
@@ -2161,13 +2164,10 @@ hipError_t dispatch_mode(const KParams& p, int grid, int opd, int vmode, bool t1
   else if (opd) e = launch_rows<BF16, ALIGNED, true, 2, false>(p, grid, st);
   else if (vmode == 1) {
     const int ng = (p.k + kGRows) / kGRows;
-    hipLaunchKernelGGL((gstat_kernel<BF16, ALIGNED>), dim3(p.B * ng * p.G), dim3(kThreads), 0, st, p);
-    e = hipGetLastError();
+    e = launch_dominant(gstat_kernel<BF16, ALIGNED>, p.B * ng * p.G, st, p);
   }
   else if (vmode == 2) {
-    hipLaunchKernelGGL((vstat_kernel<BF16, ALIGNED>), dim3(grid), dim3(kThreads), 0, st, p);
-    e = hipGetLastError();
-    timing_mark(st, 1);
+    e = launch_dominant(vstat_kernel<BF16, ALIGNED>, grid, st, p);
     if (e == hipSuccess) {
       const int gh = (p.G + kResChunks - 1) / kResChunks;
       hipLaunchKernelGGL((vres_kernel<BF16, ALIGNED>), dim3(p.B * gh), dim3(kThreads), 0, st, p);
@@ -2175,7 +2175,6 @@ hipError_t dispatch_mode(const KParams& p, int grid, int opd, int vmode, bool t1
     }
   }
   else return hipErrorInvalidValue;
-  if (vmode != 2 || opd) timing_mark(st, 1);
   if (e != hipSuccess) return e;
   if (vmode == 1) return launch_final<BF16, ALIGNED, 1>(p, st);
   if (vmode == 2) return launch_final<BF16, ALIGNED, 2>(p, st);

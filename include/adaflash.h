@@ -92,10 +92,11 @@ ADAFLASH_API const char* adaflash_last_error(void);
 /*
  * Measurement hook, for benchmarks; no part of the method.  While enabled on
  * the calling thread, every call of the verify / supervision / loss-variant
- * entry points records a pair of HIP events on its stream around its
- * dominant kernel (the row kernel: the supervision kernel, the statistics
- * kernel of sampled verification, or the greedy row kernel), for up to
- * max_records calls.  adaflash_timing_enable(0) disables the hook and
+ * entry points launches its dominant kernel (the row kernel: the
+ * supervision kernel, the statistics kernel of sampled verification, or the
+ * greedy row kernel) with a pair of HIP events attached to that dispatch,
+ * which take the kernel's own start and end times, for up to max_records
+ * calls.  adaflash_timing_enable(0) disables the hook and
  * destroys the events.  adaflash_timing_read waits for the recorded events,
  * writes up to cap durations in milliseconds (call order) and starts a new
  * series; it returns the count written, or a negative adaflash_status.
