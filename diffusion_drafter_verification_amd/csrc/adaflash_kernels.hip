@@ -703,21 +703,31 @@ __device__ __forceinline__ unsigned int ukey(float x) {
 template <bool BF16, bool ALIGNED, int VMODE>
 __device__ void finalize_request(const KParams& P, int b, FinShared& fs) {
   const int k = P.k, V = P.V, G = P.G;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x;  // (k + 1 <= 65 rows: thread i holds position i)
+  const int r0 = b * (k + 1);   // row slot of position 0
+  // Reads that do not depend on the verify length are issued with it: the
+  // clamped draft token and (sampled) the accept flag of every position.
+  int tok = 0;
+  float acc_flag = 1.f;
+  if (tid < k) {
+    const int x = P.tokens[(size_t)b * k + tid];
+    tok = x < 0 ? 0 : (x >= V ? V - 1 : x);
+    if constexpr (VMODE != 1) acc_flag = pub_load(P.rowrec + (size_t)(r0 + tid) * kRowRec + 1);
+  }
   const int L = P.Lc[b];
   if (L < 0) return;  // packed rows unusable (see pack_kernel)
-  const int r0 = b * (k + 1);  // row slot of position 0
   int A = L, token = 0;
   float sample_margin = __int_as_float(0x7fc00000);
 
   if constexpr (VMODE == 1) {
-    // Greedy: the argmax of rows 0..L from their chunk records, all rows at
-    // once (largest maximum, then lowest index, as one 64-bit key), then the
-    // first position whose draft token differs from its row's argmax.
+    // Greedy: the argmax of every row slot from its chunk records, all rows
+    // at once (largest maximum, then lowest index, as one 64-bit key; slots
+    // past row L hold stale records and are not used), then the first
+    // position whose draft token differs from its row's argmax.
     const int nrows = L + 1;
-    for (int i = tid; i < nrows; i += kThreads) fs.amax[i] = 0ull;
+    for (int i = tid; i <= k; i += kThreads) fs.amax[i] = 0ull;
     __syncthreads();
-    for (int q = tid; q < nrows * G; q += kThreads) {
+    for (int q = tid; q < (k + 1) * G; q += kThreads) {
       const int i = q / G, j = q - i * G;
       const float* rec = P.part1 + ((size_t)(r0 + i) * G + j) * kRec1;
       const float m = pub_load(rec + 0);
@@ -728,17 +738,14 @@ __device__ void finalize_request(const KParams& P, int b, FinShared& fs) {
     __syncthreads();
     int mism = kIntMax;
     int bad = 0;
-    for (int i = tid; i < nrows; i += kThreads) {
+    if (tid < nrows) {
+      const int i = tid;
       int am = (int)(0xffffffffu - (unsigned int)(fs.amax[i] & 0xffffffffull));
       if (am == kIntMax || am < 0 || am >= V) {  // NaN row: no chunk holds the maximum
         am = 0;
         bad = 1;
       }
-      if (i < L) {
-        int x = P.tokens[(size_t)b * k + i];
-        x = x < 0 ? 0 : (x >= V ? V - 1 : x);
-        if (x != am) mism = min(mism, i);
-      }
+      if (i < L && tok != am) mism = min(mism, i);
       fs.amax[i] = (unsigned long long)am;  // now the row's argmax
     }
     float v[2] = {__int_as_float(mism), __int_as_float(bad)};
@@ -749,14 +756,12 @@ __device__ void finalize_request(const KParams& P, int b, FinShared& fs) {
     token = (int)fs.amax[A];
   } else {
     // Sampled: first rejected row from the per-row accept flags.
-    int first = kIntMax;
-    for (int i = tid; i < L; i += kThreads)
-      if (pub_load(P.rowrec + (size_t)(r0 + i) * kRowRec + 1) == 0.f) first = min(first, i);
+    const int first0 = tid < L && acc_flag == 0.f ? tid : kIntMax;
     const float us = P.uniforms[(size_t)b * (k + 1) + k];
-    float v1[1] = {__int_as_float(first)};
+    float v1[1] = {__int_as_float(first0)};
     const int o1[1] = {OP_MINI};
     wg_reduce<1>(v1, o1, fs.red);
-    first = __float_as_int(v1[0]);
+    const int first = __float_as_int(v1[0]);
     A = first < L ? first : L;
 
     // Row statistics at T of the row the draw reads (rejected row A or the
@@ -891,14 +896,11 @@ __device__ void finalize_request(const KParams& P, int b, FinShared& fs) {
   }
 
   // Outputs.
-  for (int i = tid; i <= k; i += kThreads) {
+  if (tid <= k) {
+    const int i = tid;
     int32_t t = -1;
-    if (i < A) {
-      int x = P.tokens[(size_t)b * k + i];
-      t = x < 0 ? 0 : (x >= V ? V - 1 : x);
-    } else if (i == A) {
-      t = token;
-    }
+    if (i < A) t = tok;
+    else if (i == A) t = token;
     P.out_tokens[(size_t)b * (k + 1) + i] = t;
     if (P.margins) {
       if (i == k) P.margins[(size_t)b * (k + 1) + k] = sample_margin;
