@@ -654,34 +654,6 @@ struct FinShared {
   unsigned long long amax[72];      // greedy: per-row (value, index) argmax keys
 };
 
-// Chunk-level inverse CDF: thread t < G holds the mass of chunk t.  Returns the
-// chunk whose cumulative mass first exceeds u * total (else the last chunk with
-// positive mass, else 0) and the cumulative mass before it.
-__device__ void locate_chunk(float mj, int G, float us, FinShared& fs, int* jc_out, float* before_out,
-                             float* thr_out, float* tot_out) {
-  const int tid = threadIdx.x;
-  float tot;
-  const float ex = wg_scan_excl(mj, fs.red, &tot);
-  const float thr = us * tot;
-  const int cross = (tid < G && ex + mj > thr) ? tid : kIntMax;
-  const int lastpos = (tid < G && mj > 0.f) ? -tid : kIntMax;
-  float v[2] = {__int_as_float(cross), __int_as_float(lastpos)};
-  const int ops[2] = {OP_MINI, OP_MINI};
-  wg_reduce<2>(v, ops, fs.red);
-  int jc = __float_as_int(v[0]);
-  if (jc == kIntMax) {
-    const int lp = __float_as_int(v[1]);
-    jc = lp == kIntMax ? 0 : -lp;
-  }
-  if (tid == jc) fs.f[0] = ex;
-  __syncthreads();
-  *before_out = fs.f[0];
-  *jc_out = jc;
-  *thr_out = thr;
-  *tot_out = tot;
-  __syncthreads();
-}
-
 // Inclusive prefix sum across the 64 lanes of a wave.
 __device__ __forceinline__ float wave_scan_incl(float v) {
   const int lane = threadIdx.x & 63;
@@ -704,15 +676,20 @@ template <bool BF16, bool ALIGNED, int VMODE>
 __device__ void finalize_request(const KParams& P, int b, FinShared& fs) {
   const int k = P.k, V = P.V, G = P.G;
   const int tid = threadIdx.x;  // (k + 1 <= 65 rows: thread i holds position i)
+  const int lane = tid & 63;
   const int r0 = b * (k + 1);   // row slot of position 0
   // Reads that do not depend on the verify length are issued with it: the
-  // clamped draft token and (sampled) the accept flag of every position.
+  // clamped draft token of position tid and (sampled) the accept flag of
+  // position `lane` in every wave, and the uniform of the draw.
   int tok = 0;
-  float acc_flag = 1.f;
+  float acc_flag = 1.f, us = 0.f;
   if (tid < k) {
     const int x = P.tokens[(size_t)b * k + tid];
     tok = x < 0 ? 0 : (x >= V ? V - 1 : x);
-    if constexpr (VMODE != 1) acc_flag = pub_load(P.rowrec + (size_t)(r0 + tid) * kRowRec + 1);
+  }
+  if constexpr (VMODE != 1) {
+    if (lane < k) acc_flag = pub_load(P.rowrec + (size_t)(r0 + lane) * kRowRec + 1);
+    us = P.uniforms[(size_t)b * (k + 1) + k];
   }
   const int L = P.Lc[b];
   if (L < 0) return;  // packed rows unusable (see pack_kernel)
@@ -755,46 +732,76 @@ __device__ void finalize_request(const KParams& P, int b, FinShared& fs) {
     A = __float_as_int(v[0]) < L ? __float_as_int(v[0]) : L;
     token = (int)fs.amax[A];
   } else {
-    // Sampled: first rejected row from the per-row accept flags.
-    const int first0 = tid < L && acc_flag == 0.f ? tid : kIntMax;
-    const float us = P.uniforms[(size_t)b * (k + 1) + k];
-    float v1[1] = {__int_as_float(first0)};
-    const int o1[1] = {OP_MINI};
-    wg_reduce<1>(v1, o1, fs.red);
-    const int first = __float_as_int(v1[0]);
-    A = first < L ? first : L;
+    // Sampled.  Every wave finds the first rejected row, the statistics of
+    // the row the draw reads and the chunk of the draw by itself, from k <= 64
+    // accept flags (one per lane) and G <= 128 chunk records (up to two per
+    // lane), in the same fixed order in every wave: no workgroup barrier
+    // separates these steps, and all threads hold the same results.
+    const unsigned long long rej = __ballot(lane < L && acc_flag == 0.f);
+    A = rej ? min((int)__builtin_ctzll(rej), L) : L;
 
     // Row statistics at T of the row the draw reads (rejected row A or the
-    // bonus row L) and, for a rejected row, its per-chunk residual masses:
-    // all loaded in one round.
+    // bonus row L) and, for a rejected row, its per-chunk residual masses.
     const int rs = r0 + A;
-    float mp = neg_inf(), spT = 0.f, mq = neg_inf(), sqT = 0.f, res = 0.f;
-    if (tid < G) {
-      const float* rec = P.part1 + ((size_t)rs * G + tid) * kRec1;
-      mp = pub_load(rec + 0);
-      spT = pub_load(rec + 2);
-      if (A < L) {
-        mq = pub_load(rec + 4);
-        sqT = pub_load(rec + 5);
-        res = pub_load(P.part2 + ((size_t)rs * G + tid) * kRec2 + 2);
+    float mp[2], spT[2], mq[2], sqT[2], res[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int jj = lane + 64 * h;
+      mp[h] = neg_inf();
+      mq[h] = neg_inf();
+      spT[h] = sqT[h] = res[h] = 0.f;
+      if (jj < G) {
+        const float* rec = P.part1 + ((size_t)rs * G + jj) * kRec1;
+        mp[h] = pub_load(rec + 0);
+        spT[h] = pub_load(rec + 2);
+        if (A < L) {
+          mq[h] = pub_load(rec + 4);
+          sqT[h] = pub_load(rec + 5);
+          res[h] = pub_load(P.part2 + ((size_t)rs * G + jj) * kRec2 + 2);
+        }
       }
     }
-    float m[2] = {mp, mq};
-    const int mops[2] = {OP_MAX, OP_MAX};
-    wg_reduce<2>(m, mops, fs.red);
-    const float Mp = m[0], Mq = m[1];
-    const float pj = mp == neg_inf() ? 0.f : spT * fexp2((mp - Mp) * P.kT);
-    const float qj = mq == neg_inf() ? 0.f : sqT * fexp2((mq - Mq) * P.kT);
-    float sv[3] = {pj, qj, res};
-    const int sops[3] = {OP_SUM, OP_SUM, OP_SUM};
-    wg_reduce<3>(sv, sops, fs.red);
-    const float SpT = sv[0], SqT = sv[1];
+    const float Mp = wave_reduce<OP_MAX>(fmaxf(mp[0], mp[1]));
+    const float Mq = wave_reduce<OP_MAX>(fmaxf(mq[0], mq[1]));
+    float pj[2], qj[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      pj[h] = mp[h] == neg_inf() ? 0.f : spT[h] * fexp2((mp[h] - Mp) * P.kT);
+      qj[h] = mq[h] == neg_inf() ? 0.f : sqT[h] * fexp2((mq[h] - Mq) * P.kT);
+    }
+    const float SpT = wave_reduce<OP_SUM>(pj[0] + pj[1]);
+    const float SqT = wave_reduce<OP_SUM>(qj[0] + qj[1]);
+    const float Zres = wave_reduce<OP_SUM>(res[0] + res[1]);
     const float invSp = 1.f / SpT, invSq = 1.f / SqT;
-    const bool resid = A < L && sv[2] > 0.f;
-    const float mj = tid < G ? (resid ? res : pj * invSp) : 0.f;
+    const bool resid = A < L && Zres > 0.f;
+
+    // Chunk-level inverse CDF over the chunk masses in chunk order: the first
+    // chunk whose running mass passes u_s times the total, else the last
+    // chunk with positive mass, else chunk 0.
+    float mj[2], ex[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) mj[h] = lane + 64 * h < G ? (resid ? res[h] : pj[h] * invSp) : 0.f;
+    const float inc0 = wave_scan_incl(mj[0]);
+    const float tot0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(inc0), 63));
+    const float inc1 = tot0 + wave_scan_incl(mj[1]);
+    const float tot = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(inc1), 63));
+    ex[0] = __shfl_up(inc0, 1, 64);
+    ex[1] = __shfl_up(inc1, 1, 64);
+    if (lane == 0) {
+      ex[0] = 0.f;
+      ex[1] = tot0;
+    }
+    const float thr = us * tot;
+    const unsigned long long c0 = __ballot(lane < G && ex[0] + mj[0] > thr);
+    const unsigned long long c1 = __ballot(lane + 64 < G && ex[1] + mj[1] > thr);
+    const unsigned long long q0 = __ballot(lane < G && mj[0] > 0.f);
+    const unsigned long long q1 = __ballot(lane + 64 < G && mj[1] > 0.f);
     int jc = 0;
-    float base = 0.f, thr = 0.f, tot = 1.f;
-    locate_chunk(mj, G, us, fs, &jc, &base, &thr, &tot);
+    if (c0) jc = (int)__builtin_ctzll(c0);
+    else if (c1) jc = 64 + (int)__builtin_ctzll(c1);
+    else if (q1) jc = 127 - (int)__builtin_clzll(q1);
+    else if (q0) jc = 63 - (int)__builtin_clzll(q0);
+    const float base = __shfl(jc < 64 ? ex[0] : ex[1], jc & 63, 64);
 
     // Scan chunk jc in index order: per-entry masses, one prefix sum over
     // (slot, thread, entry), the lowest index whose running sum passes thr.
@@ -807,7 +814,7 @@ __device__ void finalize_request(const KParams& P, int b, FinShared& fs) {
     const float ap = -Mp * P.kT, aq = -Mq * P.kT;
     constexpr int VEC = Chunk<BF16>::VEC;
     constexpr int NV = kElems / VEC;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int wave = tid >> 6;
     float w[kElems];
     float incl[NV], tsum[NV];
 #pragma unroll
