@@ -25,7 +25,7 @@ int fail(int code, const char* fmt, const char* detail = "") {
 inline size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
 bool sizes_ok(int B, int k, int V) {
-  if (B < 0 || k < 1 || k > 64 || V < 1 || V > (1 << 20)) return false;
+  if (B < 0 || k < 1 || k > kMaxK || V < 1 || V > kMaxV) return false;
   if ((long long)B * (k + 1) >= (1LL << 24)) return false;
   return true;
 }

@@ -18,6 +18,13 @@ constexpr int kChunk = kThreads * kElems;  // elements of one row per workgroup
 
 inline int num_chunks(int V) { return (V + kChunk - 1) / kChunk; }
 
+// Largest vocabulary and draft length the verify and supervision entry
+// points accept.  The finaliser's per-wave steps hold one draft position and
+// at most two chunk records of a row per lane.
+constexpr int kMaxV = 1 << 20, kMaxK = 64;
+static_assert((kMaxV + kChunk - 1) / kChunk <= 128, "at most two chunk records per lane");
+static_assert(kMaxK <= 64, "one draft position per lane");
+
 // Arrival counters sit 256 bytes apart so that no two share a cache line.
 constexpr int kCounterStride = 64;
 // Floats per published chunk record.
