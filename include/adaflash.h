@@ -96,7 +96,9 @@ ADAFLASH_API const char* adaflash_last_error(void);
  * supervision kernel, the statistics kernel of sampled verification, or the
  * greedy row kernel) with a pair of HIP events attached to that dispatch,
  * which take the kernel's own start and end times, for up to max_records
- * calls.  adaflash_timing_enable(0) disables the hook and
+ * calls.  The events belong to the device current at
+ * adaflash_timing_enable; time calls on that device only.
+ * adaflash_timing_enable(0) disables the hook and
  * destroys the events.  adaflash_timing_read waits for the recorded events,
  * writes up to cap durations in milliseconds (call order) and starts a new
  * series; it returns the count written, or a negative adaflash_status.
