@@ -2062,8 +2062,9 @@ __global__ __launch_bounds__(kThreads) void final_kernel(KParams P) {
 
 // One workgroup of 1024 threads: clamps the verify lengths, writes the packed
 // row offsets (prefix sum: a scan inside each wave, then across the 16
-// waves), clears the arrival counters, marks every row's accept flag as not
-// yet known, and initialises the status word.
+// waves), clears the arrival counters and marks the accept flags as not yet
+// known for the draft rows in use (the only rows that wait at a row barrier
+// or whose flags are read), and initialises the status word.
 __global__ __launch_bounds__(1024) void pack_kernel(const int32_t* verify_len, int B, int k, int packed,
                                                      int32_t* row_offsets, Workspace ws, int32_t* status) {
   __shared__ int s_wave[16];
@@ -2101,14 +2102,14 @@ __global__ __launch_bounds__(1024) void pack_kernel(const int32_t* verify_len, i
     if (b < B) {
       const int off = carry + woff + x - L;
       row_offsets[b] = off;
-      for (int q = 0; q < L; ++q) ws.rowmap[off + q] = b * 64 + q;  // (k <= 64)
-    }
-    // Row slots of this block's requests, spread over the threads.
-    const int pairs = min(1024, B - base) * (k + 1);
-    const size_t r0 = (size_t)base * (k + 1);
-    for (int q = tid; q < pairs; q += 1024) {
-      ws.rowcnt[(r0 + q) * kCounterStride] = 0;
-      ws.rowrec[(r0 + q) * kRowRec + 1] = 2.f;  // accept flag: not yet known
+      // Draft rows i < L: packed row map, arrival counter, accept flag (not
+      // yet known).  Rows past L are never waited on or read.
+      const size_t r0 = (size_t)b * (k + 1);
+      for (int q = 0; q < L; ++q) {
+        ws.rowmap[off + q] = b * 64 + q;  // (k <= 64)
+        ws.rowcnt[(r0 + q) * kCounterStride] = 0;
+        ws.rowrec[(r0 + q) * kRowRec + 1] = 2.f;
+      }
     }
     carry += tot;
     __syncthreads();
