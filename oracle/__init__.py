@@ -51,7 +51,7 @@ def _load():
         vp, i32, i64, f64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
         lib.oracle_verify.restype = i32
         lib.oracle_verify.argtypes = [i32, vp, vp, vp, vp, vp, i32, i32, i32, f64, vp, vp, vp, vp,
-                                      i32, i32]
+                                      vp, i32, i32]
         lib.oracle_opd.restype = i64
         lib.oracle_opd.argtypes = [i32, vp, vp, vp, i32, i32, i32, f64, f64, vp, i64, vp, vp, vp, i32]
         _lib = lib
@@ -79,9 +79,10 @@ def verify(target: np.ndarray, draft: Optional[np.ndarray], tokens: np.ndarray,
            nthreads: Optional[int] = None) -> dict:
     """Speculative verification of a batch in double precision.
 
-    Returns accept_len [B], out_tokens [B, k+1], margins [B, k+1] and
+    Returns accept_len [B], out_tokens [B, k+1], margins [B, k+1],
     sample_info [B, 4] = (total mass, threshold, running sum before the token,
-    running sum after it)."""
+    running sum after it) and accept_pq [B, k, 2] = (p(x_i), u_i q(x_i)) of
+    every accept test (NaN where no test is defined)."""
     B, k1, V = target.shape
     k = k1 - 1
     target = np.ascontiguousarray(target)
@@ -95,12 +96,13 @@ def verify(target: np.ndarray, draft: Optional[np.ndarray], tokens: np.ndarray,
     out = np.empty((B, k + 1), dtype=np.int32)
     mg = np.empty((B, k + 1), dtype=np.float64)
     si = np.empty((B, 4), dtype=np.float64)
+    pq = np.empty((B, k, 2), dtype=np.float64)
     rc = _load().oracle_verify(_dtype_code(target), _ptr(target), _ptr(draft), _ptr(tokens), _ptr(vl),
                                _ptr(uni), B, k, V, float(T), _ptr(acc), _ptr(out), _ptr(mg), _ptr(si),
-                               int(flags), _threads(nthreads))
+                               _ptr(pq), int(flags), _threads(nthreads))
     if rc != 0:
         raise ValueError(f"oracle_verify rejected its arguments ({rc})")
-    return {"accept_len": acc, "out_tokens": out, "margins": mg, "sample_info": si}
+    return {"accept_len": acc, "out_tokens": out, "margins": mg, "sample_info": si, "accept_pq": pq}
 
 
 def opd(target: np.ndarray, draft: np.ndarray, verify_len: Optional[np.ndarray], clip_c: float,

@@ -163,11 +163,14 @@ enum {
 //   or bonus token, then -1); margins [B, k+1] (p(x_i) - u_i q(x_i) for i < L, NaN
 //   elsewhere and in greedy mode; margins[b][k] is the sample's distance to the nearest
 //   CDF boundary of the chosen token divided by the total mass; NaN in greedy mode);
-//   sample_info [B, 4] = {total mass Z, threshold, running sum before token, after token}.
+//   sample_info [B, 4] = {total mass Z, threshold, running sum before token, after token};
+//   accept_pq [B, k, 2] (may be NULL) = {p(x_i), u_i q(x_i)} of every accept test
+//   i < L (the two sides whose difference is the margin), NaN elsewhere and in
+//   greedy mode.
 int oracle_verify(int dtype, const void* target, const void* draft, const int32_t* tokens,
                   const int32_t* verify_len, const float* uniforms, int B, int k, int V, double T,
                   int32_t* accept_len, int32_t* out_tokens, double* margins, double* sample_info,
-                  int flags, int nthreads) {
+                  double* accept_pq, int flags, int nthreads) {
   if (B < 0 || k < 1 || V < 1 || !(T >= 0.0)) return -1;
   parallel_for(B, nthreads, [&](int64_t b) {
     int L = verify_len ? verify_len[b] : k;
@@ -177,6 +180,15 @@ int oracle_verify(int dtype, const void* target, const void* draft, const int32_
     std::vector<double> zp, zq, p, q;
     int A = L;
     for (int i = 0; i <= k; ++i) margins[b * (k + 1) + i] = kNaN;
+    if (accept_pq)
+      for (int i = 0; i < 2 * k; ++i) accept_pq[b * 2 * k + i] = kNaN;
+    auto record = [&](int i, double px, double uqx) {
+      margins[b * (k + 1) + i] = px - uqx;
+      if (accept_pq) {
+        accept_pq[(b * k + i) * 2 + 0] = px;
+        accept_pq[(b * k + i) * 2 + 1] = uqx;
+      }
+    };
 
     // Accept tests, left to right; stop at the first rejection.
     for (int i = 0; i < L; ++i) {
@@ -192,7 +204,7 @@ int oracle_verify(int dtype, const void* target, const void* draft, const int32_
         softmax_T(zp, T, p);
         softmax_T(zq, T, q);
         accept = (double)u[i] * q[x] < p[x];
-        margins[b * (k + 1) + i] = p[x] - (double)u[i] * q[x];
+        record(i, p[x], (double)u[i] * q[x]);
       }
       if (!accept) {
         A = i;
@@ -210,7 +222,7 @@ int oracle_verify(int dtype, const void* target, const void* draft, const int32_
         row_values(dtype, draft, b * (int64_t)k + i, V, zq);
         softmax_T(zp, T, p);
         softmax_T(zq, T, q);
-        margins[b * (k + 1) + i] = p[x] - (double)u[i] * q[x];
+        record(i, p[x], (double)u[i] * q[x]);
       }
     }
 

@@ -13,13 +13,18 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "slow: long-running statistical test")
 
 
+def _stale(lib, src):
+    return not os.path.exists(lib) or os.path.getmtime(lib) < os.path.getmtime(src)
+
+
 def _ensure_host_libs():
-    """Build the host-side helper libraries if they are missing (seconds)."""
+    """Build the host-side helper libraries if they are missing or older than
+    their source (seconds)."""
     import workloads
     import oracle
-    if not os.path.exists(workloads.LIB_PATH):
+    if _stale(workloads.LIB_PATH, os.path.join(ROOT, "workloads", "gen.cpp")):
         workloads.build()
-    if not os.path.exists(oracle.LIB_PATH):
+    if _stale(oracle.LIB_PATH, os.path.join(ROOT, "oracle", "oracle.cpp")):
         oracle.build()
 
 

@@ -455,3 +455,64 @@ def test_greedy_ties_take_the_lowest_index():
     assert list(out["out_tokens"][0]) == [0, 0, 0]
     assert list(out["accept_len"]) == [2, 1]
     assert list(out["out_tokens"][1]) == [1, 1, -1]
+
+
+# ------------------------------------ hand-computed margins and the Z == 0 case
+#
+# DFlash reading notes, section 5.2: accept iff u q(x) < p(x) (eq. 6); on a
+# rejection draw from the residual [p - q]_+ / Z (eq. 7), with no rejection
+# possible when Z = 0; the bonus token comes from the target row after the last
+# draft (Algorithm 1, step 9).  The inverse CDF takes the smallest id whose
+# running sum exceeds u Z.  The values below are worked by hand on V = 4.
+
+def _one_request(p_rows, q_row, token, u_acc, u_draw):
+    """One request, k = 1: target rows (position 0, bonus row), one draft row."""
+    with np.errstate(divide="ignore"):
+        target = np.log(np.asarray(p_rows, np.float64)).astype(np.float32)[None]
+        draft = np.log(np.asarray([q_row], np.float64)).astype(np.float32)[None]
+    tok = np.array([[token]], np.int32)
+    uni = np.array([[u_acc, u_draw]], np.float32)
+    return oracle.verify(target, draft, tok, None, uni, T=1.0)
+
+
+def test_bonus_draw_margin_by_hand():
+    # q = p on row 0, so the draft is accepted; the bonus row has cumulative
+    # mass 0.1, 0.3, 0.6, 1.0 and u = 0.35 lands in token 2's interval (0.3, 0.6]:
+    # distance to its nearer boundary 0.05, total mass 1.
+    p0 = [0.1, 0.2, 0.3, 0.4]
+    out = _one_request([p0, [0.1, 0.2, 0.3, 0.4]], p0, token=3, u_acc=0.5, u_draw=0.35)
+    assert out["accept_len"][0] == 1 and list(out["out_tokens"][0]) == [3, 2]
+    assert abs(out["margins"][0, 0] - (0.4 - 0.5 * 0.4)) < 1e-7            # p(x) - u q(x) = 0.2
+    assert np.allclose(out["accept_pq"][0, 0], [0.4, 0.2], atol=1e-7)
+    assert abs(out["margins"][0, 1] - 0.05) < 1e-7
+    assert np.allclose(out["sample_info"][0], [1.0, 0.35, 0.3, 0.6], atol=1e-7)
+
+
+@pytest.mark.parametrize("u_draw,token,margin,before,after", [(0.6, 1, 0.15, 0.0, 0.3), (0.9, 3, 0.1, 0.3, 0.4)])
+def test_residual_draw_margin_by_hand(u_draw, token, margin, before, after):
+    # p = (0.1, 0.4, 0.2, 0.3), q = (0.3, 0.1, 0.4, 0.2): residual (0, 0.3, 0, 0.1),
+    # Z = 0.4.  Draft token 0 with u = 0.9: 0.9 * 0.3 = 0.27 > 0.1, rejected with
+    # margin -0.17.  u_draw = 0.6: threshold 0.24 falls in token 1's interval
+    # (0, 0.3], margin min(0.24, 0.06) / 0.4 = 0.15; u_draw = 0.9: threshold 0.36
+    # in token 3's interval (0.3, 0.4], margin min(0.06, 0.04) / 0.4 = 0.1.
+    p = [0.1, 0.4, 0.2, 0.3]
+    q = [0.3, 0.1, 0.4, 0.2]
+    out = _one_request([p, p], q, token=0, u_acc=0.9, u_draw=u_draw)
+    assert out["accept_len"][0] == 0 and list(out["out_tokens"][0]) == [token, -1]
+    assert abs(out["margins"][0, 0] - (-0.17)) < 1e-7
+    assert np.allclose(out["accept_pq"][0, 0], [0.1, 0.27], atol=1e-7)
+    assert abs(out["margins"][0, 1] - margin) < 1e-6
+    assert np.allclose(out["sample_info"][0], [0.4, 0.4 * u_draw, before, after], atol=1e-7)
+
+
+def test_zero_residual_falls_back_to_the_target_row():
+    # p == q exactly with the draft on a token of zero mass: the test 0 < 0
+    # fails, so the draft is rejected although Z = sum [p - q]_+ = 0.  The draw
+    # then comes from p itself (total mass 1): u = 0.25 in token 1's interval
+    # (0.1, 0.3], margin min(0.15, 0.05) = 0.05.
+    p = [0.1, 0.2, 0.7, 0.0]
+    out = _one_request([p, [0.25, 0.25, 0.25, 0.25]], p, token=3, u_acc=0.5, u_draw=0.25)
+    assert out["accept_len"][0] == 0 and list(out["out_tokens"][0]) == [1, -1]
+    assert out["margins"][0, 0] == 0.0
+    assert abs(out["margins"][0, 1] - 0.05) < 1e-7
+    assert np.allclose(out["sample_info"][0], [1.0, 0.25, 0.1, 0.3], atol=1e-7)
