@@ -128,6 +128,54 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError("logits must be bfloat16 or float32")
 
 
+def _arg(t: Optional[torch.Tensor], name: str, dtype, shape=None, min_rows=None, row_len=None,
+         optional: bool = False) -> None:
+    """Host-side check of one tensor argument before its pointer reaches the
+    library (the C ABI sees raw pointers and cannot check sizes itself):
+    dtype, exact shape, or at least ``min_rows`` leading rows of ``row_len``
+    entries each."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    dts = dtype if isinstance(dtype, tuple) else (dtype,)
+    if t.dtype not in dts:
+        raise TypeError(f"{name} must be {' or '.join(str(d) for d in dts)}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if min_rows is not None:
+        if row_len is None:
+            if t.dim() != 1 or t.shape[0] < min_rows:
+                raise ValueError(f"{name} must be 1-D with at least {min_rows} entries, got {tuple(t.shape)}")
+        elif t.dim() != 2 or t.shape[0] < min_rows or t.shape[1] != row_len:
+            raise ValueError(f"{name} must be [>= {min_rows}, {row_len}], got {tuple(t.shape)}")
+
+
+def _logits(t: torch.Tensor, name: str, ndim: int) -> None:
+    if t is None:
+        raise ValueError(f"{name} is required")
+    _dtype_code(t)
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must be {ndim}-D, got {tuple(t.shape)}")
+
+
+def _check_outputs(B: int, k: int, V: int, ldtype, n_rows: int, accept_len=None, out_tokens=None, margins=None,
+                   row_offsets=None, loss_ce=None, loss_rkl=None, grad=None, status=None, ws=None,
+                   verify: bool = True) -> None:
+    if verify:
+        _arg(accept_len, "accept_len", torch.int32, (B,))
+        _arg(out_tokens, "out_tokens", torch.int32, (B, k + 1))
+        _arg(margins, "margins", torch.float32, (B, k + 1), optional=True)
+    _arg(row_offsets, "row_offsets", torch.int32, (B + 1,))
+    _arg(loss_ce, "loss_ce", torch.float32, min_rows=n_rows, optional=True)
+    _arg(loss_rkl, "loss_rkl", torch.float32, min_rows=n_rows, optional=True)
+    _arg(grad, "grad_draft", ldtype, min_rows=n_rows, row_len=V, optional=True)
+    if status is not None:
+        _arg(status, "status", torch.int32, min_rows=1)
+    if ws is not None and ws.dtype != torch.uint8:
+        raise TypeError("the workspace must be a uint8 tensor (its size is counted in bytes)")
+
+
 def _stream(stream) -> int:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -169,23 +217,37 @@ def adaflash_verify(target, draft, tokens, verify_len, uniforms, T, accept_len, 
                     clip_c, lam, row_offsets, loss_ce, loss_rkl, grad_draft, status, ws,
                     stream=None) -> None:
     """Direct binding of adaflash_verify (see include/adaflash.h)."""
+    _logits(target, "target", 3)
     B, k1, V = target.shape
+    k = k1 - 1
+    opd = loss_ce is not None or loss_rkl is not None or grad_draft is not None
+    _arg(draft, "draft", target.dtype, (B, k, V), optional=(T == 0 and not opd))
+    _arg(tokens, "tokens", torch.int32, (B, k))
+    _arg(verify_len, "verify_len", torch.int32, (B,))
+    _arg(uniforms, "uniforms", torch.float32, (B, k + 1), optional=(T == 0))
+    _check_outputs(B, k, V, target.dtype, B * k, accept_len, out_tokens, margins, row_offsets, loss_ce, loss_rkl,
+                   grad_draft, status, ws)
     rc = load_library().adaflash_verify(
         _dtype_code(target), _ptr(target), _ptr(draft), _ptr(tokens), _ptr(verify_len), _ptr(uniforms),
         B, k1 - 1, V, float(T), _ptr(accept_len), _ptr(out_tokens), _ptr(margins), float(clip_c),
         float(lam), _ptr(row_offsets), _ptr(loss_ce), _ptr(loss_rkl), _ptr(grad_draft), _ptr(status),
-        _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream))
+        _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
     _check(rc)
 
 
 def adaflash_opd_loss_fwd_bwd(target, draft, verify_len, clip_c, lam, row_offsets, loss_ce,
                               loss_rkl, grad_draft, status, ws, stream=None) -> None:
     """Direct binding of adaflash_opd_loss_fwd_bwd (see include/adaflash.h)."""
+    _logits(target, "target", 3)
     B, k1, V = target.shape
+    _arg(draft, "draft", target.dtype, (B, k1 - 1, V))
+    _arg(verify_len, "verify_len", torch.int32, (B,), optional=True)
+    _check_outputs(B, k1 - 1, V, target.dtype, B * (k1 - 1), row_offsets=row_offsets, loss_ce=loss_ce,
+                   loss_rkl=loss_rkl, grad=grad_draft, status=status, ws=ws, verify=False)
     rc = load_library().adaflash_opd_loss_fwd_bwd(
         _dtype_code(target), _ptr(target), _ptr(draft), _ptr(verify_len), B, k1 - 1, V, float(clip_c),
         float(lam), _ptr(row_offsets), _ptr(loss_ce), _ptr(loss_rkl), _ptr(grad_draft), _ptr(status),
-        _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream))
+        _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
     _check(rc)
 
 
@@ -193,14 +255,34 @@ def adaflash_verify_packed(target, draft, tokens, verify_len, uniforms, T, accep
                            clip_c, lam, row_offsets, loss_ce, loss_rkl, grad_draft, status, ws,
                            stream=None) -> None:
     """Direct binding of adaflash_verify_packed: target [sum(L_b+1), V], draft
-    [sum L_b, V]; B and k come from tokens [B, k]."""
+    [sum L_b, V]; B and k come from tokens [B, k].  The row counts must match
+    the device-side verify lengths (sum(L_b + 1) and sum L_b rows): the library
+    locates rows through them."""
+    _logits(target, "target", 2)
+    _arg(tokens, "tokens", torch.int32)
+    if tokens.dim() != 2:
+        raise ValueError(f"tokens must be [B, k], got {tuple(tokens.shape)}")
     B, k = tokens.shape
     V = target.shape[-1]
+    opd = loss_ce is not None or loss_rkl is not None or grad_draft is not None
+    _arg(draft, "draft", target.dtype, optional=(T == 0 and not opd))
+    n_rows = target.shape[0] - B
+    if draft is not None:
+        if draft.dim() != 2 or draft.shape[1] != V or draft.shape[0] + B != target.shape[0]:
+            raise ValueError(f"packed draft must be [sum L_b, V] with sum L_b = target rows - B, got "
+                             f"{tuple(draft.shape)} for target {tuple(target.shape)} and B = {B}")
+        n_rows = draft.shape[0]
+    if target.shape[0] < 2 * B or target.shape[0] > B * (k + 1):
+        raise ValueError(f"packed target must hold between 2 B and B (k + 1) rows, got {target.shape[0]}")
+    _arg(verify_len, "verify_len", torch.int32, (B,))
+    _arg(uniforms, "uniforms", torch.float32, (B, k + 1), optional=(T == 0))
+    _check_outputs(B, k, V, target.dtype, n_rows, accept_len, out_tokens, margins, row_offsets, loss_ce, loss_rkl,
+                   grad_draft, status, ws)
     rc = load_library().adaflash_verify_packed(
         _dtype_code(target), _ptr(target), _ptr(draft), _ptr(tokens), _ptr(verify_len), _ptr(uniforms),
         B, k, V, float(T), _ptr(accept_len), _ptr(out_tokens), _ptr(margins), float(clip_c),
         float(lam), _ptr(row_offsets), _ptr(loss_ce), _ptr(loss_rkl), _ptr(grad_draft), _ptr(status),
-        _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream))
+        _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
     _check(rc)
 
 
@@ -208,12 +290,23 @@ def adaflash_opd_loss_fwd_bwd_packed(target, draft, verify_len, k, clip_c, lam, 
                                      loss_rkl, grad_draft, status, ws, stream=None) -> None:
     """Direct binding of adaflash_opd_loss_fwd_bwd_packed: target
     [sum(L_b+1), V], draft [sum L_b, V]; B from verify_len [B]."""
+    _logits(target, "target", 2)
+    _arg(verify_len, "verify_len", torch.int32)
+    if verify_len.dim() != 1:
+        raise ValueError(f"verify_len must be [B], got {tuple(verify_len.shape)}")
     B = verify_len.shape[0]
     V = target.shape[-1]
+    _logits(draft, "draft", 2)
+    _arg(draft, "draft", target.dtype)
+    if draft.shape[1] != V or draft.shape[0] + B != target.shape[0] or draft.shape[0] > B * int(k):
+        raise ValueError(f"packed draft must be [sum L_b, V] with sum L_b = target rows - B <= B k, got "
+                         f"{tuple(draft.shape)} for target {tuple(target.shape)}, B = {B}, k = {k}")
+    _check_outputs(B, int(k), V, target.dtype, draft.shape[0], row_offsets=row_offsets, loss_ce=loss_ce,
+                   loss_rkl=loss_rkl, grad=grad_draft, status=status, ws=ws, verify=False)
     rc = load_library().adaflash_opd_loss_fwd_bwd_packed(
         _dtype_code(target), _ptr(target), _ptr(draft), _ptr(verify_len), B, int(k), V, float(clip_c),
         float(lam), _ptr(row_offsets), _ptr(loss_ce), _ptr(loss_rkl), _ptr(grad_draft), _ptr(status),
-        _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream))
+        _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
     _check(rc)
 
 
@@ -328,12 +421,17 @@ LOSS_VARIANTS = {"rkl": 1, "rkl_clip": 2, "mixture": 3, "fkl": 4, "wce": 5}
 def adaflash_loss_variant_fwd_bwd(target, draft, verify_len, variant, p1, p2, row_offsets, loss, grad_draft, status,
                                   ws, stream=None) -> None:
     """Direct binding of adaflash_loss_variant_fwd_bwd (see include/adaflash.h)."""
+    _logits(target, "target", 3)
     B, k1, V = target.shape
+    _arg(draft, "draft", target.dtype, (B, k1 - 1, V))
+    _arg(verify_len, "verify_len", torch.int32, (B,), optional=True)
+    _check_outputs(B, k1 - 1, V, target.dtype, B * (k1 - 1), row_offsets=row_offsets, loss_ce=loss, grad=grad_draft,
+                   status=status, ws=ws, verify=False)
     code = LOSS_VARIANTS[variant] if isinstance(variant, str) else int(variant)
     rc = load_library().adaflash_loss_variant_fwd_bwd(
         _dtype_code(target), _ptr(target), _ptr(draft), _ptr(verify_len), B, k1 - 1, V, code, float(p1),
         float(p2), _ptr(row_offsets), _ptr(loss), _ptr(grad_draft), _ptr(status), _ptr(ws),
-        ws.numel() if ws is not None else 0, _stream(stream))
+        ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
     _check(rc)
 
 
@@ -392,7 +490,7 @@ def adaflash_length_head_forward(hidden, W1, b1, w2, b2, gamma, a_hat, k_hat, ws
     lib = load_library()
     head = (_ptr(_bf16(hidden)), _ptr(_bf16(W1)), _ptr(_f32(b1)), _ptr(_f32(w2)), float(b2), B, k, H, Hp,
             float(gamma), _ptr(a_hat), _ptr(k_hat))
-    tail = (_ptr(ws), ws.numel() if ws is not None else 0, _stream(stream))
+    tail = (_ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
     if z1_cache is None:
         rc = lib.adaflash_length_head_forward(*head, *tail)
     else:
@@ -409,7 +507,7 @@ def adaflash_length_head_backward(hidden, W1, b1, w2, b2, accept_len, verify_len
     lib = load_library()
     head = (_ptr(_bf16(hidden)), _ptr(_bf16(W1)), _ptr(_f32(b1)), _ptr(_f32(w2)), float(b2), B, k, H, Hp,
             _ptr(accept_len), _ptr(verify_len), _ptr(loss), _ptr(dW1), _ptr(db1), _ptr(dw2), _ptr(db2))
-    tail = (_ptr(ws), ws.numel() if ws is not None else 0, _stream(stream))
+    tail = (_ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
     if z1_cache is None:
         rc = lib.adaflash_length_head_backward(*head, *tail)
     else:

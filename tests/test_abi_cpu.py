@@ -212,3 +212,90 @@ def test_timing_hook_argument_checks(lib):
     assert lib.adaflash_timing_enable(0) == 0  # disabling creates nothing
     assert lib.adaflash_timing_read(None, 4) == -1
     assert lib.adaflash_timing_read(None, 0) == 0  # nothing recorded
+
+
+# ---------------------------------------------- binding argument checks
+
+def _good_verify_args(B=3, k=4, V=64, dt=None):
+    import torch
+    dt = dt or torch.bfloat16
+    return dict(target=torch.zeros(B, k + 1, V, dtype=dt), draft=torch.zeros(B, k, V, dtype=dt),
+                tokens=torch.zeros(B, k, dtype=torch.int32), verify_len=torch.ones(B, dtype=torch.int32),
+                uniforms=torch.zeros(B, k + 1), T=1.0, accept_len=torch.zeros(B, dtype=torch.int32),
+                out_tokens=torch.zeros(B, k + 1, dtype=torch.int32), margins=torch.zeros(B, k + 1),
+                clip_c=10.0, lam=1.0, row_offsets=torch.zeros(B + 1, dtype=torch.int32),
+                loss_ce=torch.zeros(B * k), loss_rkl=torch.zeros(B * k),
+                grad_draft=torch.zeros(B * k, V, dtype=dt), status=torch.zeros(1, dtype=torch.int32),
+                ws=torch.zeros(16, dtype=torch.uint8))
+
+
+@pytest.mark.parametrize("name,bad,exc,what", [
+    ("tokens", lambda a: a["tokens"].long(), TypeError, "tokens"),
+    ("verify_len", lambda a: a["verify_len"].long(), TypeError, "verify_len"),
+    ("uniforms", lambda a: a["uniforms"][:, :-1].contiguous(), ValueError, "uniforms"),
+    ("uniforms", lambda a: a["uniforms"].double(), TypeError, "uniforms"),
+    ("draft", lambda a: a["draft"][:, :-1].contiguous(), ValueError, "draft"),
+    ("draft", lambda a: a["draft"].float(), TypeError, "draft"),
+    ("draft", lambda a: None, ValueError, "draft"),
+    ("grad_draft", lambda a: a["grad_draft"][:-1].contiguous(), ValueError, "grad_draft"),
+    ("grad_draft", lambda a: a["grad_draft"].float(), TypeError, "grad_draft"),
+    ("loss_ce", lambda a: a["loss_ce"][:-1].contiguous(), ValueError, "loss_ce"),
+    ("out_tokens", lambda a: a["out_tokens"][:, :-1].contiguous(), ValueError, "out_tokens"),
+    ("accept_len", lambda a: a["accept_len"].float(), TypeError, "accept_len"),
+    ("row_offsets", lambda a: a["row_offsets"][:-1].contiguous(), ValueError, "row_offsets"),
+    ("margins", lambda a: a["margins"].half(), TypeError, "margins"),
+    ("status", lambda a: a["status"].long(), TypeError, "status"),
+    ("ws", lambda a: a["ws"].float(), TypeError, "workspace"),
+])
+def test_binding_rejects_mismatched_tensors(lib, name, bad, exc, what):
+    """Every tensor's dtype and shape is checked on the host before the
+    library sees a pointer (a short buffer would otherwise be overrun on the
+    device).  The tensors are CPU tensors: the check must fire before the
+    binding asks for device pointers."""
+    import diffusion_drafter_verification_amd as ada
+    a = _good_verify_args()
+    a[name] = bad(a)
+    with pytest.raises(exc, match=what):
+        ada.adaflash_verify(**a)
+
+
+def test_binding_accepts_well_formed_tensors_up_to_the_device_check(lib):
+    """With every dtype and shape right, the only complaint about CPU tensors
+    is that they are not on the GPU."""
+    import diffusion_drafter_verification_amd as ada
+    with pytest.raises(ValueError, match="GPU tensors only"):
+        ada.adaflash_verify(**_good_verify_args())
+    a = _good_verify_args()
+    a.update(T=0.0, draft=None, uniforms=None, loss_ce=None, loss_rkl=None, grad_draft=None)
+    with pytest.raises(ValueError, match="GPU tensors only"):
+        ada.adaflash_verify(**a)
+
+
+def test_opd_and_variant_bindings_check_tensors(lib):
+    import torch
+    import diffusion_drafter_verification_amd as ada
+    B, k, V = 2, 3, 32
+    t = torch.zeros(B, k + 1, V, dtype=torch.bfloat16)
+    d = torch.zeros(B, k, V, dtype=torch.bfloat16)
+    ro = torch.zeros(B + 1, dtype=torch.int32)
+    ce = torch.zeros(B * k)
+    g = torch.zeros(B * k, V, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="draft"):
+        ada.adaflash_opd_loss_fwd_bwd(t, d[:, :2].contiguous(), None, 10.0, 1.0, ro, ce, ce, g, None, None)
+    with pytest.raises(TypeError, match="verify_len"):
+        ada.adaflash_opd_loss_fwd_bwd(t, d, torch.ones(B, dtype=torch.int64), 10.0, 1.0, ro, ce, ce, g, None, None)
+    with pytest.raises(ValueError, match="grad_draft"):
+        ada.adaflash_opd_loss_fwd_bwd(t, d, None, 10.0, 1.0, ro, ce, ce, g[:, :V - 1].contiguous(), None, None)
+    with pytest.raises(ValueError, match="loss_ce"):
+        ada.adaflash_loss_variant_fwd_bwd(t, d, None, "rkl", 0.0, 0.0, ro, ce[:2].contiguous(), g, None, None)
+    # packed forms: the draft must hold target rows - B rows
+    tp = torch.zeros(7, V, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="packed draft"):
+        ada.adaflash_opd_loss_fwd_bwd_packed(tp, torch.zeros(4, V, dtype=torch.bfloat16),
+                                             torch.ones(B, dtype=torch.int32), k, 10.0, 1.0, ro, ce, ce, g, None,
+                                             None)
+    a = _good_verify_args(B, k, V)
+    a["target"] = torch.zeros(B * 2 + 1, V, dtype=torch.bfloat16)
+    a["draft"] = torch.zeros(B + 2, V, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="packed draft"):
+        ada.adaflash_verify_packed(**a)
