@@ -97,6 +97,17 @@ struct KParams {
 // ---------------------------------------------------------------- primitives
 
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// A product rounded on its own, never fused into a following addition.  The
+// residual max(0, p - q) is a difference of two such products: when the target
+// and draft rows are identical both round to the same value and the residual is
+// exactly zero (no rejection can occur then, except on a zero-mass draft token,
+// and the draw falls back to the target row).  A contracted fma(p', s, -q)
+// would leave rounding noise there instead.
+__device__ __forceinline__ float mul_rn(float a, float b) {
+#pragma clang fp contract(off)
+  return a * b;
+}
 __device__ __forceinline__ float flog2(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
@@ -826,8 +837,8 @@ __device__ void finalize_request(const KParams& P, int b, FinShared& fs) {
         const float zp = cp.get(e);
         float mass;
         if (resid) {
-          const float pv = fexp2(fmaf(zp, P.kT, ap)) * invSp;
-          const float qv = fexp2(fmaf(cq.get(e), P.kT, aq)) * invSq;
+          const float pv = mul_rn(fexp2(fmaf(zp, P.kT, ap)), invSp);
+          const float qv = mul_rn(fexp2(fmaf(cq.get(e), P.kT, aq)), invSq);
           mass = fmaxf(0.f, pv - qv);
         } else {
           mass = zp == neg_inf() ? 0.f : fexp2(fmaf(zp, P.kT, ap)) * invSp;
@@ -1080,8 +1091,8 @@ __global__ __launch_bounds__(kThreads) void row_kernel(KParams P) {
           const float ap = -st.Mp * P.kT, aq = -st.Mq * P.kT;
 #pragma unroll
           for (int e = 0; e < kElems; ++e) {
-            const float pv = fexp2(fmaf(cp.get(e), P.kT, ap)) * invSp;
-            const float qq = fexp2(fmaf(cq.get(e), P.kT, aq)) * invSq;
+            const float pv = mul_rn(fexp2(fmaf(cp.get(e), P.kT, ap)), invSp);
+            const float qq = mul_rn(fexp2(fmaf(cq.get(e), P.kT, aq)), invSq);
             Zpart += fmaxf(0.f, pv - qq);
           }
         }
@@ -2032,8 +2043,8 @@ __global__ __launch_bounds__(kThreads) void vres_kernel(KParams P) {
     if (kResChunks * h + t < G) {
 #pragma unroll
       for (int e = 0; e < kElems; ++e) {
-        const float pv = fexp2(fmaf(cp[t].get(e), P.kT, ap)) * invSp;
-        const float qq = fexp2(fmaf(cq[t].get(e), P.kT, aq)) * invSq;
+        const float pv = mul_rn(fexp2(fmaf(cp[t].get(e), P.kT, ap)), invSp);
+        const float qq = mul_rn(fexp2(fmaf(cq[t].get(e), P.kT, aq)), invSq);
         z[t] += fmaxf(0.f, pv - qq);
       }
     }
