@@ -1786,6 +1786,403 @@ __global__ __launch_bounds__(kThreads, (sup_min_waves<BF16, ALIGNED, VMODE, FKL>
   }
 }
 
+// -------------------------------- supervision kernel for bf16 rows (V % 8 == 0)
+//
+// The passes of sup_kernel with less work per entry, for bf16 rows whose
+// length is a multiple of eight and whose base pointers are 16-byte aligned:
+//  * each thread shifts its exponentials by its own maxima, so pass 1 needs no
+//    workgroup reduction before it starts; the thread partials are rescaled
+//    once, when the waves merge them;
+//  * the thread maxima come from packed f16 maxima of the raw bf16 patterns,
+//    three words per instruction (a bf16 pattern read as f16 orders like the
+//    bf16 value unless the f16 reading is a NaN, which only -inf, +inf and
+//    |z| >= 2^121 produce; threads holding such an entry take the exact
+//    integer method);
+//  * the padding past V is -2^120, a bf16 pattern that is finite as f16;
+//  * a bonus row whose request already has a rejected draft is not loaded
+//    (the finaliser reads row L only when every draft is accepted).
+
+constexpr uint32_t kPadBf16x2 = 0xFB80FB80u;  // -2^120 in both halves
+
+// Chunk of a bf16 row with V % 8 == 0: whole slots of eight entries are inside
+// or past the row; slots past it hold the padding value.
+__device__ __forceinline__ void load_chunk_bf16(Chunk<true>& c, const void* row, int v0, int V) {
+  constexpr int NV = kElems / 8;
+  if (v0 + kChunk <= V) {
+    const __amdgpu_buffer_rsrc_t rs = row_rsrc(row, V * 2);
+    const int toff = (int)threadIdx.x * 16;
+#pragma unroll
+    for (int s = 0; s < NV; ++s) {
+      const auto q = __builtin_amdgcn_raw_buffer_load_b128(rs, toff, (v0 + s * (kThreads * 8)) * 2, kStreamPolicy);
+      c.w[s * 4 + 0] = q[0];
+      c.w[s * 4 + 1] = q[1];
+      c.w[s * 4 + 2] = q[2];
+      c.w[s * 4 + 3] = q[3];
+    }
+    return;
+  }
+#pragma unroll
+  for (int s = 0; s < NV; ++s) {
+    const int idx0 = v0 + s * (kThreads * 8) + (int)threadIdx.x * 8;
+    uint4 q = make_uint4(kPadBf16x2, kPadBf16x2, kPadBf16x2, kPadBf16x2);
+    if (idx0 < V) q = *(const uint4*)((const uint16_t*)row + idx0);
+    c.w[s * 4 + 0] = q.x;
+    c.w[s * 4 + 1] = q.y;
+    c.w[s * 4 + 2] = q.z;
+    c.w[s * 4 + 3] = q.w;
+  }
+}
+
+// Largest of the thread's 32 entries (exact).  Packed f16 maxima of the raw
+// patterns; a NaN result means some pattern is an f16 NaN, and the signed
+// 16-bit integer method (chunk_max) decides instead.
+__device__ __forceinline__ float thread_max_bf16(const Chunk<true>& c) {
+  f16x2_t m = __builtin_bit_cast(f16x2_t, c.w[0]);
+#pragma unroll
+  for (int q = 1; q < Chunk<true>::NW; ++q) m = __builtin_elementwise_maximum(m, __builtin_bit_cast(f16x2_t, c.w[q]));
+  const _Float16 h = __builtin_elementwise_maximum(m.x, m.y);
+  if (__builtin_isnan(h)) return chunk_max<true>(c);
+  return __uint_as_float((uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
+}
+
+template <int VMODE, bool FKL = false>
+__global__ __launch_bounds__(kThreads, 8) void fsup_kernel(KParams P) {
+  static_assert(VMODE == 0 || VMODE == 2, "opd only, or fused with sampled verification at T = 1");
+  constexpr bool SAMPLED = VMODE == 2, VERIFY = VMODE != 0;
+  constexpr int VEC = 8;
+  constexpr int NV = kElems / VEC;
+  __shared__ FinShared fs;
+  __shared__ int sh_ok;
+  // exp(z_q - m) of this thread's draft entries from pass 1 (m: the thread's
+  // maximum), as fp16 pairs, slot-major; each thread reads only what it wrote.
+  __shared__ uint32_t ecache[kElems / 2 * kThreads];
+  __shared__ float wpart[kWaves][6];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int G = P.G;
+  const int k = P.k, V = P.V;
+  const int s_ = (int)blockIdx.x / G;
+  const int j = (int)blockIdx.x - s_ * G;
+  const RowSlot sl = row_slot(P, s_, VERIFY);
+  if (sl.b < 0) return;
+  const int b = sl.b, i = sl.i;
+  const int r = b * (k + 1) + i;
+  const bool draft_row = sl.n >= 0;
+  const int v0 = j * kChunk;
+
+  if (VERIFY && !draft_row) {
+    // Bonus row: skip it when a draft of the request is already known to be
+    // rejected (flags of rows still undecided read "unknown", 2).
+    if (wave == 0) {
+      const bool rej = lane < i && pub_load(P.rowrec + (size_t)(r - i + lane) * kRowRec + 1) == 0.f;
+      const unsigned long long any = __ballot(rej);
+      if (lane == 0) fs.i[1] = any != 0ull;
+    }
+    __syncthreads();
+    if (fs.i[1]) return;
+  }
+
+  const void* trow = target_row_ptr<true>(P, b, i, sl.n);
+  const void* drow = nullptr;
+  if (draft_row) drow = draft_row_ptr<true>(P, b, i, sl.n);
+
+  // ---- pass 1
+  Chunk<true> cp, cq;
+  load_chunk_bf16(cp, trow, v0, V);
+  if (draft_row) load_chunk_bf16(cq, drow, v0, V);
+  int xtok = 0, n = 0;
+  float u_acc = 0.f, zpx = 0.f, zqx = 0.f;
+  if (draft_row) {
+    n = sl.n;
+    if constexpr (SAMPLED) {
+      xtok = (int)sload_u32(P.tokens + (size_t)b * k + i);
+      if (xtok < 0 || xtok >= V) {
+        if (tid == 0 && j == 0) flag(P.status, ADAFLASH_FLAG_BAD_TOKEN);
+        xtok = xtok < 0 ? 0 : V - 1;
+      }
+      u_acc = __uint_as_float(sload_u32(P.uniforms + (size_t)b * (k + 1) + i));
+      zpx = sload_logit<true>(trow, xtok);
+      zqx = sload_logit<true>(drow, xtok);
+    }
+  }
+  const float mp = thread_max_bf16(cp);
+  const float mq = draft_row ? thread_max_bf16(cq) : neg_inf();
+  cp.opaque();
+  cq.opaque();
+  const float ap = mp == neg_inf() ? 0.f : -mp * kLog2e;
+  const float aq = mq == neg_inf() ? 0.f : -mq * kLog2e;
+  float sp = 0.f, sq = 0.f, W = 0.f, Amax = neg_inf(), Wp = 0.f;
+  if (draft_row) {
+#pragma unroll
+    for (int s2 = 0; s2 < NV; ++s2) {
+      uint32_t hw[VEC / 2];
+#pragma unroll
+      for (int u = 0; u < VEC; u += 2) {
+        float ee2[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int e = s2 * VEC + u + t;
+          const float zq = cq.get(e), zp = cp.get(e);
+          const float ee = fexp2(fmaf(zq, kLog2e, aq));
+          const float ep = fexp2(fmaf(zp, kLog2e, ap));
+          sp += ep;
+          if constexpr (FKL) Wp = fmaf(ep, zq - zp, Wp);
+          sq += ee;
+          const float pr = ee * (zq - zp);
+          W += pr;
+          Amax = fmaxf(Amax, pr);
+          ee2[t] = ee;
+        }
+        hw[u / 2] = pack_f16x2(ee2[0], ee2[1]);
+      }
+      *(uint4*)(ecache + ((size_t)s2 * kThreads + tid) * 4) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    }
+  } else if (SAMPLED) {
+#pragma unroll
+    for (int e = 0; e < kElems; ++e) sp += fexp2(fmaf(cp.get(e), kLog2e, ap));
+  }
+  {
+    // Thread partials to the wave's maxima, reduced inside each wave; thread 0
+    // merges the four waves and publishes the chunk record.  Padding entries
+    // (and whole padded threads or waves) vanish in the rescaling, since the
+    // chunk holds at least one entry of the row.
+    const float Mpw = wave_reduce<OP_MAX>(mp);
+    const float Mqw = wave_reduce<OP_MAX>(mq);
+    const float fp = mp == neg_inf() ? 0.f : fexp2((mp - Mpw) * kLog2e);
+    const float fq = mq == neg_inf() ? 0.f : fexp2((mq - Mqw) * kLog2e);
+    float v0s = wave_reduce_l63<OP_SUM>(sp * fp);
+    float v1s = wave_reduce_l63<OP_SUM>(sq * fq);
+    float v2s = wave_reduce_l63<OP_SUM>(W * fq);
+    float v3s = wave_reduce_l63<OP_MAX>(Amax * fq);
+    float v4s = FKL ? wave_reduce_l63<OP_SUM>(Wp * fp) : 0.f;
+    if (lane == 63) {
+      wpart[wave][0] = Mpw;
+      wpart[wave][1] = Mqw;
+      wpart[wave][2] = v0s;
+      wpart[wave][3] = v1s;
+      wpart[wave][4] = v2s;
+      wpart[wave][5] = FKL ? v4s : v3s;
+      if (FKL) fs.f[15 - wave] = v3s;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      float Mp = wpart[0][0], Mq = wpart[0][1];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) {
+        Mp = fmaxf(Mp, wpart[w][0]);
+        Mq = fmaxf(Mq, wpart[w][1]);
+      }
+      float Sp = 0.f, Sq = 0.f, Ws = 0.f, As = neg_inf(), Wps = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float gp = wpart[w][0] == neg_inf() ? 0.f : fexp2((wpart[w][0] - Mp) * kLog2e);
+        const float gq = wpart[w][1] == neg_inf() ? 0.f : fexp2((wpart[w][1] - Mq) * kLog2e);
+        Sp += wpart[w][2] * gp;
+        Sq += wpart[w][3] * gq;
+        Ws += wpart[w][4] * gq;
+        const float aw = FKL ? fs.f[15 - w] : wpart[w][5];
+        As = fmaxf(As, aw * gq);
+        if (FKL) Wps += wpart[w][5] * gp;
+      }
+      float* rec = P.part1 + ((size_t)r * G + j) * kRec1;
+      pub_store(rec + 0, Mp);
+      pub_store(rec + 2, Sp);
+      pub_store(rec + 3, Ws);
+      pub_store(rec + 4, Mq);
+      pub_store(rec + 5, Sq);
+      pub_store(rec + 6, As);
+      if (FKL) pub_store(rec + 7, Wps);
+    }
+  }
+  if (!draft_row) return;
+
+  bool alive = arrive_and_wait(&P.rowcnt[(size_t)r * kCounterStride], G, P.status, &sh_ok);
+  if (!alive) return;
+  if (SAMPLED && wave == 1) {
+    const int l = tid - 64;
+    const bool rej = l < i && pub_load(P.rowrec + (size_t)(r - i + l) * kRowRec + 1) == 0.f;
+    const unsigned long long any = __ballot(rej);
+    if (l == 0) fs.i[0] = any != 0ull;
+  }
+  const SupStats st = combine_sup<SAMPLED, true, FKL>(P, r, fs, zpx, zqx, u_acc);
+  const bool earlier_rejected = SAMPLED && fs.i[0] != 0;
+  const float lse_q2 = st.lse_q2, lse_p2 = st.lse_p2, D = st.D, KL = st.KL;
+  const float wi = P.wdecay > 0.f ? uniform(fexp2(-(float)i * kLog2e / P.wdecay)) : 1.f;
+  const float c = P.clip_c, lam = uniform(wi * P.lambda), ace = uniform(wi * P.a_ce);
+  const float afk = FKL ? wi : 0.f;
+  const bool fast = !st.nonfinite && st.bound <= 0.999f * c;
+  const float pad = __uint_as_float(kPadBf16x2 & 0xffff0000u);
+  if (tid == 0 && j == 0 && !(st.Mp < __builtin_inff() && st.Mp > pad && st.Sp > 0.f && st.Sq > 0.f))
+    flag(P.status, ADAFLASH_FLAG_NONFINITE);
+
+  bool accept = true;
+  if constexpr (SAMPLED) {
+    accept = st.margin > 0.f;
+    if (tid == 0 && j == 0) {
+      pub_store(P.rowrec + (size_t)r * kRowRec + 1, accept ? 1.f : 0.f);
+      pub_store(P.rowrec + (size_t)r * kRowRec + 2, st.margin);
+      if (P.margins) P.margins[(size_t)b * (k + 1) + i] = st.margin;
+    }
+  }
+
+  // st.xstar is the lowest chunk whose maximum is the row maximum; that chunk
+  // finds the lowest index holding it.
+  int xs = kIntMax;
+  if (j == st.xstar) {
+    int ce = kIntMax;
+#pragma unroll
+    for (int e = kElems - 1; e >= 0; --e)
+      if (cp.get(e) == st.Mp) ce = e;
+    int cidx = ce == kIntMax ? kIntMax : entry_index<true>(v0, ce);
+    if (cidx >= V) cidx = kIntMax;
+    float x1[1] = {__int_as_float(cidx)};
+    const int o1[1] = {OP_MINI};
+    wg_reduce<1>(x1, o1, fs.red);
+    xs = __float_as_int(x1[0]);
+  }
+  cp.opaque();
+  cq.opaque();
+  const int xo = xs - v0;
+  const bool xs_here = xs < V && xo >= 0 && xo < kChunk && ((xo % (kThreads * VEC)) / VEC) == tid;
+  const float zqs = xs >= 0 && xs < V ? sload_logit<true>(drow, xs) : 0.f;
+
+  const bool need_res = SAMPLED && !accept && !earlier_rejected;
+  float Zpart = 0.f;
+  const bool whole = v0 + kChunk <= V;
+  auto store_slot = [&](int s2, const float (&g)[VEC]) {
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    const u32x4_t o = {pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]), pack_bf16x2(g[4], g[5]),
+                       pack_bf16x2(g[6], g[7])};
+    if (whole) {
+      const __amdgpu_buffer_rsrc_t rs = row_rsrc((const uint16_t*)P.grad + (size_t)n * V, V * 2);
+      __builtin_amdgcn_raw_buffer_store_b128(o, rs, tid * 16, (v0 + s2 * (kThreads * VEC)) * 2, kStreamPolicy);
+    } else {
+      const int idx0 = v0 + s2 * (kThreads * VEC) + tid * VEC;
+      if (idx0 < V) *(u32x4_t*)((uint16_t*)P.grad + (size_t)n * V + idx0) = o;
+    }
+  };
+
+  float Rrow = KL;
+  float gstar = 0.f;
+  if (fast) {
+    // g = q (lambda dz + c1), q = e s: e from the cache (this thread's shift),
+    // s = exp(m - lse_q) with m this thread's maximum.
+    const float c1 = FKL ? fmaf(-lam, D, ace - lam * KL) + afk : fmaf(-lam, D, ace - lam * KL);
+    const float sc = mq == neg_inf() ? 0.f : fexp2(-aq - lse_q2);
+    const float lsc = lam * sc, csc = c1 * sc;
+    if (P.grad) {
+#pragma unroll
+      for (int s2 = 0; s2 < NV; ++s2) {
+        const uint4 h4 = *(const uint4*)(ecache + ((size_t)s2 * kThreads + tid) * 4);
+        const uint32_t hw[4] = {h4.x, h4.y, h4.z, h4.w};
+        float dz8[8];
+        bf16_diff8(&cq.w[s2 * 4], &cp.w[s2 * 4], dz8);
+        float g[VEC];
+#pragma unroll
+        for (int u = 0; u < VEC; ++u) {
+          const float pterm = FKL ? -afk * fexp2(fmaf(cp.get(s2 * VEC + u), kLog2e, -lse_p2)) : 0.f;
+          g[u] = fma_f16(hw[u / 2], u & 1, fmaf(lsc, dz8[u], csc), pterm);
+        }
+        store_slot(s2, g);
+      }
+    }
+    if (need_res) {
+#pragma unroll
+      for (int e = 0; e < kElems; ++e) {
+        const float q = fexp2(fmaf(cq.get(e), kLog2e, -lse_q2));
+        Zpart += fmaxf(0.f, fexp2(fmaf(cp.get(e), kLog2e, -lse_p2)) - q);
+      }
+    }
+    if (xs_here) {
+      const float pstar = FKL ? -afk * fexp2(st.Mp * kLog2e - lse_p2) : 0.f;
+      const int xs_slot = xo / (kThreads * VEC), xs_u = xo % VEC;
+      const uint32_t w = ecache[((size_t)xs_slot * kThreads + tid) * 4 + xs_u / 2];
+      gstar = fma_f16(w, xs_u & 1, fmaf(lsc, zqs - st.Mp, csc), pstar) - ace;
+    }
+  } else {
+    // Exact path: clipped sums, second barrier, then the gradient with every
+    // per-entry term recomputed from the packed logits.
+    float Spart = 0.f, Rpart = 0.f;
+#pragma unroll
+    for (int e = 0; e < kElems; ++e) {
+      const float zq = cq.get(e), zp = cp.get(e);
+      const float q = fexp2(fmaf(zq, kLog2e, -lse_q2));
+      if (need_res) Zpart += fmaxf(0.f, fexp2(fmaf(zp, kLog2e, -lse_p2)) - q);
+      const float dd = (zq - zp) - D;
+      const float f = q > 0.f ? q * dd : 0.f;
+      const bool inU = f <= c;
+      Rpart += inU ? f : c;
+      Spart += inU ? f + q : 0.f;
+    }
+    float s3[3] = {Spart, Rpart, Zpart};
+    const int ops3[3] = {OP_SUM, OP_SUM, OP_SUM};
+    wg_reduce<3>(s3, ops3, fs.red);
+    if (tid == 0) {
+      float* rec = P.part2 + ((size_t)r * G + j) * kRec2;
+      pub_store(rec + 0, s3[0]);
+      pub_store(rec + 1, s3[1]);
+      if (SAMPLED) pub_store(rec + 2, s3[2]);
+    }
+    alive = arrive_and_wait(&P.rowcnt[(size_t)r * kCounterStride], 2 * G, P.status, &sh_ok);
+    if (!alive) return;
+    float sr[2] = {0.f, 0.f};
+    if (tid < G) {
+      const float* rec = P.part2 + ((size_t)r * G + tid) * kRec2;
+      sr[0] = pub_load(rec + 0);
+      sr[1] = pub_load(rec + 1);
+    }
+    const int srops[2] = {OP_SUM, OP_SUM};
+    wg_reduce<2>(sr, srops, fs.red);
+    Rrow = sr[1];
+    const float lamS = uniform(lam * sr[0]);
+    cp.opaque();
+    cq.opaque();
+    if (P.grad) {
+#pragma unroll
+      for (int s2 = 0; s2 < NV; ++s2) {
+        // The chunk's words are read again slot by slot (this path is rare),
+        // so that no chunk is held in registers across the second barrier.
+        const int idx0 = v0 + s2 * (kThreads * VEC) + tid * VEC;
+        const uint4 pad4 = make_uint4(kPadBf16x2, kPadBf16x2, kPadBf16x2, kPadBf16x2);
+        const uint4 wp = idx0 < V ? *(const uint4*)((const uint16_t*)trow + idx0) : pad4;
+        const uint4 wq = idx0 < V ? *(const uint4*)((const uint16_t*)drow + idx0) : pad4;
+        cp.w[s2 * 4 + 0] = wp.x;
+        cp.w[s2 * 4 + 1] = wp.y;
+        cp.w[s2 * 4 + 2] = wp.z;
+        cp.w[s2 * 4 + 3] = wp.w;
+        cq.w[s2 * 4 + 0] = wq.x;
+        cq.w[s2 * 4 + 1] = wq.y;
+        cq.w[s2 * 4 + 2] = wq.z;
+        cq.w[s2 * 4 + 3] = wq.w;
+        float g[VEC];
+#pragma unroll
+        for (int u = 0; u < VEC; ++u) {
+          const int e = s2 * VEC + u;
+          g[u] = grad_exact(cq.get(e), cp.get(e), lse_q2, D, lam, lamS, c, ace);
+          if constexpr (FKL) g[u] -= afk * fexp2(fmaf(cp.get(e), kLog2e, -lse_p2));
+          if (u & 1) __builtin_amdgcn_sched_barrier(0);
+        }
+        store_slot(s2, g);
+      }
+    }
+    gstar = grad_exact(zqs, st.Mp, lse_q2, D, lam, lamS, c, ace) - ace;
+    if constexpr (FKL) gstar -= afk * fexp2(st.Mp * kLog2e - lse_p2);
+  }
+  if (fast && need_res) {
+    float z1[1] = {Zpart};
+    const int o1[1] = {OP_SUM};
+    wg_reduce<1>(z1, o1, fs.red);
+    if (tid == 0) pub_store(P.part2 + ((size_t)r * G + j) * kRec2 + 2, z1[0]);
+  }
+  if (xs_here) {
+    if (P.grad) ((uint16_t*)P.grad)[(size_t)n * V + xs] = __builtin_bit_cast(uint16_t, (__bf16)gstar);
+    if (P.loss_ce) P.loss_ce[n] = lse_q2 * kLn2 - zqs;
+    if (P.loss_rkl) P.loss_rkl[n] = Rrow;
+    if (P.loss_var) P.loss_var[n] = wi * (P.a_ce * (lse_q2 * kLn2 - zqs) + P.lambda * Rrow + (FKL ? st.fkl : 0.f));
+  }
+}
+
 // ------------------------------------------ greedy verification (no OPD)
 
 // Greedy verification needs only every target row's maximum and its lowest
@@ -2178,6 +2575,16 @@ hipError_t launch_final(const KParams& p, hipStream_t st) {
 template <bool BF16, bool ALIGNED>
 hipError_t dispatch_mode(const KParams& p, int grid, int opd, int vmode, bool t1, bool fkl, hipStream_t st) {
   hipError_t e;
+  if constexpr (BF16 && ALIGNED) {
+    // bf16 rows of a multiple of eight entries: the lighter supervision kernel.
+    if (opd && (vmode == 0 || (vmode == 2 && t1))) {
+      if (vmode == 0 && fkl) e = launch_dominant(fsup_kernel<0, true>, grid, st, p);
+      else if (vmode == 0) e = launch_dominant(fsup_kernel<0>, grid, st, p);
+      else e = launch_dominant(fsup_kernel<2>, grid, st, p);
+      if (e != hipSuccess || vmode == 0) return e;
+      return launch_final<BF16, ALIGNED, 2>(p, st);
+    }
+  }
   if (opd && vmode == 0 && fkl) e = launch_sup<BF16, ALIGNED, 0, true>(p, grid, st);
   else if (opd && vmode == 0) e = launch_sup<BF16, ALIGNED, 0>(p, grid, st);
   else if (opd && vmode == 1) e = launch_sup<BF16, ALIGNED, 1>(p, grid, st);
