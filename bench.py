@@ -8,12 +8,13 @@ lambda=1; every call verifies the batch and writes per-row losses and the bf16
 gradient with respect to the draft logits.  Inputs are seeded and synthetic
 and resident in HBM before timing starts.
 
-One JSON line is printed: verified draft positions per second over whole
-calls (value), the achieved HBM bandwidth of the dominant kernel against the
-MI355X peak (roofline: algorithmic bytes per call over that kernel's average
-duration, from HIP events the library records around it on the call's
-stream), and the CPU oracle timed on a bounded sample of the same workload
-(cpu_baseline).
+One JSON line is printed: verified draft positions per second over the timed
+steps (value), the achieved HBM bandwidth of the dominant kernel against the
+MI355X peak over the same steps (roofline: algorithmic bytes per call over
+that kernel's average duration, from HIP events the library attaches to its
+dispatch on the call's stream), tau (mean accept length + 1), the CPU oracle
+timed on a bounded sample of the same workload (cpu_baseline) and the parity
+of the GPU's outputs against the oracle's on that sample (parity).
 """
 from __future__ import annotations
 
@@ -109,29 +110,64 @@ def measured_traffic(mode, default_shape=True):
     return rec["traffic_bytes_per_launch"] if rec.get("kernel_source_sha256") == sha else None
 
 
-def cpu_baseline(batch, mode, clip, lam, budget_s):
+def host_threads() -> int:
+    """Threads for the CPU oracle: the CPU share this process may use (its
+    affinity set, capped by OMP_NUM_THREADS when the host sets it: on the GPU
+    boxes each GPU comes with a share of 16 host cores)."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    cap = os.environ.get("OMP_NUM_THREADS")
+    if cap and cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
+
+
+def cpu_description() -> str:
+    """Model name, family/model/stepping and logical CPU count from /proc/cpuinfo."""
+    info = {}
+    count = 0
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ":" not in ln:
+                    continue
+                key, val = (x.strip() for x in ln.split(":", 1))
+                if key == "processor":
+                    count += 1
+                elif key in ("model name", "cpu family", "model", "stepping") and key not in info:
+                    info[key] = val
+    except OSError:
+        return ""
+    return (f"{info.get('model name', '?')} (family {info.get('cpu family', '?')}, model {info.get('model', '?')}, "
+            f"stepping {info.get('stepping', '?')}; {count} logical CPUs visible)")
+
+
+def cpu_baseline(batch, gpu_out, mode, clip, lam, budget_s):
     """The CPU oracle, as it stands, on the first requests of one input set,
-    repeated until about budget_s seconds have elapsed."""
+    repeated until about budget_s seconds have elapsed; its outputs also give
+    the parity report against the GPU's outputs for the same requests."""
     import numpy as np
     import oracle
-    threads = max(1, min(16, os.cpu_count() or 1))
+    threads = host_threads()
     nreq = 8
     t = batch.target[:nreq]
     d = batch.draft[:nreq]
     tok = batch.tokens[:nreq] if batch.tokens is not None else None
     vl = batch.verify_len[:nreq]
     uni = batch.uniforms[:nreq]
-    positions = int(np.clip(vl, 1, t.shape[1] - 1).sum())
+    k = t.shape[1] - 1
+    positions = int(np.clip(vl, 1, k).sum())
+    res = {}
+
     def run(nthreads, budget):
         done = 0
         t0 = time.perf_counter()
         while True:
             if mode == "greedy":
-                oracle.verify(t, None, tok, vl, uni, T=0.0, nthreads=nthreads)
+                res["v"] = oracle.verify(t, None, tok, vl, uni, T=0.0, nthreads=nthreads)
             elif mode != "opd":
-                oracle.verify(t, d, tok, vl, uni, T=1.0, nthreads=nthreads)
+                res["v"] = oracle.verify(t, d, tok, vl, uni, T=1.0, nthreads=nthreads)
             if mode not in ("verify", "greedy"):
-                oracle.opd(t, d, vl, clip, lam, with_grad=True, nthreads=nthreads)
+                res["o"] = oracle.opd(t, d, vl, clip, lam, with_grad=True, nthreads=nthreads)
             done += 1
             el = time.perf_counter() - t0
             if el >= budget:
@@ -139,16 +175,36 @@ def cpu_baseline(batch, mode, clip, lam, budget_s):
 
     done, el = run(threads, budget_s)
     done1, el1 = run(1, budget_s / 3)  # one thread, to show the scaling
-    model = ""
-    try:
-        with open("/proc/cpuinfo") as f:
-            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
-    except OSError:
-        pass
-    return {"value": positions * done / el, "unit": "positions/s", "cores": threads, "kind": "oracle",
-            "sample": f"{nreq} requests ({positions} verified positions) of input set 0, "
-                      f"{done} repetitions in {el:.1f} s, {threads} threads",
-            "value_1_thread": positions * done1 / el1, "cpu_model": model}
+    out = {"value": positions * done / el, "unit": "positions/s", "cores": threads, "kind": "oracle",
+           "sample": f"{nreq} requests ({positions} verified positions) of input set 0, "
+                     f"{done} repetitions in {el:.1f} s, {threads} threads",
+           "value_1_thread": positions * done1 / el1, "cpu_model": cpu_description()}
+    return out, parity_report(res, gpu_out, tok, vl, k, mode, nreq, positions)
+
+
+def parity_report(ref, g, tok, vl, k, mode, nreq, positions):
+    """GPU outputs of the sampled requests against the oracle's (bands as in
+    the parity tests: tests/parity.py)."""
+    import numpy as np
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import parity
+    rep = {"requests": nreq, "rows": positions}
+    if "v" in ref:
+        gv = {"accept_len": g["accept_len"][:nreq], "out_tokens": g["out_tokens"][:nreq]}
+        T = 0.0 if mode == "greedy" else 1.0
+        rep.update(parity.verify_counts(gv, ref["v"], T, tok, vl, k))
+        if T > 0:
+            rep["max_margin_error"] = parity.margin_error(g["margins"][:nreq], ref["v"]["margins"], vl, k)
+    if "o" in ref:
+        o = ref["o"]
+        rep["max_loss_rel_error"] = max(parity.loss_rel_error(g["loss_ce"][:positions], o["loss_ce"]),
+                                        parity.loss_rel_error(g["loss_rkl"][:positions], o["loss_rkl"]))
+        rep["loss_over_tolerance"] = int((parity.loss_excess(g["loss_ce"][:positions], o["loss_ce"]) > 0).sum()
+                                         + (parity.loss_excess(g["loss_rkl"][:positions], o["loss_rkl"]) > 0).sum())
+        ge = parity.grad_errors(g["grad"][:positions], o["grad"])
+        rep["max_grad_abs_error"] = ge["max_abs"]
+        rep["grad_over_tolerance"] = ge["over_tol"]
+    return rep
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak, AMD published
@@ -384,13 +440,21 @@ def main():
                args.lam, ro, ce if fused else None, rk if fused else None,
                grad if fused else None, status, ws, stream)
 
-    # accept lengths per set (for the bonus-row byte count)
-    accs = []
-    for ds in dsets:
+    # One call per set before the warm-up: accept lengths (for the bonus-row
+    # byte count and tau) and, for set 0, the outputs the oracle leg checks.
+    accs, taus, first = [], [], None
+    for si, ds in enumerate(dsets):
         call(ds)
         torch.cuda.synchronize()
         assert int(status.item()) == 0, f"status flags {int(status.item())}"
-        accs.append(acc.cpu().numpy().copy())
+        a = acc.cpu().numpy().copy()
+        accs.append(a)
+        taus.append(float((a + 1).mean()))
+        if si == 0:
+            N0 = int(np.clip(sets[0].verify_len[:8], 1, k).sum())
+            first = {"accept_len": a, "out_tokens": outt.cpu().numpy(), "margins": mg.cpu().numpy(),
+                     "loss_ce": ce[:N0].cpu().numpy(), "loss_rkl": rk[:N0].cpu().numpy(),
+                     "grad": grad[:N0].float().cpu().numpy()}
     bytes_per_set = [algorithmic_bytes(bt.verify_len, a, B, k, V, args.mode) for bt, a in zip(sets, accs)]
     pos_per_set = [int(np.clip(bt.verify_len, 1, k).sum()) for bt in sets]
 
@@ -398,9 +462,30 @@ def main():
         call(dsets[i % len(dsets)])
     torch.cuda.synchronize()
 
-    # Pass 1: events around each whole call (the per-call distribution).  It
-    # runs first so that the two passes below find the GPU's clocks settled
-    # even when few warm-up calls were asked for.
+    # The timed steps: back-to-back calls bracketed by synchronisations
+    # (value, ms_per_step).  The library attaches a pair of HIP events to the
+    # dispatch of each call's dominant kernel (adaflash_timing_enable), which
+    # take that kernel's own start and end times on the call's stream: the
+    # roofline comes from the same steps.
+    ada.adaflash_timing_enable(args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        call(dsets[i % len(dsets)])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kdur = np.array(ada.adaflash_timing_read(args.steps)) * 1e-3  # seconds
+    ada.adaflash_timing_enable(0)
+    st = int(status.item())
+    if st != 0:
+        print(f"status flags {st} after the timed calls", file=sys.stderr)
+        sys.exit(1)
+    if len(kdur) != args.steps:
+        print("dominant-kernel timing incomplete", file=sys.stderr)
+        sys.exit(1)
+
+    # After the timed steps: events around each whole call (the per-call
+    # distribution, pack and finaliser included).
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     for i in range(args.steps):
@@ -408,38 +493,29 @@ def main():
         call(dsets[i % len(dsets)])
         ends[i].record(stream)
     torch.cuda.synchronize()
-    # Pass 2: HIP events attached by the library to the dispatch of each
-    # call's dominant kernel (for the roofline).
-    ada.adaflash_timing_enable(args.steps)
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        call(dsets[i % len(dsets)])
-    torch.cuda.synchronize()
-    kdur = np.array(ada.adaflash_timing_read(args.steps)) * 1e-3  # seconds
-    ada.adaflash_timing_enable(0)
-    # Pass 3, the timed steps: back-to-back calls with no event between
-    # them, bracketed by synchronisations (value and ms_per_step).
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        call(dsets[i % len(dsets)])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    st = int(status.item())
-    if st != 0:
-        print(f"status flags {st} after the timed calls", file=sys.stderr)
-        sys.exit(1)
+    durs = np.array([s_.elapsed_time(e_) for s_, e_ in zip(starts, ends)]) * 1e-3  # seconds
 
-    durs = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)]) * 1e-3  # seconds
     idx = np.arange(args.steps) % len(dsets)
     positions = float(sum(pos_per_set[j] for j in idx))
     bytes_total = float(sum(bytes_per_set[j] for j in idx))
-    avg_dur = float(durs.mean())
-    if len(kdur) != args.steps:
-        print("dominant-kernel timing incomplete", file=sys.stderr)
-        sys.exit(1)
     kavg = float(kdur.mean())
     achieved = bytes_total / args.steps / kavg / 1e9
 
+    T = 0.0 if args.mode == "greedy" else 1.0
+    what = {"fused": "fused verify + supervision", "verify": "sampled verification",
+            "greedy": "greedy verification", "opd": "supervision only"}[args.mode]
+    if args.variant:
+        what += f" ({args.variant} loss)"
+    noise = "sigma_b~U{0.3,1,2}" if wl.sigma_choice else f"sigma={wl.sigmas[0]:g}"
+    lens = ("verify_len~U{1..%d}" % k) if wl.ragged else ("verify_len=%d" % k)
+    sup = ""
+    if args.mode in ("fused", "opd"):
+        vp = {"rkl": "delta=inf", "rkl_clip": "delta=0.01", "mixture": "alpha=0.8, delta=0.01", "fkl": "",
+              "wce": "position decay 7"}
+        sup = (", " + vp[args.variant]) if args.variant else f", c={args.clip:g}, lambda={args.lam:g}"
+    workload = (f"{args.workload}: {what}, B={B}, k={k}, V={V}, bf16 logits, {lens}, z_p=2N-1.1ln(v+1), "
+                f"z_q=0.7z_p+{noise}N" + ("" if args.mode == "opd" else f", T={T:g}") + sup
+                + f", layout={args.layout}")
     res = {
         "metric": METRIC,
         "value": positions / elapsed,
@@ -453,33 +529,29 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {
-            "workload": ("%s fused verify+supervision: B=%d, k=%d, V=%d, bf16 logits, "
-                         "verify_len%s, sigma_b~U{0.3,1,2}, T=%d, c=%g, lambda=%g, mode=%s%s, layout=%s"
-                         % (args.workload, B, k, V, ("~U{1..%d}" % k) if wl.ragged else ("=%d" % k),
-                            0 if args.mode == "greedy" else 1,
-                            args.clip, args.lam, args.mode,
-                            (", variant=%s" % args.variant) if args.variant else "", args.layout)),
-            "B": B, "k": k, "V": V, "input_sets": args.sets,
-        },
+        "config": {"workload": workload, "B": B, "k": k, "V": V, "input_sets": args.sets},
         "roofline": {
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": measured_traffic(args.mode, args.workload == "c128" and not packed),
+            "traffic": measured_traffic(args.mode, args.workload == "c128" and not packed and not args.variant
+                                        and args.clip == 10.0),
         },
-        "dominant_kernel": {"fused": "sup_kernel", "opd": "sup_kernel", "verify": "vstat_kernel",
+        "dominant_kernel": {"fused": "fsup_kernel", "opd": "fsup_kernel", "verify": "vstat_kernel",
                             "greedy": "gstat_kernel"}[args.mode],
         "dominant_kernel_us_avg": kavg * 1e6,
-        "kernel_ms_avg": avg_dur * 1e3,
-        "kernel_ms_p10_p50_p90": [float(np.percentile(durs, q) * 1e3) for q in (10, 50, 90)],
+        "dominant_kernel_us_p10_p50_p90": [float(np.percentile(kdur, q) * 1e6) for q in (10, 50, 90)],
+        "call_ms_p10_p50_p90": [float(np.percentile(durs, q) * 1e3) for q in (10, 50, 90)],
         "algorithmic_bytes_per_call": bytes_total / args.steps,
         "verified_positions_per_call": positions / args.steps,
     }
+    if args.mode != "opd":
+        res["tau"] = float(np.mean(taus))  # mean accept length + 1 over the input sets' requests
     if not args.no_cpu and not args.variant:
-        res["cpu_baseline"] = cpu_baseline(sets[0], args.mode, args.clip, args.lam, args.cpu_seconds)
+        res["cpu_baseline"], res["parity"] = cpu_baseline(sets[0], first, args.mode, args.clip, args.lam,
+                                                          args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 
