@@ -61,6 +61,9 @@ def load_library() -> ctypes.CDLL:
         lib.adaflash_verify.restype = i32
         lib.adaflash_verify.argtypes = [i32, vp, vp, vp, vp, vp, i32, i32, i32, f32, vp, vp, vp,
                                         f32, f32, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.adaflash_verify_noalloc.restype = i32
+        lib.adaflash_verify_noalloc.argtypes = [i32, vp, vp, vp, vp, vp, i32, i32, i32, f32, vp, vp, vp,
+                                                f32, f32, vp, vp, vp, vp, vp, vp]
         lib.adaflash_opd_loss_fwd_bwd.restype = i32
         lib.adaflash_opd_loss_fwd_bwd.argtypes = [i32, vp, vp, vp, i32, i32, i32, f32, f32, vp, vp,
                                                   vp, vp, vp, vp, sz, vp]
@@ -232,6 +235,32 @@ def adaflash_verify(target, draft, tokens, verify_len, uniforms, T, accept_len, 
         B, k1 - 1, V, float(T), _ptr(accept_len), _ptr(out_tokens), _ptr(margins), float(clip_c),
         float(lam), _ptr(row_offsets), _ptr(loss_ce), _ptr(loss_rkl), _ptr(grad_draft), _ptr(status),
         _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
+    _check(rc)
+
+
+NOALLOC_WORKSPACE_BYTES = 16 << 20  # ADAFLASH_NOALLOC_WORKSPACE_BYTES
+
+
+def adaflash_verify_noalloc(target, draft, tokens, verify_len, uniforms, T, accept_len, out_tokens, margins,
+                            clip_c, lam, row_offsets, loss_ce, loss_rkl, grad_draft, status, stream=None) -> None:
+    """Direct binding of adaflash_verify_noalloc: adaflash_verify without a
+    workspace argument (the library's own device array is used; calls that
+    overlap on one GPU race)."""
+    _logits(target, "target", 3)
+    B, k1, V = target.shape
+    k = k1 - 1
+    opd = loss_ce is not None or loss_rkl is not None or grad_draft is not None
+    _arg(draft, "draft", target.dtype, (B, k, V), optional=(T == 0 and not opd))
+    _arg(tokens, "tokens", torch.int32, (B, k))
+    _arg(verify_len, "verify_len", torch.int32, (B,))
+    _arg(uniforms, "uniforms", torch.float32, (B, k + 1), optional=(T == 0))
+    _check_outputs(B, k, V, target.dtype, B * k, accept_len, out_tokens, margins, row_offsets, loss_ce, loss_rkl,
+                   grad_draft, status)
+    rc = load_library().adaflash_verify_noalloc(
+        _dtype_code(target), _ptr(target), _ptr(draft), _ptr(tokens), _ptr(verify_len), _ptr(uniforms),
+        B, k, V, float(T), _ptr(accept_len), _ptr(out_tokens), _ptr(margins), float(clip_c),
+        float(lam), _ptr(row_offsets), _ptr(loss_ce), _ptr(loss_rkl), _ptr(grad_draft), _ptr(status),
+        _stream(stream))
     _check(rc)
 
 

@@ -110,12 +110,18 @@ static int run(LaunchArgs& a, void* workspace) {
   return ADAFLASH_OK;
 }
 
-static int verify_impl(int packed, adaflash_dtype dtype, const void* target_logits, const void* draft_logits,
-                       const int32_t* draft_tokens, const int32_t* verify_len, const float* uniforms,
-                       int B, int k, int V, float T, int32_t* accept_len, int32_t* out_tokens,
-                       float* margins, float clip_c, float lambda, int32_t* row_offsets,
-                       float* loss_ce, float* loss_rkl, void* grad_draft, int32_t* status_flags,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace adaflash {
+int fail_with(int code, const char* msg) { return fail(code, "%s", msg); }
+
+int verify_impl(int packed, int dtype_code, const void* target_logits, const void* draft_logits,
+                const int32_t* draft_tokens, const int32_t* verify_len, const float* uniforms,
+                int B, int k, int V, float T, int32_t* accept_len, int32_t* out_tokens,
+                float* margins, float clip_c, float lambda, int32_t* row_offsets,
+                float* loss_ce, float* loss_rkl, void* grad_draft, int32_t* status_flags,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  const adaflash_dtype dtype = (adaflash_dtype)dtype_code;
   const bool opd = loss_ce || loss_rkl || grad_draft;
   if (!(T >= 0.f) || std::isinf(T)) return fail(ADAFLASH_E_INVALID, "T must be finite and >= 0%s");
   const bool need_draft = T > 0.f || opd;
@@ -156,6 +162,10 @@ static int verify_impl(int packed, adaflash_dtype dtype, const void* target_logi
   a.stream = (hipStream_t)stream;
   return run(a, workspace);
 }
+
+}  // namespace adaflash
+
+extern "C" {
 
 static int opd_impl(int packed, adaflash_dtype dtype, const void* target_logits,
                     const void* draft_logits, const int32_t* verify_len, int B, int k,

@@ -77,6 +77,16 @@ struct LaunchArgs {
 // launch error.
 hipError_t launch(const LaunchArgs& a);
 
+// Argument checks and launch of adaflash_verify (packed = 0) and
+// adaflash_verify_packed (packed = 1) with a given workspace; returns an
+// adaflash_status.  fail_with records the message adaflash_last_error returns.
+int verify_impl(int packed, int dtype, const void* target_logits, const void* draft_logits,
+                const int32_t* draft_tokens, const int32_t* verify_len, const float* uniforms, int B, int k, int V,
+                float T, int32_t* accept_len, int32_t* out_tokens, float* margins, float clip_c, float lambda,
+                int32_t* row_offsets, float* loss_ce, float* loss_rkl, void* grad_draft, int32_t* status_flags,
+                void* workspace, size_t workspace_bytes, void* stream);
+int fail_with(int code, const char* msg);
+
 // Measurement hook (adaflash_timing_enable / adaflash_timing_read).
 int timing_enable(int cap);
 int timing_read(float* ms, int cap);

@@ -160,6 +160,28 @@ ADAFLASH_API int adaflash_verify(adaflash_dtype dtype, const void* target_logits
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * adaflash_verify_noalloc -- adaflash_verify for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Same arguments, outputs and errors as
+ * adaflash_verify (padded logits layout), without the workspace: the call
+ * uses a device array of the library, ADAFLASH_NOALLOC_WORKSPACE_BYTES per
+ * GPU (every GPU the library runs on holds one until the process ends), whose
+ * address is looked up on the first call on each device; it calls no
+ * allocating routine.  Returns ADAFLASH_E_UNSUPPORTED, with nothing enqueued,
+ * when adaflash_workspace_bytes(B, k, V) exceeds that size (at V = 151936 and
+ * k = 16 up to about 800 requests fit).  Every call on one GPU shares the
+ * array and initialises what it reads: calls that overlap on one GPU (other
+ * streams or host threads) race, and the caller must order them.
+ */
+#define ADAFLASH_NOALLOC_WORKSPACE_BYTES ((size_t)16 << 20)
+ADAFLASH_API int adaflash_verify_noalloc(adaflash_dtype dtype, const void* target_logits, const void* draft_logits,
+                    const int32_t* draft_tokens, const int32_t* verify_len, const float* uniforms,
+                    int B, int k, int V, float T, int32_t* accept_len, int32_t* out_tokens,
+                    float* margins, float clip_c, float lambda, int32_t* row_offsets,
+                    float* loss_ce, float* loss_rkl, void* grad_draft, int32_t* status_flags,
+                    void* stream);
+
+/*
  * adaflash_opd_loss_fwd_bwd -- supervision only (no verification) for the
  * verified rows of a replay batch (AdaFlash review, Algorithm 1 steps 4-6 and
  * Algorithm 2, at temperature 1).

@@ -299,3 +299,16 @@ def test_opd_and_variant_bindings_check_tensors(lib):
     a["draft"] = torch.zeros(B + 2, V, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="packed draft"):
         ada.adaflash_verify_packed(**a)
+
+
+def test_noalloc_entry_point_rejects_sizes_beyond_its_array(lib):
+    """adaflash_verify_noalloc checks the batch against its fixed device array
+    before anything else (no GPU needed for the rejection)."""
+    import diffusion_drafter_verification_amd as ada
+    f = lib.adaflash_verify_noalloc
+    null = [None] * 5
+    assert lib.adaflash_workspace_bytes(4096, 16, 151936) > ada.NOALLOC_WORKSPACE_BYTES
+    rc = f(1, *null, 4096, 16, 151936, 1.0, None, None, None, 10.0, 1.0, None, None, None, None, None, None)
+    assert rc == -4 and b"no-allocation" in lib.adaflash_last_error()
+    rc = f(1, *null, 4, 0, 151936, 1.0, None, None, None, 10.0, 1.0, None, None, None, None, None, None)
+    assert rc == -1
