@@ -2101,19 +2101,40 @@ __global__ __launch_bounds__(kThreads, 8) void fsup_kernel(KParams P) {
       gstar = fma_f16(w, xs_u & 1, fmaf(lsc, zqs - st.Mp, csc), pstar) - ace;
     }
   } else {
-    // Exact path: clipped sums, second barrier, then the gradient with every
-    // per-entry term recomputed from the packed logits.
+    // Exact path: clipped sums, second barrier, then the gradient.  A wave
+    // whose entries cannot be clipped (the fast path's bound, taken per
+    // thread: f_v <= s (A_t + max(0, -D)), with A_t = max e dz over the
+    // thread and s = exp(m - lse_q)) takes its sums from the pass-1 partials,
+    // sum_U f = s (W_t - D e_t) and sum_U q = s e_t, and writes the gradient
+    // with the fast path's formula; the other waves recompute every term from
+    // the packed logits, which stay in registers.
+    const float sc = mq == neg_inf() ? 0.f : fexp2(-aq - lse_q2);
+    const float tb = sc * (Amax + fmaxf(0.f, -D));
+    const bool wskip = __ballot(!(tb <= 0.999f * c)) == 0ull;  // (uniform in the wave)
     float Spart = 0.f, Rpart = 0.f;
+    if (wskip) {
+      const float F = sc * fmaf(-D, sq, W);
+      Rpart = F;
+      Spart = fmaf(sc, sq, F);
+      if (need_res) {
 #pragma unroll
-    for (int e = 0; e < kElems; ++e) {
-      const float zq = cq.get(e), zp = cp.get(e);
-      const float q = fexp2(fmaf(zq, kLog2e, -lse_q2));
-      if (need_res) Zpart += fmaxf(0.f, fexp2(fmaf(zp, kLog2e, -lse_p2)) - q);
-      const float dd = (zq - zp) - D;
-      const float f = q > 0.f ? q * dd : 0.f;
-      const bool inU = f <= c;
-      Rpart += inU ? f : c;
-      Spart += inU ? f + q : 0.f;
+        for (int e = 0; e < kElems; ++e) {
+          const float q = fexp2(fmaf(cq.get(e), kLog2e, -lse_q2));
+          Zpart += fmaxf(0.f, fexp2(fmaf(cp.get(e), kLog2e, -lse_p2)) - q);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < kElems; ++e) {
+        const float zq = cq.get(e), zp = cp.get(e);
+        const float q = fexp2(fmaf(zq, kLog2e, -lse_q2));
+        if (need_res) Zpart += fmaxf(0.f, fexp2(fmaf(zp, kLog2e, -lse_p2)) - q);
+        const float dd = (zq - zp) - D;
+        const float f = q > 0.f ? q * dd : 0.f;
+        const bool inU = f <= c;
+        Rpart += inU ? f : c;
+        Spart += inU ? f + q : 0.f;
+      }
     }
     float s3[3] = {Spart, Rpart, Zpart};
     const int ops3[3] = {OP_SUM, OP_SUM, OP_SUM};
@@ -2136,32 +2157,30 @@ __global__ __launch_bounds__(kThreads, 8) void fsup_kernel(KParams P) {
     wg_reduce<2>(sr, srops, fs.red);
     Rrow = sr[1];
     const float lamS = uniform(lam * sr[0]);
-    cp.opaque();
-    cq.opaque();
+    // Unclipped entries: g = q (ace - lambda S + lambda (dz - D + 1)).
+    const float c1x = fmaf(lam, 1.f - D, ace) - lamS + afk;
+    const float lsc = lam * sc, csc = c1x * sc;
     if (P.grad) {
 #pragma unroll
       for (int s2 = 0; s2 < NV; ++s2) {
-        // The chunk's words are read again slot by slot (this path is rare),
-        // so that no chunk is held in registers across the second barrier.
-        const int idx0 = v0 + s2 * (kThreads * VEC) + tid * VEC;
-        const uint4 pad4 = make_uint4(kPadBf16x2, kPadBf16x2, kPadBf16x2, kPadBf16x2);
-        const uint4 wp = idx0 < V ? *(const uint4*)((const uint16_t*)trow + idx0) : pad4;
-        const uint4 wq = idx0 < V ? *(const uint4*)((const uint16_t*)drow + idx0) : pad4;
-        cp.w[s2 * 4 + 0] = wp.x;
-        cp.w[s2 * 4 + 1] = wp.y;
-        cp.w[s2 * 4 + 2] = wp.z;
-        cp.w[s2 * 4 + 3] = wp.w;
-        cq.w[s2 * 4 + 0] = wq.x;
-        cq.w[s2 * 4 + 1] = wq.y;
-        cq.w[s2 * 4 + 2] = wq.z;
-        cq.w[s2 * 4 + 3] = wq.w;
         float g[VEC];
+        if (wskip) {
+          const uint4 h4 = *(const uint4*)(ecache + ((size_t)s2 * kThreads + tid) * 4);
+          const uint32_t hw[4] = {h4.x, h4.y, h4.z, h4.w};
+          float dz8[8];
+          bf16_diff8(&cq.w[s2 * 4], &cp.w[s2 * 4], dz8);
 #pragma unroll
-        for (int u = 0; u < VEC; ++u) {
-          const int e = s2 * VEC + u;
-          g[u] = grad_exact(cq.get(e), cp.get(e), lse_q2, D, lam, lamS, c, ace);
-          if constexpr (FKL) g[u] -= afk * fexp2(fmaf(cp.get(e), kLog2e, -lse_p2));
-          if (u & 1) __builtin_amdgcn_sched_barrier(0);
+          for (int u = 0; u < VEC; ++u) {
+            const float pterm = FKL ? -afk * fexp2(fmaf(cp.get(s2 * VEC + u), kLog2e, -lse_p2)) : 0.f;
+            g[u] = fma_f16(hw[u / 2], u & 1, fmaf(lsc, dz8[u], csc), pterm);
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < VEC; ++u) {
+            const int e = s2 * VEC + u;
+            g[u] = grad_exact(cq.get(e), cp.get(e), lse_q2, D, lam, lamS, c, ace);
+            if constexpr (FKL) g[u] -= afk * fexp2(fmaf(cp.get(e), kLog2e, -lse_p2));
+          }
         }
         store_slot(s2, g);
       }
