@@ -665,6 +665,14 @@ struct FinShared {
   unsigned long long amax[72];      // greedy: per-row (value, index) argmax keys
 };
 
+// Shared scratch of the supervision kernel for bf16 rows: reductions and the
+// row values handed between waves.
+struct SupShared {
+  float red[kWaves * 8];
+  float f[16];
+  int i[8];
+};
+
 // Inclusive prefix sum across the 64 lanes of a wave.
 __device__ __forceinline__ float wave_scan_incl(float v) {
   const int lane = threadIdx.x & 63;
@@ -1242,8 +1250,8 @@ __device__ __forceinline__ float accept_margin(float zpx, float zqx, float u, fl
 // hands the results to the other waves through fs.f; otherwise every wave
 // takes part.  CHUNK_X: the records carry no argmax; xstar is then the lowest
 // chunk whose maximum is the row maximum.
-template <bool SAMPLED, bool CHUNK_X, bool FKL>
-__device__ SupStats combine_sup(const KParams& P, int r, FinShared& fs, float zpx, float zqx, float u) {
+template <bool SAMPLED, bool CHUNK_X, bool FKL, typename SH>
+__device__ SupStats combine_sup(const KParams& P, int r, SH& fs, float zpx, float zqx, float u) {
   const int tid = threadIdx.x;
   const int G = P.G;
   auto reduce = [&](float mp, float mq, float sp, float sq, float w, float a, int idx, bool valid,
@@ -1851,12 +1859,15 @@ __global__ __launch_bounds__(kThreads, 8) void fsup_kernel(KParams P) {
   constexpr bool SAMPLED = VMODE == 2, VERIFY = VMODE != 0;
   constexpr int VEC = 8;
   constexpr int NV = kElems / VEC;
-  __shared__ FinShared fs;
+  __shared__ SupShared fs;
   __shared__ int sh_ok;
   // exp(z_q - m) of this thread's draft entries from pass 1 (m: the thread's
   // maximum), as fp16 pairs, slot-major; each thread reads only what it wrote.
   __shared__ uint32_t ecache[kElems / 2 * kThreads];
   __shared__ float wpart[kWaves][6];
+  // This thread's pass-1 sums e, W and max e dz for the exact path (kept in
+  // LDS rather than in registers across the row barrier).
+  __shared__ float tpart[3][kThreads];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -1942,6 +1953,9 @@ __global__ __launch_bounds__(kThreads, 8) void fsup_kernel(KParams P) {
 #pragma unroll
     for (int e = 0; e < kElems; ++e) sp += fexp2(fmaf(cp.get(e), kLog2e, ap));
   }
+  tpart[0][tid] = sq;
+  tpart[1][tid] = W;
+  tpart[2][tid] = Amax;
   {
     // Thread partials to the wave's maxima, reduced inside each wave; thread 0
     // merges the four waves and publishes the chunk record.  Padding entries
@@ -2109,13 +2123,14 @@ __global__ __launch_bounds__(kThreads, 8) void fsup_kernel(KParams P) {
     // with the fast path's formula; the other waves recompute every term from
     // the packed logits, which stay in registers.
     const float sc = mq == neg_inf() ? 0.f : fexp2(-aq - lse_q2);
-    const float tb = sc * (Amax + fmaxf(0.f, -D));
+    const float tb = sc * (tpart[2][tid] + fmaxf(0.f, -D));
     const bool wskip = __ballot(!(tb <= 0.999f * c)) == 0ull;  // (uniform in the wave)
     float Spart = 0.f, Rpart = 0.f;
     if (wskip) {
-      const float F = sc * fmaf(-D, sq, W);
+      const float e_t = tpart[0][tid];
+      const float F = sc * fmaf(-D, e_t, tpart[1][tid]);
       Rpart = F;
-      Spart = fmaf(sc, sq, F);
+      Spart = fmaf(sc, e_t, F);
       if (need_res) {
 #pragma unroll
         for (int e = 0; e < kElems; ++e) {
