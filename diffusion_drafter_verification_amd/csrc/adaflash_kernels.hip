@@ -691,7 +691,11 @@ __device__ __forceinline__ unsigned int ukey(float x) {
 }
 
 // Draws the correction or bonus token for request b.  Runs on one workgroup.
-template <bool BF16, bool ALIGNED, int VMODE>
+// LOG2REC: the chunk records hold their sums relative to powers of two (the
+// bf16 supervision kernel's records: reference exponents in rec[1] and rec[4],
+// in log2 units, at T = 1); otherwise relative to the chunk maxima rec[0] and
+// rec[4] of z / T.
+template <bool BF16, bool ALIGNED, int VMODE, bool LOG2REC = false>
 __device__ void finalize_request(const KParams& P, int b, FinShared& fs) {
   const int k = P.k, V = P.V, G = P.G;
   const int tid = threadIdx.x;  // (k + 1 <= 65 rows: thread i holds position i)
@@ -771,7 +775,7 @@ __device__ void finalize_request(const KParams& P, int b, FinShared& fs) {
       spT[h] = sqT[h] = res[h] = 0.f;
       if (jj < G) {
         const float* rec = P.part1 + ((size_t)rs * G + jj) * kRec1;
-        mp[h] = pub_load(rec + 0);
+        mp[h] = pub_load(rec + (LOG2REC ? 1 : 0));
         spT[h] = pub_load(rec + 2);
         if (A < L) {
           mq[h] = pub_load(rec + 4);
@@ -785,8 +789,13 @@ __device__ void finalize_request(const KParams& P, int b, FinShared& fs) {
     float pj[2], qj[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      pj[h] = mp[h] == neg_inf() ? 0.f : spT[h] * fexp2((mp[h] - Mp) * P.kT);
-      qj[h] = mq[h] == neg_inf() ? 0.f : sqT[h] * fexp2((mq[h] - Mq) * P.kT);
+      if constexpr (LOG2REC) {
+        pj[h] = mp[h] == neg_inf() ? 0.f : __builtin_ldexpf(spT[h], (int)fmaxf(mp[h] - Mp, -256.f));
+        qj[h] = mq[h] == neg_inf() ? 0.f : __builtin_ldexpf(sqT[h], (int)fmaxf(mq[h] - Mq, -256.f));
+      } else {
+        pj[h] = mp[h] == neg_inf() ? 0.f : spT[h] * fexp2((mp[h] - Mp) * P.kT);
+        qj[h] = mq[h] == neg_inf() ? 0.f : sqT[h] * fexp2((mq[h] - Mq) * P.kT);
+      }
     }
     const float SpT = wave_reduce<OP_SUM>(pj[0] + pj[1]);
     const float SqT = wave_reduce<OP_SUM>(qj[0] + qj[1]);
@@ -830,7 +839,7 @@ __device__ void finalize_request(const KParams& P, int b, FinShared& fs) {
     Chunk<BF16> cp, cq;
     load_chunk<BF16, ALIGNED>(cp, trow, v0, V);
     if (resid) load_chunk<BF16, ALIGNED>(cq, drow, v0, V);
-    const float ap = -Mp * P.kT, aq = -Mq * P.kT;
+    const float ap = LOG2REC ? -Mp : -Mp * P.kT, aq = LOG2REC ? -Mq : -Mq * P.kT;
     constexpr int VEC = Chunk<BF16>::VEC;
     constexpr int NV = kElems / VEC;
     const int wave = tid >> 6;
@@ -1368,6 +1377,102 @@ __device__ SupStats combine_sup(const KParams& P, int r, SH& fs, float zpx, floa
   return s;
 }
 
+// Power-of-two scale exponent of a block of logits with maximum m:
+// ceil(m log2 e), clamped to [-2^20, 2^20] (-inf and NaN give -2^20).  Every
+// exp(z - ...) of the block is taken as 2^(z log2 e - a) <= 1 (up to one
+// rounding), and partial sums at different exponents merge by exact scaling
+// with ldexp.  Monotone in m: the exponent of a maximum is the maximum of the
+// exponents.
+__device__ __forceinline__ int shift_of(float m) {
+  return (int)fminf(fmaxf(__builtin_ceilf(m * kLog2e), -1048576.f), 1048576.f);
+}
+
+// Row statistics from the chunk records of the bf16 supervision kernel, whose
+// sums are relative to powers of two: rec[1] = a_p and rec[4] = a_q (the
+// chunk's scale exponents), rec[2] = sum 2^(z_p log2 e - a_p), rec[5] the same
+// for z_q, rec[3] = W and rec[6] = A on the z_q scale, rec[7] = sum p' (z_q -
+// z_p) on the z_p scale (forward KL), rec[0] = the chunk's exact maximum of
+// z_p (x*: the lowest chunk holding the row maximum).  Wave 0 reduces them,
+// chunk j in lane j (G <= 64), and hands the results to the other waves
+// through fs.f; lse_q2 and lse_p2 are in log2 units.
+template <bool SAMPLED, bool FKL, typename SH>
+__device__ SupStats combine_sup_pow2(const KParams& P, int r, SH& fs, float zpx, float zqx, float u) {
+  const int tid = threadIdx.x;
+  const int G = P.G;  // <= 64 (the host dispatches larger rows elsewhere)
+  if (tid < 64) {
+    float mx = neg_inf(), ap = neg_inf(), aq = neg_inf(), a = neg_inf();
+    float sp = 0.f, w = 0.f, sq = 0.f, wp = 0.f;
+    const bool valid = tid < G;
+    if (valid) {
+      const float* rec = P.part1 + ((size_t)r * G + tid) * kRec1;
+      mx = pub_load(rec + 0);
+      ap = pub_load(rec + 1);
+      sp = pub_load(rec + 2);
+      w = pub_load(rec + 3);
+      aq = pub_load(rec + 4);
+      sq = pub_load(rec + 5);
+      a = pub_load(rec + 6);
+      if (FKL) wp = pub_load(rec + 7);
+    }
+    // Scale exponents are integers in [-2^20, 2^20] (float in the record).
+    const int api = valid ? (int)ap : -(1 << 21), aqi = valid ? (int)aq : -(1 << 21);
+    const float Mx = wave_reduce<OP_MAX>(mx);
+    const int Api = __float_as_int(wave_reduce<OP_MAXI>(__int_as_float(api)));
+    const int Aqi = __float_as_int(wave_reduce<OP_MAXI>(__int_as_float(aqi)));
+    const float Ap = (float)Api, Aq = (float)Aqi;
+    const int dp = max(api - Api, -256), dq = max(aqi - Aqi, -256);
+    float v[7];
+    v[0] = wave_reduce<OP_SUM>(__builtin_ldexpf(sp, dp));
+    v[1] = wave_reduce<OP_SUM>(__builtin_ldexpf(sq, dq));
+    v[2] = wave_reduce<OP_SUM>(__builtin_ldexpf(w, dq));
+    v[3] = wave_reduce<OP_MAX>(__builtin_ldexpf(a, dq));
+    v[4] = wave_reduce<OP_MINI>(__int_as_float(valid && mx == Mx ? tid : kIntMax));
+    v[5] = wave_reduce<OP_MAXI>(
+        __int_as_float(!valid || (__builtin_isfinite(w) && !__builtin_isnan(a) && a < __builtin_inff()) ? 0 : 1));
+    v[6] = FKL ? wave_reduce<OP_SUM>(__builtin_ldexpf(wp, dp)) : 0.f;
+    if (tid == 0) {
+      const float rSp = __builtin_amdgcn_rcpf(v[0]), rSq = __builtin_amdgcn_rcpf(v[1]);
+      const float lq = Aq + flog2(v[1]);
+      const float lp = Ap + flog2(v[0]);
+      const float D = (lq - lp) * kLn2;
+      fs.f[0] = Mx;
+      fs.f[1] = Aq;
+#pragma unroll
+      for (int q = 0; q < 6; ++q) fs.f[2 + q] = v[q];
+      if (SAMPLED) {
+        const float px = fexp2(fmaf(zpx, kLog2e, -Ap)) * rSp;
+        const float qx = fexp2(fmaf(zqx, kLog2e, -Aq)) * rSq;
+        fs.f[8] = px - u * qx;
+      }
+      fs.f[9] = lq;
+      fs.f[10] = lp;
+      fs.f[11] = D;
+      fs.f[12] = v[2] * rSq - D;
+      fs.f[13] = (v[3] + fmaxf(0.f, -D)) * rSq;
+      fs.f[14] = v[6];
+    }
+  }
+  __syncthreads();
+  SupStats s;
+  s.Mp = uniform(fs.f[0]);
+  s.Mq = uniform(fs.f[1]);
+  s.Sp = uniform(fs.f[2]);
+  s.Sq = uniform(fs.f[3]);
+  s.Wsum = uniform(fs.f[4]);
+  s.BA = uniform(fs.f[5]);
+  s.xstar = __float_as_int(uniform(fs.f[6]));
+  s.nonfinite = __float_as_int(uniform(fs.f[7])) != 0;
+  s.margin = SAMPLED ? uniform(fs.f[8]) : 0.f;
+  s.lse_q2 = uniform(fs.f[9]);
+  s.lse_p2 = uniform(fs.f[10]);
+  s.D = uniform(fs.f[11]);
+  s.KL = uniform(fs.f[12]);
+  s.bound = uniform(fs.f[13]);
+  // Forward KL = sum p (log p - log q) = -E_p[z_q - z_p] + D.
+  s.fkl = FKL ? uniform(-fs.f[14] / s.Sp + s.D) : 0.f;
+  return s;
+}
+
 // Gradient value of the exact path (q recomputed in fp32: clip decisions).
 __device__ __forceinline__ float grad_exact(float zq, float zp, float lse_q2, float D, float lam, float lamS,
                                             float c, float ace) {
@@ -1864,7 +1969,7 @@ __global__ __launch_bounds__(kThreads, 8) void fsup_kernel(KParams P) {
   // exp(z_q - m) of this thread's draft entries from pass 1 (m: the thread's
   // maximum), as fp16 pairs, slot-major; each thread reads only what it wrote.
   __shared__ uint32_t ecache[kElems / 2 * kThreads];
-  __shared__ float wpart[kWaves][6];
+  __shared__ float wpart[kWaves][8];
   // This thread's pass-1 sums e, W and max e dz for the exact path (kept in
   // LDS rather than in registers across the row barrier).
   __shared__ float tpart[3][kThreads];
@@ -1921,8 +2026,9 @@ __global__ __launch_bounds__(kThreads, 8) void fsup_kernel(KParams P) {
   const float mq = draft_row ? thread_max_bf16(cq) : neg_inf();
   cp.opaque();
   cq.opaque();
-  const float ap = mp == neg_inf() ? 0.f : -mp * kLog2e;
-  const float aq = mq == neg_inf() ? 0.f : -mq * kLog2e;
+  // Each thread's exponentials relative to 2^(its scale exponent).
+  const int Ap = shift_of(mp), Aq = shift_of(mq);
+  const float ap = -(float)Ap, aq = -(float)Aq;
   float sp = 0.f, sq = 0.f, W = 0.f, Amax = neg_inf(), Wp = 0.f;
   if (draft_row) {
 #pragma unroll
@@ -1957,56 +2063,75 @@ __global__ __launch_bounds__(kThreads, 8) void fsup_kernel(KParams P) {
   tpart[1][tid] = W;
   tpart[2][tid] = Amax;
   {
-    // Thread partials to the wave's maxima, reduced inside each wave; thread 0
-    // merges the four waves and publishes the chunk record.  Padding entries
-    // (and whole padded threads or waves) vanish in the rescaling, since the
-    // chunk holds at least one entry of the row.
-    const float Mpw = wave_reduce<OP_MAX>(mp);
-    const float Mqw = wave_reduce<OP_MAX>(mq);
-    const float fp = mp == neg_inf() ? 0.f : fexp2((mp - Mpw) * kLog2e);
-    const float fq = mq == neg_inf() ? 0.f : fexp2((mq - Mqw) * kLog2e);
-    float v0s = wave_reduce_l63<OP_SUM>(sp * fp);
-    float v1s = wave_reduce_l63<OP_SUM>(sq * fq);
-    float v2s = wave_reduce_l63<OP_SUM>(W * fq);
-    float v3s = wave_reduce_l63<OP_MAX>(Amax * fq);
-    float v4s = FKL ? wave_reduce_l63<OP_SUM>(Wp * fp) : 0.f;
+    // Thread partials to the wave's scale exponents (exact ldexp), reduced
+    // inside each wave; thread 0 merges the four waves the same way and
+    // publishes the chunk record.  Padding entries (and whole padded threads
+    // or waves) are exact zeros or vanish in the scaling, since the chunk
+    // holds at least one entry of the row.
+    const int Apw = __float_as_int(wave_reduce<OP_MAXI>(__int_as_float(Ap)));
+    const int Aqw = __float_as_int(wave_reduce<OP_MAXI>(__int_as_float(Aq)));
+    const float Mpw = wave_reduce_l63<OP_MAX>(mp);
+    const int dp = Ap - Apw, dq = Aq - Aqw;
+    const float v0s = wave_reduce_l63<OP_SUM>(__builtin_ldexpf(sp, dp));
+    const float v1s = wave_reduce_l63<OP_SUM>(__builtin_ldexpf(sq, dq));
+    const float v2s = wave_reduce_l63<OP_SUM>(__builtin_ldexpf(W, dq));
+    const float v3s = wave_reduce_l63<OP_MAX>(__builtin_ldexpf(Amax, dq));
+    const float v4s = FKL ? wave_reduce_l63<OP_SUM>(__builtin_ldexpf(Wp, dp)) : 0.f;
     if (lane == 63) {
       wpart[wave][0] = Mpw;
-      wpart[wave][1] = Mqw;
+      wpart[wave][1] = __int_as_float(Apw);
       wpart[wave][2] = v0s;
-      wpart[wave][3] = v1s;
-      wpart[wave][4] = v2s;
-      wpart[wave][5] = FKL ? v4s : v3s;
-      if (FKL) fs.f[15 - wave] = v3s;
+      wpart[wave][3] = __int_as_float(Aqw);
+      wpart[wave][4] = v1s;
+      wpart[wave][5] = v2s;
+      wpart[wave][6] = v3s;
+      wpart[wave][7] = v4s;
     }
     __syncthreads();
-    if (tid == 0) {
-      float Mp = wpart[0][0], Mq = wpart[0][1];
-#pragma unroll
-      for (int w = 1; w < kWaves; ++w) {
-        Mp = fmaxf(Mp, wpart[w][0]);
-        Mq = fmaxf(Mq, wpart[w][1]);
+    if (wave == 0) {
+      // Lane w < 4 holds wave w's partials; two quad steps merge them, in the
+      // order (w0 + w1) + (w2 + w3), into lane 0.
+      const bool hw = lane < kWaves;
+      const int wl = hw ? lane : 0;
+      float Mp = hw ? wpart[wl][0] : neg_inf();
+      int Apc = hw ? __float_as_int(wpart[wl][1]) : -1048576;
+      int Aqc = hw ? __float_as_int(wpart[wl][3]) : -1048576;
+      const int ap_l = Apc, aq_l = Aqc;
+      Mp = fmaxf(Mp, dpp_f<0xB1>(Mp));
+      Mp = fmaxf(Mp, dpp_f<0x4E>(Mp));
+      Apc = max(Apc, dpp_i<0xB1>(Apc));
+      Apc = max(Apc, dpp_i<0x4E>(Apc));
+      Aqc = max(Aqc, dpp_i<0xB1>(Aqc));
+      Aqc = max(Aqc, dpp_i<0x4E>(Aqc));
+      const int ep = ap_l - Apc, eq = aq_l - Aqc;
+      float Sp = hw ? __builtin_ldexpf(wpart[wl][2], ep) : 0.f;
+      float Sq = hw ? __builtin_ldexpf(wpart[wl][4], eq) : 0.f;
+      float Ws = hw ? __builtin_ldexpf(wpart[wl][5], eq) : 0.f;
+      float As = hw ? __builtin_ldexpf(wpart[wl][6], eq) : neg_inf();
+      float Wps = FKL && hw ? __builtin_ldexpf(wpart[wl][7], ep) : 0.f;
+      Sp += dpp_f<0xB1>(Sp);
+      Sp += dpp_f<0x4E>(Sp);
+      Sq += dpp_f<0xB1>(Sq);
+      Sq += dpp_f<0x4E>(Sq);
+      Ws += dpp_f<0xB1>(Ws);
+      Ws += dpp_f<0x4E>(Ws);
+      As = fmaxf(As, dpp_f<0xB1>(As));
+      As = fmaxf(As, dpp_f<0x4E>(As));
+      if (FKL) {
+        Wps += dpp_f<0xB1>(Wps);
+        Wps += dpp_f<0x4E>(Wps);
       }
-      float Sp = 0.f, Sq = 0.f, Ws = 0.f, As = neg_inf(), Wps = 0.f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float gp = wpart[w][0] == neg_inf() ? 0.f : fexp2((wpart[w][0] - Mp) * kLog2e);
-        const float gq = wpart[w][1] == neg_inf() ? 0.f : fexp2((wpart[w][1] - Mq) * kLog2e);
-        Sp += wpart[w][2] * gp;
-        Sq += wpart[w][3] * gq;
-        Ws += wpart[w][4] * gq;
-        const float aw = FKL ? fs.f[15 - w] : wpart[w][5];
-        As = fmaxf(As, aw * gq);
-        if (FKL) Wps += wpart[w][5] * gp;
+      if (lane == 0) {
+        float* rec = P.part1 + ((size_t)r * G + j) * kRec1;
+        pub_store(rec + 0, Mp);
+        pub_store(rec + 1, (float)Apc);
+        pub_store(rec + 2, Sp);
+        pub_store(rec + 3, Ws);
+        pub_store(rec + 4, (float)Aqc);
+        pub_store(rec + 5, Sq);
+        pub_store(rec + 6, As);
+        if (FKL) pub_store(rec + 7, Wps);
       }
-      float* rec = P.part1 + ((size_t)r * G + j) * kRec1;
-      pub_store(rec + 0, Mp);
-      pub_store(rec + 2, Sp);
-      pub_store(rec + 3, Ws);
-      pub_store(rec + 4, Mq);
-      pub_store(rec + 5, Sq);
-      pub_store(rec + 6, As);
-      if (FKL) pub_store(rec + 7, Wps);
     }
   }
   if (!draft_row) return;
@@ -2019,7 +2144,7 @@ __global__ __launch_bounds__(kThreads, 8) void fsup_kernel(KParams P) {
     const unsigned long long any = __ballot(rej);
     if (l == 0) fs.i[0] = any != 0ull;
   }
-  const SupStats st = combine_sup<SAMPLED, true, FKL>(P, r, fs, zpx, zqx, u_acc);
+  const SupStats st = combine_sup_pow2<SAMPLED, FKL>(P, r, fs, zpx, zqx, u_acc);
   const bool earlier_rejected = SAMPLED && fs.i[0] != 0;
   const float lse_q2 = st.lse_q2, lse_p2 = st.lse_p2, D = st.D, KL = st.KL;
   const float wi = P.wdecay > 0.f ? uniform(fexp2(-(float)i * kLog2e / P.wdecay)) : 1.f;
@@ -2083,7 +2208,7 @@ __global__ __launch_bounds__(kThreads, 8) void fsup_kernel(KParams P) {
     // g = q (lambda dz + c1), q = e s: e from the cache (this thread's shift),
     // s = exp(m - lse_q) with m this thread's maximum.
     const float c1 = FKL ? fmaf(-lam, D, ace - lam * KL) + afk : fmaf(-lam, D, ace - lam * KL);
-    const float sc = mq == neg_inf() ? 0.f : fexp2(-aq - lse_q2);
+    const float sc = fexp2(-aq - lse_q2);
     const float lsc = lam * sc, csc = c1 * sc;
     if (P.grad) {
 #pragma unroll
@@ -2122,7 +2247,7 @@ __global__ __launch_bounds__(kThreads, 8) void fsup_kernel(KParams P) {
     // sum_U f = s (W_t - D e_t) and sum_U q = s e_t, and writes the gradient
     // with the fast path's formula; the other waves recompute every term from
     // the packed logits, which stay in registers.
-    const float sc = mq == neg_inf() ? 0.f : fexp2(-aq - lse_q2);
+    const float sc = fexp2(-aq - lse_q2);
     const float tb = sc * (tpart[2][tid] + fmaxf(0.f, -D));
     const bool wskip = __ballot(!(tb <= 0.999f * c)) == 0ull;  // (uniform in the wave)
     float Spart = 0.f, Rpart = 0.f;
@@ -2494,10 +2619,10 @@ __global__ __launch_bounds__(kThreads) void vres_kernel(KParams P) {
 
 // One workgroup per request, after the row kernel: first rejection, then the
 // correction or bonus draw.
-template <bool BF16, bool ALIGNED, int VMODE>
+template <bool BF16, bool ALIGNED, int VMODE, bool LOG2REC = false>
 __global__ __launch_bounds__(kThreads) void final_kernel(KParams P) {
   __shared__ FinShared fs;
-  finalize_request<BF16, ALIGNED, VMODE>(P, (int)blockIdx.x, fs);
+  finalize_request<BF16, ALIGNED, VMODE, LOG2REC>(P, (int)blockIdx.x, fs);
 }
 
 // --------------------------------------------------------------- pack kernel
@@ -2600,9 +2725,9 @@ hipError_t launch_sup(const KParams& p, int grid, hipStream_t st) {
   return launch_dominant(sup_kernel<BF16, ALIGNED, VMODE, FKL>, grid, st, p);
 }
 
-template <bool BF16, bool ALIGNED, int VMODE>
+template <bool BF16, bool ALIGNED, int VMODE, bool LOG2REC = false>
 hipError_t launch_final(const KParams& p, hipStream_t st) {
-  hipLaunchKernelGGL((final_kernel<BF16, ALIGNED, VMODE>), dim3(p.B), dim3(kThreads), 0, st, p);
+  hipLaunchKernelGGL((final_kernel<BF16, ALIGNED, VMODE, LOG2REC>), dim3(p.B), dim3(kThreads), 0, st, p);
   return hipGetLastError();
 }
 
@@ -2611,12 +2736,12 @@ hipError_t dispatch_mode(const KParams& p, int grid, int opd, int vmode, bool t1
   hipError_t e;
   if constexpr (BF16 && ALIGNED) {
     // bf16 rows of a multiple of eight entries: the lighter supervision kernel.
-    if (opd && (vmode == 0 || (vmode == 2 && t1))) {
+    if (opd && (vmode == 0 || (vmode == 2 && t1)) && p.G <= 64) {
       if (vmode == 0 && fkl) e = launch_dominant(fsup_kernel<0, true>, grid, st, p);
       else if (vmode == 0) e = launch_dominant(fsup_kernel<0>, grid, st, p);
       else e = launch_dominant(fsup_kernel<2>, grid, st, p);
       if (e != hipSuccess || vmode == 0) return e;
-      return launch_final<BF16, ALIGNED, 2>(p, st);
+      return launch_final<BF16, ALIGNED, 2, true>(p, st);
     }
   }
   if (opd && vmode == 0 && fkl) e = launch_sup<BF16, ALIGNED, 0, true>(p, grid, st);
