@@ -11,8 +11,11 @@ SOURCES = ["adaflash_kernels.hip", "adaflash_length_head.hip", "adaflash_api.cpp
            "adaflash_noalloc.hip"]
 
 # Packed-FP32 VALU instructions are disabled for every HIP translation unit.
+# A local that shadows another is an error (a shadowed call epoch once tagged
+# the row-barrier records with the wrong value).
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-fvisibility=hidden",
+    "-Werror=shadow",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 

@@ -41,13 +41,15 @@ size_t workspace_layout(int B, int k, int V, char* base, Workspace* ws) {
     off = align_up(off + bytes);
     return base ? base + at : nullptr;
   };
+  char* epoch = take(sizeof(uint32_t));  // first: at the same place for every (B, k, V)
   char* Lc = take(sizeof(int32_t) * (size_t)(B + 1));
   char* rowmap = take(sizeof(int32_t) * (rows > 0 ? (size_t)B * k : 1));
   char* rowcnt = take(sizeof(int32_t) * kCounterStride * (rows > 0 ? rows : 1));
-  char* part1 = take(sizeof(float) * kRec1 * (rows > 0 ? rows : 1) * G);
-  char* part2 = take(sizeof(float) * kRec2 * (rows > 0 ? rows : 1) * G);
+  char* part1 = take(sizeof(uint64_t) * kRec1 * (rows > 0 ? rows : 1) * G);
+  char* part2 = take(sizeof(uint64_t) * kRec2 * (rows > 0 ? rows : 1) * G);
   char* rowrec = take(sizeof(float) * kRowRec * (rows > 0 ? rows : 1));
   if (ws) {
+    ws->epoch = (uint32_t*)epoch;
     ws->Lc = (int32_t*)Lc;
     ws->rowmap = (int32_t*)rowmap;
     ws->rowcnt = (int32_t*)rowcnt;

@@ -30,13 +30,16 @@ constexpr int kCounterStride = 64;
 // Floats per published chunk record.
 constexpr int kRec1 = 8, kRec2 = 4, kRowRec = 4;
 
-// Device scratch carved out of the caller's workspace.
+// Device scratch carved out of the caller's workspace.  The record arrays
+// have room for 64-bit fields (the bf16 supervision kernel tags every field
+// with the call's epoch).
 struct Workspace {
+  uint32_t* epoch;   // [1] at offset 0: call counter, advanced once per call on the device
   int32_t* Lc;       // [B+1]  clamped verify lengths; Lc[B] = rows in use N (0: none usable)
   int32_t* rowmap;   // [B*k]  packed draft row n -> 64 b + i (request b, position i)
   int32_t* rowcnt;   // [B*(k+1)*kCounterStride] per-row arrival counters (zeroed per call)
-  float* part1;      // [B*(k+1)*G*kRec1] per-chunk row statistics
-  float* part2;      // [B*(k+1)*G*kRec2] per-chunk supervision / residual partials
+  float* part1;      // [B*(k+1)*G*kRec1] per-chunk row statistics (64-bit fields: twice that)
+  float* part2;      // [B*(k+1)*G*kRec2] per-chunk supervision / residual partials (likewise)
   float* rowrec;     // [B*(k+1)*kRowRec] per-row accept flag and margin
 };
 

@@ -81,6 +81,7 @@ struct KParams {
   float* part1;
   float* part2;
   float* rowrec;
+  const uint32_t* epoch;  // this call's epoch (advanced by the pack kernel)
   int B, k, V, G;
   float kT;  // log2(e) / T (0 in greedy mode)
   float clip_c, lambda;
@@ -327,6 +328,81 @@ __device__ bool arrive_and_wait(int32_t* cnt, int target, int32_t* status, int* 
 
 __device__ __forceinline__ void flag(int32_t* status, int bits) {
   if (status) __hip_atomic_fetch_or(status, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Tagged record fields: a value and the call's epoch in one 64-bit word,
+// written and read with single agent-scope atomic accesses.  A reader that
+// finds the current epoch in a field holds that field's value from this call,
+// whatever the order in which the writer's stores and its arrival at the row
+// counter became visible: the writer counts its arrival without waiting for
+// its record stores to complete, and a reader re-reads only a field that is
+// not there yet.  The epoch word sits at the start of the workspace and grows
+// by one per call, so no field left by an earlier call (or any constant fill)
+// carries the current epoch.
+__device__ __forceinline__ void tag_store(float* base, size_t field, float v, uint32_t ep) {
+  __hip_atomic_store((uint64_t*)base + field, ((uint64_t)ep << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t tag_load(const float* base, size_t field) {
+  return __hip_atomic_load((uint64_t*)const_cast<float*>(base) + field, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float tag_value(uint64_t w) { return __uint_as_float((uint32_t)w); }
+__device__ __forceinline__ bool tag_is(uint64_t w, uint32_t ep) { return (uint32_t)(w >> 32) == ep; }
+
+// A wave waits until the counter reaches `target` (every lane reads the same
+// word: one request per poll).  Returns false when the wait hit its bound
+// (flagging the status word) or another wait already did.
+__device__ bool wait_count(const int32_t* cnt, int target, int32_t* status) {
+  int spins = 0;
+  while (__builtin_amdgcn_readfirstlane(
+             __hip_atomic_load(const_cast<int32_t*>(cnt), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < target) {
+    __builtin_amdgcn_s_sleep(4);
+    ++spins;
+    if (spins > kSpinLimit ||
+        ((spins & 63) == 0 && status &&
+         (__hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & ADAFLASH_FLAG_SYNC_TIMEOUT))) {
+      if ((threadIdx.x & 63) == 0) flag(status, ADAFLASH_FLAG_SYNC_TIMEOUT);
+      return false;
+    }
+  }
+  return true;
+}
+
+// A wave waits until, in every lane with `want`, fields [off, off + cnt) of
+// record `rec` at recs (records `stride` fields apart; cnt <= N) carry epoch
+// ep, and leaves their values in v[0 .. cnt).  Lanes poll only their own
+// incomplete fields.  Returns false when the wait hit its bound (flagging the
+// status word) or another wait already did.  Must be called by a whole wave.
+template <int N>
+__device__ bool poll_fields(const float* recs, int stride, bool want, int rec, int off, int cnt, uint32_t ep,
+                            float (&v)[N], int32_t* status) {
+  const int lane = threadIdx.x & 63;
+  bool done = !want;
+  int spins = 0;
+  for (;;) {
+    if (!done) {
+      uint64_t w[N];
+#pragma unroll
+      for (int n = 0; n < N; ++n) w[n] = n < cnt ? tag_load(recs, (size_t)rec * stride + off + n) : 0ull;
+      done = true;
+#pragma unroll
+      for (int n = 0; n < N; ++n) {
+        if (n < cnt) {
+          done = done && tag_is(w[n], ep);
+          v[n] = tag_value(w[n]);
+        }
+      }
+    }
+    if (__ballot(!done) == 0ull) return true;
+    __builtin_amdgcn_s_sleep(2);
+    ++spins;
+    if (spins > kSpinLimit ||
+        ((spins & 63) == 0 && status &&
+         (__hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & ADAFLASH_FLAG_SYNC_TIMEOUT))) {
+      if (lane == 0) flag(status, ADAFLASH_FLAG_SYNC_TIMEOUT);
+      return false;
+    }
+  }
 }
 
 // ------------------------------------------------------------ chunk storage
@@ -691,10 +767,11 @@ __device__ __forceinline__ unsigned int ukey(float x) {
 }
 
 // Draws the correction or bonus token for request b.  Runs on one workgroup.
-// LOG2REC: the chunk records hold their sums relative to powers of two (the
-// bf16 supervision kernel's records: reference exponents in rec[1] and rec[4],
-// in log2 units, at T = 1); otherwise relative to the chunk maxima rec[0] and
-// rec[4] of z / T.
+// LOG2REC: the records of the bf16 supervision kernel (64-bit tagged fields,
+// sums relative to powers of two with the exponents in fields 1 and 4, at
+// T = 1); otherwise float records relative to the chunk maxima rec[0] and
+// rec[4] of z / T.  (Both are complete here: the finaliser runs after the
+// kernel that wrote them.)
 template <bool BF16, bool ALIGNED, int VMODE, bool LOG2REC = false>
 __device__ void finalize_request(const KParams& P, int b, FinShared& fs) {
   const int k = P.k, V = P.V, G = P.G;
@@ -774,13 +851,24 @@ __device__ void finalize_request(const KParams& P, int b, FinShared& fs) {
       mq[h] = neg_inf();
       spT[h] = sqT[h] = res[h] = 0.f;
       if (jj < G) {
-        const float* rec = P.part1 + ((size_t)rs * G + jj) * kRec1;
-        mp[h] = pub_load(rec + (LOG2REC ? 1 : 0));
-        spT[h] = pub_load(rec + 2);
-        if (A < L) {
-          mq[h] = pub_load(rec + 4);
-          sqT[h] = pub_load(rec + 5);
-          res[h] = pub_load(P.part2 + ((size_t)rs * G + jj) * kRec2 + 2);
+        if constexpr (LOG2REC) {
+          const size_t f0 = ((size_t)rs * G + jj) * kRec1;
+          mp[h] = tag_value(tag_load(P.part1, f0 + 1));
+          spT[h] = tag_value(tag_load(P.part1, f0 + 2));
+          if (A < L) {
+            mq[h] = tag_value(tag_load(P.part1, f0 + 4));
+            sqT[h] = tag_value(tag_load(P.part1, f0 + 5));
+            res[h] = tag_value(tag_load(P.part2, ((size_t)rs * G + jj) * kRec2 + 2));
+          }
+        } else {
+          const float* rec = P.part1 + ((size_t)rs * G + jj) * kRec1;
+          mp[h] = pub_load(rec + 0);
+          spT[h] = pub_load(rec + 2);
+          if (A < L) {
+            mq[h] = pub_load(rec + 4);
+            sqT[h] = pub_load(rec + 5);
+            res[h] = pub_load(P.part2 + ((size_t)rs * G + jj) * kRec2 + 2);
+          }
         }
       }
     }
@@ -1232,6 +1320,7 @@ struct SupStats {
   // unclipped reverse KL, and the bound on the largest per-entry term.
   float lse_q2, lse_p2, D, KL, bound;
   float fkl;  // forward KL(p || q) of the row (forward-KL variant only)
+  int alive;  // the row's records arrived (bf16 supervision kernel; 0: the wait hit its bound)
 };
 
 __device__ __forceinline__ void derive_sup(float Mp, float Mq, float Sp, float Sq, float Wsum, float BA,
@@ -1392,28 +1481,30 @@ __device__ __forceinline__ int shift_of(float m) {
 // chunk's scale exponents), rec[2] = sum 2^(z_p log2 e - a_p), rec[5] the same
 // for z_q, rec[3] = W and rec[6] = A on the z_q scale, rec[7] = sum p' (z_q -
 // z_p) on the z_p scale (forward KL), rec[0] = the chunk's exact maximum of
-// z_p (x*: the lowest chunk holding the row maximum).  Wave 0 reduces them,
-// chunk j in lane j (G <= 64), and hands the results to the other waves
-// through fs.f; lse_q2 and lse_p2 are in log2 units.
+// z_p (x*: the lowest chunk holding the row maximum); every field is tagged
+// with the call's epoch.  Wave 0 waits for the row's G arrivals and for the
+// records (the row barrier), reduces them, chunk j in lane j (G <= 32), and
+// hands the results to the other waves through fs.f; lse_q2 and lse_p2 are
+// in log2 units.
 template <bool SAMPLED, bool FKL, typename SH>
-__device__ SupStats combine_sup_pow2(const KParams& P, int r, SH& fs, float zpx, float zqx, float u) {
+__device__ SupStats combine_sup_pow2(const KParams& P, int r, SH& fs, float zpx, float zqx, float u, uint32_t ep) {
   const int tid = threadIdx.x;
-  const int G = P.G;  // <= 64 (the host dispatches larger rows elsewhere)
+  const int G = P.G;  // <= 32 (the host dispatches larger rows elsewhere)
   if (tid < 64) {
-    float mx = neg_inf(), ap = neg_inf(), aq = neg_inf(), a = neg_inf();
-    float sp = 0.f, w = 0.f, sq = 0.f, wp = 0.f;
-    const bool valid = tid < G;
-    if (valid) {
-      const float* rec = P.part1 + ((size_t)r * G + tid) * kRec1;
-      mx = pub_load(rec + 0);
-      ap = pub_load(rec + 1);
-      sp = pub_load(rec + 2);
-      w = pub_load(rec + 3);
-      aq = pub_load(rec + 4);
-      sq = pub_load(rec + 5);
-      a = pub_load(rec + 6);
-      if (FKL) wp = pub_load(rec + 7);
-    }
+    // Lane c holds fields 0-3 of record c, lane 32 + c fields 4-7; the two
+    // halves then swap, and the reductions run over lanes c < G.
+    const int c = tid & 31, half = tid >> 5;
+    float h[4] = {0.f, 0.f, 0.f, 0.f};
+    const float* recs = (const float*)((const uint64_t*)P.part1 + (size_t)r * G * kRec1);
+    const bool ok = wait_count(P.rowcnt + (size_t)r * kCounterStride, G, P.status) &&
+                    poll_fields<4>(recs, kRec1, c < G, c, 4 * half, half && !FKL ? 3 : 4, ep, h, P.status);
+    float o[4];
+#pragma unroll
+    for (int n = 0; n < 4; ++n) o[n] = __shfl_xor(h[n], 32, 64);
+    const bool valid = half == 0 && c < G;
+    const float mx = valid ? h[0] : neg_inf(), ap = h[1], sp = valid ? h[2] : 0.f, w = valid ? h[3] : 0.f;
+    const float aq = o[0], sq = valid ? o[1] : 0.f, a = valid ? o[2] : neg_inf();
+    const float wp = FKL && valid ? o[3] : 0.f;
     // Scale exponents are integers in [-2^20, 2^20] (float in the record).
     const int api = valid ? (int)ap : -(1 << 21), aqi = valid ? (int)aq : -(1 << 21);
     const float Mx = wave_reduce<OP_MAX>(mx);
@@ -1431,6 +1522,7 @@ __device__ SupStats combine_sup_pow2(const KParams& P, int r, SH& fs, float zpx,
         __int_as_float(!valid || (__builtin_isfinite(w) && !__builtin_isnan(a) && a < __builtin_inff()) ? 0 : 1));
     v[6] = FKL ? wave_reduce<OP_SUM>(__builtin_ldexpf(wp, dp)) : 0.f;
     if (tid == 0) {
+      fs.i[2] = ok;
       const float rSp = __builtin_amdgcn_rcpf(v[0]), rSq = __builtin_amdgcn_rcpf(v[1]);
       const float lq = Aq + flog2(v[1]);
       const float lp = Ap + flog2(v[0]);
@@ -1470,6 +1562,7 @@ __device__ SupStats combine_sup_pow2(const KParams& P, int r, SH& fs, float zpx,
   s.bound = uniform(fs.f[13]);
   // Forward KL = sum p (log p - log q) = -E_p[z_q - z_p] + D.
   s.fkl = FKL ? uniform(-fs.f[14] / s.Sp + s.D) : 0.f;
+  s.alive = __builtin_amdgcn_readfirstlane(fs.i[2]);
   return s;
 }
 
@@ -1965,7 +2058,6 @@ __global__ __launch_bounds__(kThreads, 8) void fsup_kernel(KParams P) {
   constexpr int VEC = 8;
   constexpr int NV = kElems / VEC;
   __shared__ SupShared fs;
-  __shared__ int sh_ok;
   // exp(z_q - m) of this thread's draft entries from pass 1 (m: the thread's
   // maximum), as fp16 pairs, slot-major; each thread reads only what it wrote.
   __shared__ uint32_t ecache[kElems / 2 * kThreads];
@@ -1980,6 +2072,7 @@ __global__ __launch_bounds__(kThreads, 8) void fsup_kernel(KParams P) {
   const int k = P.k, V = P.V;
   const int s_ = (int)blockIdx.x / G;
   const int j = (int)blockIdx.x - s_ * G;
+  const uint32_t call_epoch = sload_u32(P.epoch);
   const RowSlot sl = row_slot(P, s_, VERIFY);
   if (sl.b < 0) return;
   const int b = sl.b, i = sl.i;
@@ -2103,12 +2196,12 @@ __global__ __launch_bounds__(kThreads, 8) void fsup_kernel(KParams P) {
       Apc = max(Apc, dpp_i<0x4E>(Apc));
       Aqc = max(Aqc, dpp_i<0xB1>(Aqc));
       Aqc = max(Aqc, dpp_i<0x4E>(Aqc));
-      const int ep = ap_l - Apc, eq = aq_l - Aqc;
-      float Sp = hw ? __builtin_ldexpf(wpart[wl][2], ep) : 0.f;
-      float Sq = hw ? __builtin_ldexpf(wpart[wl][4], eq) : 0.f;
-      float Ws = hw ? __builtin_ldexpf(wpart[wl][5], eq) : 0.f;
-      float As = hw ? __builtin_ldexpf(wpart[wl][6], eq) : neg_inf();
-      float Wps = FKL && hw ? __builtin_ldexpf(wpart[wl][7], ep) : 0.f;
+      const int sp_e = ap_l - Apc, sq_e = aq_l - Aqc;
+      float Sp = hw ? __builtin_ldexpf(wpart[wl][2], sp_e) : 0.f;
+      float Sq = hw ? __builtin_ldexpf(wpart[wl][4], sq_e) : 0.f;
+      float Ws = hw ? __builtin_ldexpf(wpart[wl][5], sq_e) : 0.f;
+      float As = hw ? __builtin_ldexpf(wpart[wl][6], sq_e) : neg_inf();
+      float Wps = FKL && hw ? __builtin_ldexpf(wpart[wl][7], sp_e) : 0.f;
       Sp += dpp_f<0xB1>(Sp);
       Sp += dpp_f<0x4E>(Sp);
       Sq += dpp_f<0xB1>(Sq);
@@ -2122,29 +2215,32 @@ __global__ __launch_bounds__(kThreads, 8) void fsup_kernel(KParams P) {
         Wps += dpp_f<0x4E>(Wps);
       }
       if (lane == 0) {
-        float* rec = P.part1 + ((size_t)r * G + j) * kRec1;
-        pub_store(rec + 0, Mp);
-        pub_store(rec + 1, (float)Apc);
-        pub_store(rec + 2, Sp);
-        pub_store(rec + 3, Ws);
-        pub_store(rec + 4, (float)Aqc);
-        pub_store(rec + 5, Sq);
-        pub_store(rec + 6, As);
-        if (FKL) pub_store(rec + 7, Wps);
+        const size_t f0 = ((size_t)r * G + j) * kRec1;
+        tag_store(P.part1, f0 + 0, Mp, call_epoch);
+        tag_store(P.part1, f0 + 1, (float)Apc, call_epoch);
+        tag_store(P.part1, f0 + 2, Sp, call_epoch);
+        tag_store(P.part1, f0 + 3, Ws, call_epoch);
+        tag_store(P.part1, f0 + 4, (float)Aqc, call_epoch);
+        tag_store(P.part1, f0 + 5, Sq, call_epoch);
+        tag_store(P.part1, f0 + 6, As, call_epoch);
+        if (FKL) tag_store(P.part1, f0 + 7, Wps, call_epoch);
+        if (draft_row)
+          __hip_atomic_fetch_add(P.rowcnt + (size_t)r * kCounterStride, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
   if (!draft_row) return;
 
-  bool alive = arrive_and_wait(&P.rowcnt[(size_t)r * kCounterStride], G, P.status, &sh_ok);
-  if (!alive) return;
+  // Wave 1 reads the accept flags of the earlier rows while wave 0 waits for
+  // the row's records.
   if (SAMPLED && wave == 1) {
     const int l = tid - 64;
     const bool rej = l < i && pub_load(P.rowrec + (size_t)(r - i + l) * kRowRec + 1) == 0.f;
     const unsigned long long any = __ballot(rej);
     if (l == 0) fs.i[0] = any != 0ull;
   }
-  const SupStats st = combine_sup_pow2<SAMPLED, FKL>(P, r, fs, zpx, zqx, u_acc);
+  const SupStats st = combine_sup_pow2<SAMPLED, FKL>(P, r, fs, zpx, zqx, u_acc, call_epoch);
+  if (!st.alive) return;
   const bool earlier_rejected = SAMPLED && fs.i[0] != 0;
   const float lse_q2 = st.lse_q2, lse_p2 = st.lse_p2, D = st.D, KL = st.KL;
   const float wi = P.wdecay > 0.f ? uniform(fexp2(-(float)i * kLog2e / P.wdecay)) : 1.f;
@@ -2280,23 +2376,30 @@ __global__ __launch_bounds__(kThreads, 8) void fsup_kernel(KParams P) {
     const int ops3[3] = {OP_SUM, OP_SUM, OP_SUM};
     wg_reduce<3>(s3, ops3, fs.red);
     if (tid == 0) {
-      float* rec = P.part2 + ((size_t)r * G + j) * kRec2;
-      pub_store(rec + 0, s3[0]);
-      pub_store(rec + 1, s3[1]);
-      if (SAMPLED) pub_store(rec + 2, s3[2]);
+      const size_t f0 = ((size_t)r * G + j) * kRec2;
+      tag_store(P.part2, f0 + 0, s3[0], call_epoch);
+      tag_store(P.part2, f0 + 1, s3[1], call_epoch);
+      if (SAMPLED) tag_store(P.part2, f0 + 2, s3[2], call_epoch);
+      __hip_atomic_fetch_add(P.rowcnt + (size_t)r * kCounterStride, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    alive = arrive_and_wait(&P.rowcnt[(size_t)r * kCounterStride], 2 * G, P.status, &sh_ok);
-    if (!alive) return;
-    float sr[2] = {0.f, 0.f};
-    if (tid < G) {
-      const float* rec = P.part2 + ((size_t)r * G + tid) * kRec2;
-      sr[0] = pub_load(rec + 0);
-      sr[1] = pub_load(rec + 1);
+    // Second row barrier: wave 0 waits for the G partial sums S and R.
+    if (wave == 0) {
+      float f2[2] = {0.f, 0.f};
+      const float* recs2 = (const float*)((const uint64_t*)P.part2 + (size_t)r * G * kRec2);
+      const bool ok = wait_count(P.rowcnt + (size_t)r * kCounterStride, 2 * G, P.status) &&
+                      poll_fields<2>(recs2, kRec2, lane < G, lane, 0, 2, call_epoch, f2, P.status);
+      const float S = wave_reduce<OP_SUM>(lane < G ? f2[0] : 0.f);
+      const float R = wave_reduce<OP_SUM>(lane < G ? f2[1] : 0.f);
+      if (lane == 0) {
+        fs.f[0] = S;
+        fs.f[1] = R;
+        fs.i[3] = ok;
+      }
     }
-    const int srops[2] = {OP_SUM, OP_SUM};
-    wg_reduce<2>(sr, srops, fs.red);
-    Rrow = sr[1];
-    const float lamS = uniform(lam * sr[0]);
+    __syncthreads();
+    if (!__builtin_amdgcn_readfirstlane(fs.i[3])) return;
+    Rrow = uniform(fs.f[1]);
+    const float lamS = uniform(lam * fs.f[0]);
     // Unclipped entries: g = q (ace - lambda S + lambda (dz - D + 1)).
     const float c1x = fmaf(lam, 1.f - D, ace) - lamS + afk;
     const float lsc = lam * sc, csc = c1x * sc;
@@ -2332,7 +2435,7 @@ __global__ __launch_bounds__(kThreads, 8) void fsup_kernel(KParams P) {
     float z1[1] = {Zpart};
     const int o1[1] = {OP_SUM};
     wg_reduce<1>(z1, o1, fs.red);
-    if (tid == 0) pub_store(P.part2 + ((size_t)r * G + j) * kRec2 + 2, z1[0]);
+    if (tid == 0) tag_store(P.part2, ((size_t)r * G + j) * kRec2 + 2, z1[0], call_epoch);
   }
   if (xs_here) {
     if (P.grad) ((uint16_t*)P.grad)[(size_t)n * V + xs] = __builtin_bit_cast(uint16_t, (__bf16)gstar);
@@ -2631,7 +2734,8 @@ __global__ __launch_bounds__(kThreads) void final_kernel(KParams P) {
 // row offsets (prefix sum: a scan inside each wave, then across the 16
 // waves), clears the arrival counters and marks the accept flags as not yet
 // known for the draft rows in use (the only rows that wait at a row barrier
-// or whose flags are read), and initialises the status word.
+// or whose flags are read), advances the workspace's call epoch and
+// initialises the status word.
 __global__ __launch_bounds__(1024) void pack_kernel(const int32_t* verify_len, int B, int k, int packed,
                                                      int32_t* row_offsets, Workspace ws, int32_t* status) {
   __shared__ int s_wave[16];
@@ -2687,6 +2791,7 @@ __global__ __launch_bounds__(1024) void pack_kernel(const int32_t* verify_len, i
   if (packed && s_flags)
     for (int b = tid; b < B; b += 1024) ws.Lc[b] = -1;
   if (tid == 0) {
+    ws.epoch[0] += 1u;
     row_offsets[B] = carry;
     ws.Lc[B] = packed && s_flags ? 0 : carry;  // rows the row kernels run on
     if (status) *status = s_flags;
@@ -2736,7 +2841,7 @@ hipError_t dispatch_mode(const KParams& p, int grid, int opd, int vmode, bool t1
   hipError_t e;
   if constexpr (BF16 && ALIGNED) {
     // bf16 rows of a multiple of eight entries: the lighter supervision kernel.
-    if (opd && (vmode == 0 || (vmode == 2 && t1)) && p.G <= 64) {
+    if (opd && (vmode == 0 || (vmode == 2 && t1)) && p.G <= 32) {
       if (vmode == 0 && fkl) e = launch_dominant(fsup_kernel<0, true>, grid, st, p);
       else if (vmode == 0) e = launch_dominant(fsup_kernel<0>, grid, st, p);
       else e = launch_dominant(fsup_kernel<2>, grid, st, p);
@@ -2824,6 +2929,7 @@ hipError_t launch(const LaunchArgs& a) {
   p.part1 = a.ws.part1;
   p.part2 = a.ws.part2;
   p.rowrec = a.ws.rowrec;
+  p.epoch = a.ws.epoch;
   p.B = a.B;
   p.k = a.k;
   p.V = a.V;

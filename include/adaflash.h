@@ -27,7 +27,8 @@
  * Conventions shared by every entry point
  *  - All array arguments are DEVICE pointers owned by the caller; the library
  *    allocates nothing and keeps no state between calls (the measurement
- *    hook adaflash_timing_enable aside, which owns its HIP events).  Calls are enqueued
+ *    hook adaflash_timing_enable aside, which owns its HIP events; a
+ *    workspace carries only its call counter from one call to the next).  Calls are enqueued
  *    on `stream` (a hipStream_t; NULL = the null stream) and return without
  *    synchronising.  Concurrent calls must use distinct workspaces.
  *  - Logits are row-major, contiguous; `dtype` selects fp32 or bf16 (raw
@@ -83,7 +84,10 @@ typedef enum { ADAFLASH_F32 = 0, ADAFLASH_BF16 = 1 } adaflash_dtype;
 ADAFLASH_API int adaflash_version(void);
 
 /* Bytes of device workspace either entry point needs for these sizes
- * (0 on invalid sizes).  The workspace needs no initialisation. */
+ * (0 on invalid sizes).  The workspace needs no initialisation: its first
+ * word is a call counter that each call advances on the device (any initial
+ * value works), so that cross-workgroup records left by earlier calls are
+ * never mistaken for the current call's. */
 ADAFLASH_API size_t adaflash_workspace_bytes(int B, int k, int V);
 
 /* Description of the last error returned on this thread ("" if none). */
@@ -169,7 +173,7 @@ ADAFLASH_API int adaflash_verify(adaflash_dtype dtype, const void* target_logits
  * address is looked up on the first call on each device; it calls no
  * allocating routine.  Returns ADAFLASH_E_UNSUPPORTED, with nothing enqueued,
  * when adaflash_workspace_bytes(B, k, V) exceeds that size (at V = 151936 and
- * k = 16 up to about 800 requests fit).  Every call on one GPU shares the
+ * k = 16 up to about 460 requests fit).  Every call on one GPU shares the
  * array and initialises what it reads: calls that overlap on one GPU (other
  * streams or host threads) race, and the caller must order them.
  */
