@@ -7,8 +7,8 @@ import subprocess
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB_PATH = os.path.join(PKG, "libadaflash.so")
-SOURCES = ["adaflash_kernels.hip", "adaflash_length_head.hip", "adaflash_api.cpp", "adaflash_admission.cpp",
-           "adaflash_noalloc.hip"]
+SOURCES = ["adaflash_kernels.hip", "adaflash_length_head.hip", "adaflash_api.cpp", "adaflash_layout.cpp",
+           "adaflash_admission.cpp", "adaflash_noalloc.hip"]
 
 # Packed-FP32 VALU instructions are disabled for every HIP translation unit.
 # A local that shadows another is an error (a shadowed call epoch once tagged

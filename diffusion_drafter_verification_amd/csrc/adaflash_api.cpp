@@ -22,8 +22,6 @@ int fail(int code, const char* fmt, const char* detail = "") {
   return code;
 }
 
-inline size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
-
 bool sizes_ok(int B, int k, int V) {
   if (B < 0 || k < 1 || k > kMaxK || V < 1 || V > kMaxV) return false;
   if ((long long)B * (k + 1) >= (1LL << 24)) return false;
@@ -31,34 +29,6 @@ bool sizes_ok(int B, int k, int V) {
 }
 
 }  // namespace
-
-size_t workspace_layout(int B, int k, int V, char* base, Workspace* ws) {
-  const size_t rows = (size_t)B * (k + 1);
-  const size_t G = (size_t)num_chunks(V);
-  size_t off = 0;
-  auto take = [&](size_t bytes) {
-    size_t at = off;
-    off = align_up(off + bytes);
-    return base ? base + at : nullptr;
-  };
-  char* epoch = take(sizeof(uint32_t));  // first: at the same place for every (B, k, V)
-  char* Lc = take(sizeof(int32_t) * (size_t)(B + 1));
-  char* rowmap = take(sizeof(int32_t) * (rows > 0 ? (size_t)B * k : 1));
-  char* rowcnt = take(sizeof(int32_t) * kCounterStride * (rows > 0 ? rows : 1));
-  char* part1 = take(sizeof(uint64_t) * kRec1 * (rows > 0 ? rows : 1) * G);
-  char* part2 = take(sizeof(uint64_t) * kRec2 * (rows > 0 ? rows : 1) * G);
-  char* rowrec = take(sizeof(float) * kRowRec * (rows > 0 ? rows : 1));
-  if (ws) {
-    ws->epoch = (uint32_t*)epoch;
-    ws->Lc = (int32_t*)Lc;
-    ws->rowmap = (int32_t*)rowmap;
-    ws->rowcnt = (int32_t*)rowcnt;
-    ws->part1 = (float*)part1;
-    ws->part2 = (float*)part2;
-    ws->rowrec = (float*)rowrec;
-  }
-  return off;
-}
 
 }  // namespace adaflash
 

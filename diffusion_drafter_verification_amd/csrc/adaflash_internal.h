@@ -109,6 +109,15 @@ struct LhWorkspace {
 
 size_t lh_workspace_layout(int B, int k, int H, int Hp, char* base, LhWorkspace* ws);
 
+// Output tile of the length head's products (rows and columns per workgroup),
+// and the split of a reduction of length K over slices for a product with
+// `tiles` output tiles.
+constexpr int kLhTile = 64;
+struct LhSplit {
+  int S, kslice;
+};
+LhSplit lh_split_k(int K, long long tiles);
+
 struct LhArgs {
   const uint16_t* h;   // [B, k, H] bf16
   const uint16_t* W1;  // [Hp, H] bf16

@@ -33,7 +33,7 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kLhThreads = 256;  // four waves, one 32 x 32 output tile each
-constexpr int kTile = 64;        // output tile per workgroup (rows and columns)
+constexpr int kTile = kLhTile;   // output tile per workgroup (rows and columns)
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.f / (1.f + __expf(-x)); }
 
@@ -336,66 +336,14 @@ __global__ __launch_bounds__(kLhThreads) void lh_small_grads(const float* __rest
   }
 }
 
-// Split of a reduction of length K for a product with `tiles` output tiles:
-// enough slices for about 1024 workgroups, each slice a multiple of 16 and at
-// least 256 long.
-struct Split {
-  int S, kslice;
-};
-Split split_k(int K, long long tiles) {
-  if (tiles < 1) tiles = 1;  // (an empty product)
-  long long want = (1024 + tiles - 1) / tiles;
-  long long maxs = K / 256 > 0 ? K / 256 : 1;
-  int S = (int)(want < 1 ? 1 : (want > maxs ? maxs : want));
-  int ks = (K + S - 1) / S;
-  ks = ks < 16 ? 16 : (ks + 15) & ~15;
-  S = K > 0 ? (K + ks - 1) / ks : 1;
-  return {S, ks};
-}
-
 }  // namespace
-
-size_t lh_workspace_layout(int B, int k, int H, int Hp, char* base, LhWorkspace* ws) {
-  const size_t M = (size_t)B * k;
-  const size_t Mp = (M + 15) & ~size_t(15);
-  const size_t ntiles = (M + kTile - 1) / kTile;
-  const Split sf = split_k(H, (long long)ntiles * ((Hp + kTile - 1) / kTile));
-  const Split sb = split_k((int)Mp, (long long)((Hp + kTile - 1) / kTile) * ((H + kTile - 1) / kTile));
-  size_t off = 0;
-  auto take = [&](size_t bytes) {
-    size_t at = off;
-    off = (off + bytes + 255) & ~size_t(255);
-    return base ? base + at : nullptr;
-  };
-  char* z1 = take(sizeof(float) * sf.S * M * Hp);
-  char* zsum = take(sizeof(float) * M * Hp);
-  char* hbar = take(sizeof(float) * (size_t)B * Hp);
-  char* ds = take(sizeof(float) * (size_t)B);
-  char* dzh = take(sizeof(uint16_t) * Mp * Hp);
-  char* dzl = take(sizeof(uint16_t) * Mp * Hp);
-  char* part = take(sizeof(float) * (size_t)B * Hp);
-  char* hT = take(sizeof(uint16_t) * (size_t)H * Mp);
-  char* dwp = take(sizeof(float) * sb.S * (size_t)Hp * H);
-  if (ws) {
-    ws->z1 = (float*)z1;
-    ws->zsum = (float*)zsum;
-    ws->hbar = (float*)hbar;
-    ws->ds = (float*)ds;
-    ws->dzh = (uint16_t*)dzh;
-    ws->dzl = (uint16_t*)dzl;
-    ws->db1_part = (float*)part;
-    ws->hT = (uint16_t*)hT;
-    ws->dw_part = (float*)dwp;
-  }
-  return off;
-}
 
 hipError_t lh_launch(const LhArgs& a) {
   const int M = a.B * a.k;
   const int Mp = (M + 15) & ~15;
   if (M == 0) return hipSuccess;
   const int mt = (M + kTile - 1) / kTile, nt = (a.Hp + kTile - 1) / kTile;
-  const Split sf = split_k(a.H, (long long)mt * nt);
+  const LhSplit sf = lh_split_k(a.H, (long long)mt * nt);
   const bool bwd = a.accept_len != nullptr;
   hipError_t e = hipSuccess;
   // The projection Z1 = h W1^T: from the caller's copy of the forward's, or
@@ -427,7 +375,7 @@ hipError_t lh_launch(const LhArgs& a) {
   if (e != hipSuccess) return e;
   // dW1 [H' x H] = (dZ1^T high + remainder) [H' x Mp] . (h^T)^T, reduction over Mp.
   const int rt = nt, ct = (a.H + kTile - 1) / kTile;
-  const Split sb = split_k(Mp, (long long)rt * ct);
+  const LhSplit sb = lh_split_k(Mp, (long long)rt * ct);
   hipLaunchKernelGGL((lh_gemm_tn<true>), dim3(rt, ct, sb.S), dim3(kLhThreads), 0, a.stream, a.ws.dzh, a.ws.dzl, Mp,
                      a.ws.hT, Mp, a.ws.dw_part, a.Hp, a.H, Mp, sb.kslice);
   e = hipGetLastError();

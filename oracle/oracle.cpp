@@ -287,7 +287,9 @@ int oracle_verify(int dtype, const void* target, const void* draft, const int32_
 //   Packed row n is (b, i) with i < L_b, in request order (L_b = verify_len[b]
 //   clamped to [1, k], or k when verify_len is NULL).  `rows` lists the packed
 //   rows to evaluate (NULL: all of them, in order); results are written at the
-//   position of each row in that list.  grad [nrows, V] may be NULL.
+//   position of each row in that list.  loss_ce and loss_rkl [nrows] are
+//   required when any row is evaluated; grad [nrows, V] may be NULL.  With
+//   rows non-NULL and nrows == 0 nothing is evaluated (only N is returned).
 //   Returns the number of packed rows N, or a negative value on bad arguments.
 int64_t oracle_opd(int dtype, const void* target, const void* draft, const int32_t* verify_len,
                    int B, int k, int V, double c, double lambda, const int64_t* rows, int64_t nrows,
@@ -305,6 +307,7 @@ int64_t oracle_opd(int dtype, const void* target, const void* draft, const int32
   }
   const int64_t N = (int64_t)row_b.size();
   const int64_t n_eval = rows ? nrows : N;
+  if (n_eval < 0 || (n_eval > 0 && (!loss_ce || !loss_rkl))) return -1;
   for (int64_t j = 0; j < n_eval; ++j)
     if (rows && (rows[j] < 0 || rows[j] >= N)) return -2;
 
