@@ -71,6 +71,8 @@ def load_library() -> ctypes.CDLL:
         lib.adaflash_timing_enable.argtypes = [i32]
         lib.adaflash_timing_read.restype = i32
         lib.adaflash_timing_read.argtypes = [ctypes.POINTER(ctypes.c_float), i32]
+        lib.adaflash_timing_every.restype = i32
+        lib.adaflash_timing_every.argtypes = [i32]
         lib.adaflash_verify_packed.restype = i32
         lib.adaflash_verify_packed.argtypes = lib.adaflash_verify.argtypes
         lib.adaflash_opd_loss_fwd_bwd_packed.restype = i32
@@ -190,9 +192,38 @@ def _check(rc: int):
         raise AdaflashError(rc, load_library().adaflash_last_error().decode())
 
 
+class PreparedCall:
+    """One entry-point call, checked and marshalled once, for repetition:
+    run() repeats the C call with the same tensors, sizes and stream (the
+    tensors must keep their storage, shapes and dtypes meanwhile; the object
+    holds references to them).  Returned by the direct bindings when called
+    with prepare=True."""
+
+    def __init__(self, fn, args, keep):
+        self._fn = fn
+        self._args = tuple(t(a) for t, a in zip(fn.argtypes, args))
+        self._keep = keep
+
+    def run(self) -> None:
+        rc = self._fn(*self._args)
+        if rc != 0:
+            _check(rc)
+
+
+def _invoke(fn, args, keep, prepare: bool):
+    if prepare:
+        return PreparedCall(fn, args, keep)
+    _check(fn(*args))
+
+
 def adaflash_timing_enable(max_records: int) -> None:
     """Direct binding of adaflash_timing_enable (benchmark hook)."""
     _check(load_library().adaflash_timing_enable(int(max_records)))
+
+
+def adaflash_timing_every(n: int) -> None:
+    """Direct binding of adaflash_timing_every (events on every n-th call)."""
+    _check(load_library().adaflash_timing_every(int(n)))
 
 
 def adaflash_timing_read(cap: int) -> list:
@@ -218,7 +249,7 @@ def workspace(B: int, k: int, V: int, device="cuda") -> torch.Tensor:
 
 def adaflash_verify(target, draft, tokens, verify_len, uniforms, T, accept_len, out_tokens, margins,
                     clip_c, lam, row_offsets, loss_ce, loss_rkl, grad_draft, status, ws,
-                    stream=None) -> None:
+                    stream=None, prepare: bool = False):
     """Direct binding of adaflash_verify (see include/adaflash.h)."""
     _logits(target, "target", 3)
     B, k1, V = target.shape
@@ -230,19 +261,22 @@ def adaflash_verify(target, draft, tokens, verify_len, uniforms, T, accept_len, 
     _arg(uniforms, "uniforms", torch.float32, (B, k + 1), optional=(T == 0))
     _check_outputs(B, k, V, target.dtype, B * k, accept_len, out_tokens, margins, row_offsets, loss_ce, loss_rkl,
                    grad_draft, status, ws)
-    rc = load_library().adaflash_verify(
+    args = (
         _dtype_code(target), _ptr(target), _ptr(draft), _ptr(tokens), _ptr(verify_len), _ptr(uniforms),
         B, k1 - 1, V, float(T), _ptr(accept_len), _ptr(out_tokens), _ptr(margins), float(clip_c),
         float(lam), _ptr(row_offsets), _ptr(loss_ce), _ptr(loss_rkl), _ptr(grad_draft), _ptr(status),
         _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
-    _check(rc)
+    keep = (accept_len, draft, grad_draft, loss_ce, loss_rkl, margins, out_tokens, row_offsets, status, target,
+            tokens, uniforms, verify_len, ws)
+    return _invoke(load_library().adaflash_verify, args, keep, prepare)
 
 
 NOALLOC_WORKSPACE_BYTES = 16 << 20  # ADAFLASH_NOALLOC_WORKSPACE_BYTES
 
 
 def adaflash_verify_noalloc(target, draft, tokens, verify_len, uniforms, T, accept_len, out_tokens, margins,
-                            clip_c, lam, row_offsets, loss_ce, loss_rkl, grad_draft, status, stream=None) -> None:
+                            clip_c, lam, row_offsets, loss_ce, loss_rkl, grad_draft, status, stream=None,
+                            prepare: bool = False):
     """Direct binding of adaflash_verify_noalloc: adaflash_verify without a
     workspace argument (the library's own device array is used; calls that
     overlap on one GPU race)."""
@@ -256,16 +290,18 @@ def adaflash_verify_noalloc(target, draft, tokens, verify_len, uniforms, T, acce
     _arg(uniforms, "uniforms", torch.float32, (B, k + 1), optional=(T == 0))
     _check_outputs(B, k, V, target.dtype, B * k, accept_len, out_tokens, margins, row_offsets, loss_ce, loss_rkl,
                    grad_draft, status)
-    rc = load_library().adaflash_verify_noalloc(
+    args = (
         _dtype_code(target), _ptr(target), _ptr(draft), _ptr(tokens), _ptr(verify_len), _ptr(uniforms),
         B, k, V, float(T), _ptr(accept_len), _ptr(out_tokens), _ptr(margins), float(clip_c),
         float(lam), _ptr(row_offsets), _ptr(loss_ce), _ptr(loss_rkl), _ptr(grad_draft), _ptr(status),
         _stream(stream))
-    _check(rc)
+    keep = (accept_len, draft, grad_draft, loss_ce, loss_rkl, margins, out_tokens, row_offsets, status, target,
+            tokens, uniforms, verify_len)
+    return _invoke(load_library().adaflash_verify_noalloc, args, keep, prepare)
 
 
 def adaflash_opd_loss_fwd_bwd(target, draft, verify_len, clip_c, lam, row_offsets, loss_ce,
-                              loss_rkl, grad_draft, status, ws, stream=None) -> None:
+                              loss_rkl, grad_draft, status, ws, stream=None, prepare: bool = False):
     """Direct binding of adaflash_opd_loss_fwd_bwd (see include/adaflash.h)."""
     _logits(target, "target", 3)
     B, k1, V = target.shape
@@ -273,16 +309,17 @@ def adaflash_opd_loss_fwd_bwd(target, draft, verify_len, clip_c, lam, row_offset
     _arg(verify_len, "verify_len", torch.int32, (B,), optional=True)
     _check_outputs(B, k1 - 1, V, target.dtype, B * (k1 - 1), row_offsets=row_offsets, loss_ce=loss_ce,
                    loss_rkl=loss_rkl, grad=grad_draft, status=status, ws=ws, verify=False)
-    rc = load_library().adaflash_opd_loss_fwd_bwd(
+    args = (
         _dtype_code(target), _ptr(target), _ptr(draft), _ptr(verify_len), B, k1 - 1, V, float(clip_c),
         float(lam), _ptr(row_offsets), _ptr(loss_ce), _ptr(loss_rkl), _ptr(grad_draft), _ptr(status),
         _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
-    _check(rc)
+    keep = (draft, grad_draft, loss_ce, loss_rkl, row_offsets, status, target, verify_len, ws)
+    return _invoke(load_library().adaflash_opd_loss_fwd_bwd, args, keep, prepare)
 
 
 def adaflash_verify_packed(target, draft, tokens, verify_len, uniforms, T, accept_len, out_tokens, margins,
                            clip_c, lam, row_offsets, loss_ce, loss_rkl, grad_draft, status, ws,
-                           stream=None) -> None:
+                           stream=None, prepare: bool = False):
     """Direct binding of adaflash_verify_packed: target [sum(L_b+1), V], draft
     [sum L_b, V]; B and k come from tokens [B, k].  The row counts must match
     the device-side verify lengths (sum(L_b + 1) and sum L_b rows): the library
@@ -307,16 +344,18 @@ def adaflash_verify_packed(target, draft, tokens, verify_len, uniforms, T, accep
     _arg(uniforms, "uniforms", torch.float32, (B, k + 1), optional=(T == 0))
     _check_outputs(B, k, V, target.dtype, n_rows, accept_len, out_tokens, margins, row_offsets, loss_ce, loss_rkl,
                    grad_draft, status, ws)
-    rc = load_library().adaflash_verify_packed(
+    args = (
         _dtype_code(target), _ptr(target), _ptr(draft), _ptr(tokens), _ptr(verify_len), _ptr(uniforms),
         B, k, V, float(T), _ptr(accept_len), _ptr(out_tokens), _ptr(margins), float(clip_c),
         float(lam), _ptr(row_offsets), _ptr(loss_ce), _ptr(loss_rkl), _ptr(grad_draft), _ptr(status),
         _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
-    _check(rc)
+    keep = (accept_len, draft, grad_draft, loss_ce, loss_rkl, margins, out_tokens, row_offsets, status, target,
+            tokens, uniforms, verify_len, ws)
+    return _invoke(load_library().adaflash_verify_packed, args, keep, prepare)
 
 
 def adaflash_opd_loss_fwd_bwd_packed(target, draft, verify_len, k, clip_c, lam, row_offsets, loss_ce,
-                                     loss_rkl, grad_draft, status, ws, stream=None) -> None:
+                                     loss_rkl, grad_draft, status, ws, stream=None, prepare: bool = False):
     """Direct binding of adaflash_opd_loss_fwd_bwd_packed: target
     [sum(L_b+1), V], draft [sum L_b, V]; B from verify_len [B]."""
     _logits(target, "target", 2)
@@ -332,11 +371,12 @@ def adaflash_opd_loss_fwd_bwd_packed(target, draft, verify_len, k, clip_c, lam, 
                          f"{tuple(draft.shape)} for target {tuple(target.shape)}, B = {B}, k = {k}")
     _check_outputs(B, int(k), V, target.dtype, draft.shape[0], row_offsets=row_offsets, loss_ce=loss_ce,
                    loss_rkl=loss_rkl, grad=grad_draft, status=status, ws=ws, verify=False)
-    rc = load_library().adaflash_opd_loss_fwd_bwd_packed(
+    args = (
         _dtype_code(target), _ptr(target), _ptr(draft), _ptr(verify_len), B, int(k), V, float(clip_c),
         float(lam), _ptr(row_offsets), _ptr(loss_ce), _ptr(loss_rkl), _ptr(grad_draft), _ptr(status),
         _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
-    _check(rc)
+    keep = (draft, grad_draft, loss_ce, loss_rkl, row_offsets, status, target, verify_len, ws)
+    return _invoke(load_library().adaflash_opd_loss_fwd_bwd_packed, args, keep, prepare)
 
 
 def verify(target: torch.Tensor, draft: Optional[torch.Tensor], tokens: torch.Tensor,
@@ -448,7 +488,7 @@ LOSS_VARIANTS = {"rkl": 1, "rkl_clip": 2, "mixture": 3, "fkl": 4, "wce": 5}
 
 
 def adaflash_loss_variant_fwd_bwd(target, draft, verify_len, variant, p1, p2, row_offsets, loss, grad_draft, status,
-                                  ws, stream=None) -> None:
+                                  ws, stream=None, prepare: bool = False):
     """Direct binding of adaflash_loss_variant_fwd_bwd (see include/adaflash.h)."""
     _logits(target, "target", 3)
     B, k1, V = target.shape
@@ -457,11 +497,12 @@ def adaflash_loss_variant_fwd_bwd(target, draft, verify_len, variant, p1, p2, ro
     _check_outputs(B, k1 - 1, V, target.dtype, B * (k1 - 1), row_offsets=row_offsets, loss_ce=loss, grad=grad_draft,
                    status=status, ws=ws, verify=False)
     code = LOSS_VARIANTS[variant] if isinstance(variant, str) else int(variant)
-    rc = load_library().adaflash_loss_variant_fwd_bwd(
+    args = (
         _dtype_code(target), _ptr(target), _ptr(draft), _ptr(verify_len), B, k1 - 1, V, code, float(p1),
         float(p2), _ptr(row_offsets), _ptr(loss), _ptr(grad_draft), _ptr(status), _ptr(ws),
         ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
-    _check(rc)
+    keep = (draft, grad_draft, loss, row_offsets, status, target, verify_len, ws)
+    return _invoke(load_library().adaflash_loss_variant_fwd_bwd, args, keep, prepare)
 
 
 def loss_variant_fwd_bwd(target: torch.Tensor, draft: torch.Tensor, verify_len: Optional[torch.Tensor], variant,
@@ -498,50 +539,65 @@ def length_head_workspace(B: int, k: int, H: int, Hp: int, device="cuda") -> tor
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
-def _bf16(t: torch.Tensor) -> torch.Tensor:
-    if t.dtype != torch.bfloat16:
-        raise TypeError("hidden states and W1 must be bfloat16")
-    return t
+def _lh_inputs(hidden, W1, b1, w2):
+    _arg(hidden, "hidden", torch.bfloat16)
+    if hidden.dim() != 3:
+        raise ValueError(f"hidden must be [B, k, H], got {tuple(hidden.shape)}")
+    B, k, H = hidden.shape
+    _arg(W1, "W1", torch.bfloat16)
+    if W1.dim() != 2 or W1.shape[1] != H:
+        raise ValueError(f"W1 must be [H', {H}], got {tuple(W1.shape)}")
+    Hp = W1.shape[0]
+    _arg(b1, "b1", torch.float32, (Hp,))
+    _arg(w2, "w2", torch.float32, (Hp,))
+    return B, k, H, Hp
 
 
-def _f32(t: torch.Tensor) -> torch.Tensor:
-    if t.dtype != torch.float32:
-        raise TypeError("b1 and w2 must be float32")
-    return t
+def _lh_workspace(ws):
+    if ws is not None and ws.dtype != torch.uint8:
+        raise TypeError("the workspace must be a uint8 tensor (its size is counted in bytes)")
+    return ws.numel() * ws.element_size() if ws is not None else 0
 
 
 def adaflash_length_head_forward(hidden, W1, b1, w2, b2, gamma, a_hat, k_hat, ws, stream=None,
-                                 z1_cache=None) -> None:
+                                 z1_cache=None, prepare: bool = False):
     """Direct binding of adaflash_length_head_forward, or of
     adaflash_length_head_forward_cached when z1_cache ([B k, H'] fp32) is given."""
-    B, k, H = hidden.shape
-    Hp = W1.shape[0]
+    B, k, H, Hp = _lh_inputs(hidden, W1, b1, w2)
+    _arg(a_hat, "a_hat", torch.float32, (B,), optional=True)
+    _arg(k_hat, "k_hat", torch.int32, (B,), optional=True)
+    _arg(z1_cache, "z1_cache", torch.float32, (B * k, Hp), optional=True)
     lib = load_library()
-    head = (_ptr(_bf16(hidden)), _ptr(_bf16(W1)), _ptr(_f32(b1)), _ptr(_f32(w2)), float(b2), B, k, H, Hp,
-            float(gamma), _ptr(a_hat), _ptr(k_hat))
-    tail = (_ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
+    head = (_ptr(hidden), _ptr(W1), _ptr(b1), _ptr(w2), float(b2), B, k, H, Hp, float(gamma), _ptr(a_hat),
+            _ptr(k_hat))
+    tail = (_ptr(ws), _lh_workspace(ws), _stream(stream))
+    keep = (hidden, W1, b1, w2, a_hat, k_hat, z1_cache, ws)
     if z1_cache is None:
-        rc = lib.adaflash_length_head_forward(*head, *tail)
-    else:
-        rc = lib.adaflash_length_head_forward_cached(*head, _ptr(z1_cache), *tail)
-    _check(rc)
+        return _invoke(lib.adaflash_length_head_forward, head + tail, keep, prepare)
+    return _invoke(lib.adaflash_length_head_forward_cached, head + (_ptr(z1_cache),) + tail, keep, prepare)
 
 
 def adaflash_length_head_backward(hidden, W1, b1, w2, b2, accept_len, verify_len, loss, dW1, db1, dw2, db2, ws,
-                                  stream=None, z1_cache=None) -> None:
+                                  stream=None, z1_cache=None, prepare: bool = False):
     """Direct binding of adaflash_length_head_backward, or of
     adaflash_length_head_backward_cached when z1_cache (the forward's) is given."""
-    B, k, H = hidden.shape
-    Hp = W1.shape[0]
+    B, k, H, Hp = _lh_inputs(hidden, W1, b1, w2)
+    _arg(accept_len, "accept_len", torch.int32, (B,))
+    _arg(verify_len, "verify_len", torch.int32, (B,))
+    _arg(loss, "loss", torch.float32, (B,), optional=True)
+    _arg(dW1, "dW1", torch.float32, (Hp, H), optional=True)
+    _arg(db1, "db1", torch.float32, (Hp,), optional=True)
+    _arg(dw2, "dw2", torch.float32, (Hp,), optional=True)
+    _arg(db2, "db2", torch.float32, min_rows=1, optional=True)
+    _arg(z1_cache, "z1_cache", torch.float32, (B * k, Hp), optional=True)
     lib = load_library()
-    head = (_ptr(_bf16(hidden)), _ptr(_bf16(W1)), _ptr(_f32(b1)), _ptr(_f32(w2)), float(b2), B, k, H, Hp,
-            _ptr(accept_len), _ptr(verify_len), _ptr(loss), _ptr(dW1), _ptr(db1), _ptr(dw2), _ptr(db2))
-    tail = (_ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
+    head = (_ptr(hidden), _ptr(W1), _ptr(b1), _ptr(w2), float(b2), B, k, H, Hp, _ptr(accept_len), _ptr(verify_len),
+            _ptr(loss), _ptr(dW1), _ptr(db1), _ptr(dw2), _ptr(db2))
+    tail = (_ptr(ws), _lh_workspace(ws), _stream(stream))
+    keep = (hidden, W1, b1, w2, accept_len, verify_len, loss, dW1, db1, dw2, db2, z1_cache, ws)
     if z1_cache is None:
-        rc = lib.adaflash_length_head_backward(*head, *tail)
-    else:
-        rc = lib.adaflash_length_head_backward_cached(*head, _ptr(z1_cache), *tail)
-    _check(rc)
+        return _invoke(lib.adaflash_length_head_backward, head + tail, keep, prepare)
+    return _invoke(lib.adaflash_length_head_backward_cached, head + (_ptr(z1_cache),) + tail, keep, prepare)
 
 
 def length_head_forward(hidden: torch.Tensor, W1: torch.Tensor, b1: torch.Tensor, w2: torch.Tensor, b2: float,

@@ -44,6 +44,11 @@ int adaflash_timing_enable(int max_records) {
   return ADAFLASH_OK;
 }
 
+int adaflash_timing_every(int n) {
+  if (timing_every(n) != 0) return fail(ADAFLASH_E_INVALID, "n must be at least 1%s");
+  return ADAFLASH_OK;
+}
+
 int adaflash_timing_read(float* ms, int cap) {
   if (cap < 0 || (cap > 0 && !ms)) return fail(ADAFLASH_E_INVALID, "bad output buffer%s");
   const int n = timing_read(ms, cap);

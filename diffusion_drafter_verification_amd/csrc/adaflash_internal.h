@@ -93,6 +93,7 @@ int fail_with(int code, const char* msg);
 // Measurement hook (adaflash_timing_enable / adaflash_timing_read).
 int timing_enable(int cap);
 int timing_read(float* ms, int cap);
+int timing_every(int n);
 
 // Adaptive length head (adaflash_length_head.hip).
 struct LhWorkspace {

@@ -70,12 +70,12 @@ struct KParams {
   int32_t* accept_len;
   int32_t* out_tokens;
   float* margins;
-  const int32_t* row_offsets;
+  int32_t* row_offsets;
   float* loss_ce;
   float* loss_rkl;
   void* grad;
   int32_t* status;
-  const int32_t* Lc;
+  int32_t* Lc;
   const int32_t* rowmap;
   int32_t* rowcnt;
   float* part1;
@@ -93,6 +93,11 @@ struct KParams {
   // Logit layout: 0 = padded [B, k+1, V] / [B, k, V]; 1 = packed
   // [sum (L_b + 1), V] / [sum L_b, V] (rows located through row_offsets).
   int packed;
+  // Verify-only, padded layout: the first kernel's block 0 does the pack
+  // kernel's work (clamped lengths, row offsets, status word), and the other
+  // blocks clamp their own request's length from verify_len.
+  int pack_here;
+  const int32_t* verify_len;
 };
 
 // ---------------------------------------------------------------- primitives
@@ -620,12 +625,19 @@ __device__ __forceinline__ RowSlot row_slot(const KParams& P, int s, bool bonus)
   }
   return o;
 }
+// L_b = verify_len[b] clamped to [1, k] (k when verify_len is NULL).
+__device__ __forceinline__ int clamp_len(const KParams& P, int b) {
+  const int L = P.verify_len ? (int)sload_u32(P.verify_len + b) : P.k;
+  return L < 1 ? 1 : (L > P.k ? P.k : L);
+}
+
 __device__ __forceinline__ RowSlot row_slot_interleaved(const KParams& P, int s, bool bonus) {
   RowSlot o;
   o.b = s / (P.k + 1);
   o.i = s - o.b * (P.k + 1);
-  const int L = (int)sload_u32(P.Lc + o.b);
-  const int off = (int)sload_u32(P.row_offsets + o.b);
+  // (padded rows, located by (b, i); packed rows through the row offsets)
+  const int L = P.pack_here ? clamp_len(P, o.b) : (int)sload_u32(P.Lc + o.b);
+  const int off = P.pack_here ? 0 : (int)sload_u32(P.row_offsets + o.b);
   o.n = o.i < L ? off + o.i : -1;
   if (L < 0 || o.i > L || (!bonus && o.i == L)) o.b = -1;
   return o;
@@ -2445,6 +2457,57 @@ __global__ __launch_bounds__(kThreads, 8) void fsup_kernel(KParams P) {
   }
 }
 
+// ------------------------------------- verify-only: the pack step in block 0
+
+// The pack kernel's work for the verify-only paths on padded logits, by one
+// whole block: Lc, row_offsets (a scan in each wave, then across the waves,
+// kThreads requests at a time), Lc[B] = N, and the status word (nothing else
+// of the first kernel writes it).
+__device__ void pack_rows_block(const KParams& P) {
+  __shared__ int s_wave[kWaves];
+  __shared__ int s_bad;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) s_bad = 0;
+  __syncthreads();
+  int carry = 0;
+  for (int base = 0; base < P.B; base += kThreads) {
+    const int b = base + tid;
+    int L = 0;
+    if (b < P.B) {
+      L = P.verify_len ? P.verify_len[b] : P.k;
+      if (L < 1 || L > P.k) {
+        atomicOr(&s_bad, ADAFLASH_FLAG_BAD_VERIFY_LEN);
+        L = L < 1 ? 1 : P.k;
+      }
+      P.Lc[b] = L;
+      P.rowcnt[((size_t)b * (P.k + 1) + P.k) * kCounterStride] = 0;  // the request's arrivals (vres_kernel)
+    }
+    int x = L;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(x, off, 64);
+      if (lane >= off) x += t;
+    }
+    if (lane == 63) s_wave[wave] = x;
+    __syncthreads();
+    int woff = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const int t = s_wave[w];
+      if (w < wave) woff += t;
+      tot += t;
+    }
+    if (b < P.B) P.row_offsets[b] = carry + woff + x - L;
+    carry += tot;
+    __syncthreads();
+  }
+  if (tid == 0) {
+    P.row_offsets[P.B] = carry;
+    P.Lc[P.B] = carry;
+    if (P.status) *P.status = s_bad;
+  }
+}
+
 // ------------------------------------------ greedy verification (no OPD)
 
 // Greedy verification needs only every target row's maximum and its lowest
@@ -2463,7 +2526,8 @@ __global__ __launch_bounds__(kThreads) void gstat_kernel(KParams P) {
   const int q = (int)blockIdx.x / G;
   const int j = (int)blockIdx.x - q * G;
   const int b = q / NG, g = q - b * NG;
-  const int L = P.Lc[b];
+  if (P.pack_here && blockIdx.x == 0) pack_rows_block(P);
+  const int L = P.pack_here ? clamp_len(P, b) : P.Lc[b];
   if (L < 0) return;
   const int i0 = g * kGRows;
   if (i0 > L) return;
@@ -2516,9 +2580,10 @@ __global__ __launch_bounds__(kThreads) void gstat_kernel(KParams P) {
 // place only (the accept test), and the residual of one row per request, so
 // it runs without any barrier between workgroups: vstat_kernel publishes the
 // chunk statistics of every row in use and exits; vres_kernel (one workgroup
-// per request and chunk) combines them, runs the accept tests, finds the
-// first rejection and, for a rejected request, computes the residual mass of
-// its chunk of that row (the one row read a second time); final_kernel draws.
+// per request and pair of chunks) combines them, runs the accept tests, finds
+// the first rejection and, for a rejected request, computes the residual mass
+// of its chunks of that row (the one row read a second time); the last of the
+// request's workgroups draws.
 
 // Pass 1 of one (row, chunk): chunk maxima of z_p (and z_q for draft rows)
 // and sums of exp((z - m) / T), published as a part1 record.
@@ -2529,6 +2594,7 @@ __global__ __launch_bounds__(kThreads) void vstat_kernel(KParams P) {
   const int G = P.G, k = P.k, V = P.V;
   const int s_ = (int)blockIdx.x / G;
   const int j = (int)blockIdx.x - s_ * G;
+  if (P.pack_here && blockIdx.x == 0) pack_rows_block(P);
   const RowSlot sl = row_slot_interleaved(P, s_, true);
   if (sl.b < 0) return;
   const int b = sl.b, i = sl.i;
@@ -2602,18 +2668,68 @@ __device__ __forceinline__ float row16_reduce(float v) {
   return v;
 }
 
+// Residual masses sum max(0, p - q) of chunks kResChunks*h ... of the rejected
+// row A of request b, for the draw (s_row: that row's statistics).
+template <bool BF16, bool ALIGNED>
+__device__ void residual_of_chunks(const KParams& P, int b, int A, int h, const float (*s_row)[4], float* red) {
+  const int tid = threadIdx.x;
+  const int G = P.G, k = P.k, V = P.V;
+  const int r0 = b * (k + 1);
+  const int rA = r0 + A;
+  const void* trow = target_row_ptr<BF16>(P, b, A);
+  const void* drow = draft_row_ptr<BF16>(P, b, A);
+  // All chunks' loads first, then the arithmetic.
+  Chunk<BF16> cp[kResChunks], cq[kResChunks];
+#pragma unroll
+  for (int t = 0; t < kResChunks; ++t) {
+    const int jt = kResChunks * h + t;
+    if (jt < G) {
+      load_chunk<BF16, ALIGNED>(cp[t], trow, jt * kChunk, V);
+      load_chunk<BF16, ALIGNED>(cq[t], drow, jt * kChunk, V);
+    }
+  }
+  const float invSp = 1.f / s_row[A][1], invSq = 1.f / s_row[A][3];
+  const float ap = -s_row[A][0] * P.kT, aq = -s_row[A][2] * P.kT;
+  float z[kResChunks];
+  int o[kResChunks];
+#pragma unroll
+  for (int t = 0; t < kResChunks; ++t) {
+    z[t] = 0.f;
+    o[t] = OP_SUM;
+    if (kResChunks * h + t < G) {
+#pragma unroll
+      for (int e = 0; e < kElems; ++e) {
+        const float pv = mul_rn(fexp2(fmaf(cp[t].get(e), P.kT, ap)), invSp);
+        const float qq = mul_rn(fexp2(fmaf(cq[t].get(e), P.kT, aq)), invSq);
+        z[t] += fmaxf(0.f, pv - qq);
+      }
+    }
+  }
+  wg_reduce_lead<kResChunks>(z, o, red);
+  if (tid == 0) {
+#pragma unroll
+    for (int t = 0; t < kResChunks; ++t) {
+      const int jt = kResChunks * h + t;
+      if (jt < G) pub_store(P.part2 + ((size_t)rA * G + jt) * kRec2 + 2, z[t]);
+    }
+  }
+}
+
 // One workgroup per (request b, chunk j).  Each 16-lane row of the workgroup
 // takes one draft row (16 at a time): lane c folds the records of chunks c,
 // c + 16, ..., the lanes reduce them, the first lane runs the accept test.
 // Every workgroup of the request does the same and finds the same first
 // rejection A; for A < L it computes the residual mass sum max(0, p - q) of
-// its chunk of row A for the finaliser.
+// its chunks of row A.  The last workgroup of the request to finish runs the
+// finaliser (no kernel of its own on this path).
 template <bool BF16, bool ALIGNED>
 __global__ __launch_bounds__(kThreads) void vres_kernel(KParams P) {
   __shared__ float red[kWaves * 8];
   __shared__ float s_row[64][4];  // Mp, SpT, Mq, SqT of every draft row
   __shared__ int s_acc[64];
   __shared__ int s_first;
+  __shared__ int s_last;
+  __shared__ FinShared fs;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = P.G, k = P.k, V = P.V;
   const int GH = (G + kResChunks - 1) / kResChunks;
@@ -2676,46 +2792,17 @@ __global__ __launch_bounds__(kThreads) void vres_kernel(KParams P) {
   }
   __syncthreads();
   const int A = s_first;
-  if (A >= L) return;  // every draft accepted: the bonus draw needs no residual
-
-  const int rA = r0 + A;
-  const void* trow = target_row_ptr<BF16>(P, b, A);
-  const void* drow = draft_row_ptr<BF16>(P, b, A);
-  // All chunks' loads first, then the arithmetic.
-  Chunk<BF16> cp[kResChunks], cq[kResChunks];
-#pragma unroll
-  for (int t = 0; t < kResChunks; ++t) {
-    const int jt = kResChunks * h + t;
-    if (jt < G) {
-      load_chunk<BF16, ALIGNED>(cp[t], trow, jt * kChunk, V);
-      load_chunk<BF16, ALIGNED>(cq[t], drow, jt * kChunk, V);
-    }
-  }
-  const float invSp = 1.f / s_row[A][1], invSq = 1.f / s_row[A][3];
-  const float ap = -s_row[A][0] * P.kT, aq = -s_row[A][2] * P.kT;
-  float z[kResChunks];
-  int o[kResChunks];
-#pragma unroll
-  for (int t = 0; t < kResChunks; ++t) {
-    z[t] = 0.f;
-    o[t] = OP_SUM;
-    if (kResChunks * h + t < G) {
-#pragma unroll
-      for (int e = 0; e < kElems; ++e) {
-        const float pv = mul_rn(fexp2(fmaf(cp[t].get(e), P.kT, ap)), invSp);
-        const float qq = mul_rn(fexp2(fmaf(cq[t].get(e), P.kT, aq)), invSq);
-        z[t] += fmaxf(0.f, pv - qq);
-      }
-    }
-  }
-  wg_reduce_lead<kResChunks>(z, o, red);
+  if (A < L) residual_of_chunks<BF16, ALIGNED>(P, b, A, h, s_row, red);
+  // The last of the request's GH workgroups to arrive (every store of the
+  // others complete) draws the correction or bonus token.
   if (tid == 0) {
-#pragma unroll
-    for (int t = 0; t < kResChunks; ++t) {
-      const int jt = kResChunks * h + t;
-      if (jt < G) pub_store(P.part2 + ((size_t)rA * G + jt) * kRec2 + 2, z[t]);
-    }
+    complete_stores();
+    const int old = __hip_atomic_fetch_add(P.rowcnt + (size_t)(r0 + k) * kCounterStride, 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+    s_last = old == GH - 1;
   }
+  __syncthreads();
+  if (s_last) finalize_request<BF16, ALIGNED, 2>(P, b, fs);
 }
 
 // ----------------------------------------------------------- finalise kernel
@@ -2776,6 +2863,7 @@ __global__ __launch_bounds__(1024) void pack_kernel(const int32_t* verify_len, i
       // Draft rows i < L: packed row map, arrival counter, accept flag (not
       // yet known).  Rows past L are never waited on or read.
       const size_t r0 = (size_t)b * (k + 1);
+      ws.rowcnt[(r0 + k) * kCounterStride] = 0;  // the request's arrivals (verification alone)
       for (int q = 0; q < L; ++q) {
         ws.rowmap[off + q] = b * 64 + q;  // (k <= 64)
         ws.rowcnt[(r0 + q) * kCounterStride] = 0;
@@ -2805,13 +2893,15 @@ __global__ __launch_bounds__(1024) void pack_kernel(const int32_t* verify_len, i
 struct Timing {
   std::vector<hipEvent_t> ev;  // two per record
   int cap = 0, used = 0;
+  int every = 1;  // events on every `every`-th dominant launch
+  long long seen = 0;
 };
 thread_local Timing t_timing;
 
 template <typename K>
 hipError_t launch_dominant(K kernel, int grid, hipStream_t st, const KParams& p) {
   Timing& t = t_timing;
-  if (t.used < t.cap) {
+  if (t.used < t.cap && t.seen++ % t.every == 0) {
     hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, st, t.ev[2 * t.used], t.ev[2 * t.used + 1], 0, p);
     ++t.used;
   } else {
@@ -2860,11 +2950,11 @@ hipError_t dispatch_mode(const KParams& p, int grid, int opd, int vmode, bool t1
   }
   else if (vmode == 2) {
     e = launch_dominant(vstat_kernel<BF16, ALIGNED>, grid, st, p);
-    if (e == hipSuccess) {
-      const int gh = (p.G + kResChunks - 1) / kResChunks;
-      hipLaunchKernelGGL((vres_kernel<BF16, ALIGNED>), dim3(p.B * gh), dim3(kThreads), 0, st, p);
-      e = hipGetLastError();
-    }
+    if (e != hipSuccess) return e;
+    // (vres_kernel draws as well)
+    const int gh = (p.G + kResChunks - 1) / kResChunks;
+    hipLaunchKernelGGL((vres_kernel<BF16, ALIGNED>), dim3(p.B * gh), dim3(kThreads), 0, st, p);
+    return hipGetLastError();
   }
   else return hipErrorInvalidValue;
   if (e != hipSuccess) return e;
@@ -2880,6 +2970,8 @@ int timing_enable(int cap) {
   for (hipEvent_t e : t.ev) (void)hipEventDestroy(e);
   t.ev.clear();
   t.cap = t.used = 0;
+  t.every = 1;
+  t.seen = 0;
   if (cap <= 0) return 0;
   t.ev.resize(2 * (size_t)cap, nullptr);
   for (auto& e : t.ev)
@@ -2888,6 +2980,13 @@ int timing_enable(int cap) {
       return -1;
     }
   t.cap = cap;
+  return 0;
+}
+
+int timing_every(int n) {
+  if (n < 1) return -1;
+  t_timing.every = n;
+  t_timing.seen = 0;
   return 0;
 }
 
@@ -2905,10 +3004,15 @@ int timing_read(float* ms, int cap) {
 
 hipError_t launch(const LaunchArgs& a) {
   const int bonus = a.verify ? 1 : 0;
-  hipLaunchKernelGGL(pack_kernel, dim3(1), dim3(1024), 0, a.stream, a.verify_len, a.B, a.k, a.packed,
-                     a.row_offsets, a.ws, a.status);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.B == 0) return e;
+  // Verification alone on padded logits needs none of the pack kernel's row
+  // map, counters or flags: its first kernel does the rest of that work.
+  const bool pack_here = a.verify && !a.opd && !a.packed && a.B > 0;
+  if (!pack_here) {
+    hipLaunchKernelGGL(pack_kernel, dim3(1), dim3(1024), 0, a.stream, a.verify_len, a.B, a.k, a.packed,
+                       a.row_offsets, a.ws, a.status);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.B == 0) return e;
+  }
 
   KParams p;
   p.target = a.target;
@@ -2941,6 +3045,8 @@ hipError_t launch(const LaunchArgs& a) {
   p.wdecay = a.wdecay;
   p.loss_var = a.loss_var;
   p.packed = a.packed;
+  p.pack_here = pack_here;
+  p.verify_len = a.verify_len;
 
   const int vmode = a.verify ? (a.T > 0.f ? 2 : 1) : 0;
   const int rows_max = a.B * (a.k + bonus);

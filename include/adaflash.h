@@ -106,9 +106,14 @@ ADAFLASH_API const char* adaflash_last_error(void);
  * destroys the events.  adaflash_timing_read waits for the recorded events,
  * writes up to cap durations in milliseconds (call order) and starts a new
  * series; it returns the count written, or a negative adaflash_status.
+ * adaflash_timing_every(n), n >= 1, attaches the events to every n-th call
+ * only (the first one included; 1 = every call, the default, which
+ * adaflash_timing_enable restores): attached events add a few microseconds
+ * to a call, so a benchmark samples its calls.
  */
 ADAFLASH_API int adaflash_timing_enable(int max_records);
 ADAFLASH_API int adaflash_timing_read(float* ms, int cap);
+ADAFLASH_API int adaflash_timing_every(int n);
 
 /*
  * adaflash_verify -- speculative verification of a batch of B requests, with

@@ -198,6 +198,8 @@ static void timing_calls() {
   error_text_ok();
   CHECK(adaflash_timing_enable((1 << 20) + 1) < 0);
   CHECK(adaflash_timing_enable(4) == 0);
+  CHECK(adaflash_timing_every(0) < 0);
+  CHECK(adaflash_timing_every(3) == 0);
   float ms[4];
   CHECK(adaflash_timing_read(ms, 4) >= 0);
   CHECK(adaflash_timing_enable(0) == 0);

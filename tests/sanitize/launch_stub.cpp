@@ -9,6 +9,7 @@ hipError_t launch(const LaunchArgs&) { return hipErrorInvalidValue; }
 hipError_t lh_launch(const LhArgs&) { return hipErrorInvalidValue; }
 int timing_enable(int cap) { return cap < 0 ? -1 : 0; }
 int timing_read(float*, int) { return 0; }
+int timing_every(int n) { return n < 1 ? -1 : 0; }
 }  // namespace adaflash
 
 extern "C" const char* hipGetErrorString(hipError_t) { return "launch stubbed out (sanitizer build)"; }

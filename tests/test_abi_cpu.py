@@ -212,6 +212,10 @@ def test_timing_hook_argument_checks(lib):
     assert lib.adaflash_timing_enable(0) == 0  # disabling creates nothing
     assert lib.adaflash_timing_read(None, 4) == -1
     assert lib.adaflash_timing_read(None, 0) == 0  # nothing recorded
+    lib.adaflash_timing_every.restype = ctypes.c_int
+    lib.adaflash_timing_every.argtypes = [ctypes.c_int]
+    assert lib.adaflash_timing_every(0) == -1
+    assert lib.adaflash_timing_every(1) == 0
 
 
 # ---------------------------------------------- binding argument checks
@@ -257,6 +261,50 @@ def test_binding_rejects_mismatched_tensors(lib, name, bad, exc, what):
     a[name] = bad(a)
     with pytest.raises(exc, match=what):
         ada.adaflash_verify(**a)
+
+
+@pytest.mark.parametrize("name,bad,exc,what", [
+    ("tokens", lambda a: a["tokens"].long(), TypeError, "tokens"),
+    ("grad_draft", lambda a: a["grad_draft"][:-1].contiguous(), ValueError, "grad_draft"),
+    ("target", lambda a: a["target"], ValueError, "GPU tensors only"),
+])
+def test_prepared_call_is_checked_like_a_direct_one(lib, name, bad, exc, what):
+    import diffusion_drafter_verification_amd as ada
+    a = _good_verify_args()
+    a[name] = bad(a)
+    with pytest.raises(exc, match=what):
+        ada.adaflash_verify(**a, prepare=True)
+
+
+def test_length_head_bindings_check_tensors(lib):
+    import torch
+    import diffusion_drafter_verification_amd as ada
+    B, k, H, Hp = 2, 4, 64, 32
+    h = torch.zeros(B, k, H, dtype=torch.bfloat16)
+    W1 = torch.zeros(Hp, H, dtype=torch.bfloat16)
+    b1, w2 = torch.zeros(Hp), torch.zeros(Hp)
+    a_hat, k_hat = torch.zeros(B), torch.zeros(B, dtype=torch.int32)
+    with pytest.raises(TypeError, match="hidden"):
+        ada.adaflash_length_head_forward(h.float(), W1, b1, w2, 0.0, 1.0, a_hat, k_hat, None)
+    with pytest.raises(ValueError, match="W1"):
+        ada.adaflash_length_head_forward(h, W1[:, :H - 1].contiguous(), b1, w2, 0.0, 1.0, a_hat, k_hat, None)
+    with pytest.raises(ValueError, match="b1"):
+        ada.adaflash_length_head_forward(h, W1, b1[:-1].contiguous(), w2, 0.0, 1.0, a_hat, k_hat, None)
+    with pytest.raises(ValueError, match="a_hat"):
+        ada.adaflash_length_head_forward(h, W1, b1, w2, 0.0, 1.0, a_hat[:1].contiguous(), k_hat, None)
+    with pytest.raises(ValueError, match="z1_cache"):
+        ada.adaflash_length_head_forward(h, W1, b1, w2, 0.0, 1.0, a_hat, k_hat, None,
+                                         z1_cache=torch.zeros(B * k, Hp + 1))
+    al = torch.zeros(B, dtype=torch.int32)
+    with pytest.raises(ValueError, match="dW1"):
+        ada.adaflash_length_head_backward(h, W1, b1, w2, 0.0, al, al, torch.zeros(B), torch.zeros(Hp, H + 1),
+                                          b1, w2, torch.zeros(1), None)
+    with pytest.raises(TypeError, match="verify_len"):
+        ada.adaflash_length_head_backward(h, W1, b1, w2, 0.0, al, al.long(), torch.zeros(B), torch.zeros(Hp, H),
+                                          b1, w2, torch.zeros(1), None)
+    with pytest.raises(ValueError, match="GPU tensors only"):
+        ada.adaflash_length_head_backward(h, W1, b1, w2, 0.0, al, al, torch.zeros(B), torch.zeros(Hp, H),
+                                          b1.clone(), w2.clone(), torch.zeros(1), None, prepare=True)
 
 
 def test_binding_accepts_well_formed_tensors_up_to_the_device_check(lib):

@@ -69,3 +69,33 @@ def test_every_entry_written_and_repeatable(setup, mode, c):
             assert torch.equal(first[1], snap[1])
             if mode == "fused":
                 assert torch.equal(first[2], snap[2]) and torch.equal(first[3], snap[3])
+
+
+def test_prepared_call_repeats_the_direct_call(setup):
+    """A prepared call (checked and marshalled once) gives the direct call's
+    outputs bit for bit, on every repetition, with the outputs cleared in
+    between."""
+    import torch
+    ada, i, o, N = setup
+    print("prepared call", flush=True)
+    args = (i["t"], i["d"], i["tok"], i["vl"], i["u"], 1.0, o["acc"], o["outt"], o["mg"], 10.0, 1.0, o["ro"],
+            o["ce"], o["rk"], o["grad"], o["st"], o["ws"])
+    ada.adaflash_verify(*args)
+    torch.cuda.synchronize()
+    ref = {kk: o[kk].clone() for kk in ("acc", "outt", "mg", "ro", "ce", "rk")}
+    ref_grad = o["grad"][:N].clone()
+    prep = ada.adaflash_verify(*args, prepare=True)
+    for rep in range(3):
+        for kk in ("ce", "rk", "mg"):
+            o[kk].fill_(float("nan"))
+        o["grad"].fill_(float("nan"))
+        o["acc"].fill_(-7)
+        prep.run()
+        torch.cuda.synchronize()
+        assert int(o["st"].item()) == 0
+        for kk, v in ref.items():
+            g, r = (o[kk][:N], v[:N]) if kk in ("ce", "rk") else (o[kk], v)
+            if g.dtype == torch.float32:  # bit patterns (margins hold NaN past each verify length)
+                g, r = g.view(torch.int32), r.view(torch.int32)
+            assert torch.equal(g, r), kk
+        assert torch.equal(o["grad"][:N].view(torch.int16), ref_grad.view(torch.int16))

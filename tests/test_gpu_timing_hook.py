@@ -72,3 +72,32 @@ def test_hook_records_and_leaves_outputs_unchanged(mode):
         assert o.keys() == ref.keys()
         for key in ref:
             assert np.array_equal(o[key].view(np.uint8), ref[key].view(np.uint8)), key
+
+
+def test_hook_samples_every_nth_call():
+    """adaflash_timing_every(n): events on calls 0, n, 2n, ... only, up to the
+    capacity; adaflash_timing_enable restores every call."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import diffusion_drafter_verification_amd as ada
+    print("timing hook stride", flush=True)
+    bt = W.generate(_wl(92), with_tokens=False)
+    t, d = to_dev(bt.target, True), to_dev(bt.draft, True)
+    vl = torch.from_numpy(bt.verify_len).cuda()
+    with pytest.raises(ada.AdaflashError):
+        ada.adaflash_timing_every(0)
+    try:
+        ada.adaflash_timing_enable(8)
+        ada.adaflash_timing_every(3)
+        for _ in range(7):  # calls 0, 3 and 6 carry events
+            ada.opd_loss_fwd_bwd(t, d, vl, clip_c=10.0, lam=1.0)
+        torch.cuda.synchronize()
+        assert len(ada.adaflash_timing_read(8)) == 3
+        ada.adaflash_timing_enable(8)  # back to every call
+        for _ in range(2):
+            ada.opd_loss_fwd_bwd(t, d, vl, clip_c=10.0, lam=1.0)
+        torch.cuda.synchronize()
+        assert len(ada.adaflash_timing_read(8)) == 2
+    finally:
+        ada.adaflash_timing_enable(0)
