@@ -97,23 +97,25 @@ int timing_every(int n);
 
 // Adaptive length head (adaflash_length_head.hip).
 struct LhWorkspace {
-  float* z1;         // [S, B*k, Hp] split-K slices of the projection
-  float* zsum;       // [B*k, Hp] their sum
+  float* z1;         // [Sf, B*k, Hp] split-K slices of the projection h W1^T
+  float* zsum;       // [B*k, Hp] their sum (when the caller keeps no copy)
   float* hbar;       // [B, Hp] pooled vectors (backward)
   float* ds;         // [B] d loss / d logit (backward)
-  uint16_t* dzh;     // [Hp, Mp] dZ1^T, bf16 high part (backward)
-  uint16_t* dzl;     // [Hp, Mp] dZ1^T, bf16 remainder (backward)
+  uint16_t* dzh;     // [B*k, Hq] dZ1, bf16 high part (backward; Hq = Hp rounded up to 8)
+  uint16_t* dzl;     // [B*k, Hq] dZ1, bf16 remainder (backward)
   float* db1_part;   // [B, Hp] per-request column sums of dZ1 (for db1)
-  uint16_t* hT;      // [H, Mp] transposed hidden states (backward)
-  float* dw_part;    // [S, Hp, H] split-K partial sums of dW1 (backward)
+  float* dw_part;    // [Sb, Hp, H] split-K partial sums of dW1 (backward)
 };
 
 size_t lh_workspace_layout(int B, int k, int H, int Hp, char* base, LhWorkspace* ws);
 
-// Output tile of the length head's products (rows and columns per workgroup),
-// and the split of a reduction of length K over slices for a product with
-// `tiles` output tiles.
+// Output tile of the length head's products (64 x 64), and the split of a
+// reduction of length K over slices for `tiles` output tiles: about 1024
+// workgroups, slices a multiple of 64 long and at least 256.
 constexpr int kLhTile = 64;
+inline long long lh_tiles(long long rows, long long cols) {
+  return ((rows + kLhTile - 1) / kLhTile) * ((cols + kLhTile - 1) / kLhTile);
+}
 struct LhSplit {
   int S, kslice;
 };

@@ -40,40 +40,35 @@ size_t workspace_layout(int B, int k, int V, char* base, Workspace* ws) {
   return off;
 }
 
-// Split of a reduction of length K for a product with `tiles` output tiles:
-// enough slices for about 1024 workgroups, each slice a multiple of 16 and at
-// least 256 long.
 LhSplit lh_split_k(int K, long long tiles) {
   if (tiles < 1) tiles = 1;  // (an empty product)
-  long long want = (1024 + tiles - 1) / tiles;
-  long long maxs = K / 256 > 0 ? K / 256 : 1;
+  const long long want = (1024 + tiles - 1) / tiles;
+  const long long maxs = K / 256 > 0 ? K / 256 : 1;
   int S = (int)(want < 1 ? 1 : (want > maxs ? maxs : want));
   int ks = (K + S - 1) / S;
-  ks = ks < 16 ? 16 : (ks + 15) & ~15;
+  ks = (ks + 63) & ~63;  // whole 64-wide rounds of the products
   S = K > 0 ? (K + ks - 1) / ks : 1;
   return {S, ks};
 }
 
 size_t lh_workspace_layout(int B, int k, int H, int Hp, char* base, LhWorkspace* ws) {
   const size_t M = (size_t)B * k;
-  const size_t Mp = (M + 15) & ~size_t(15);
-  const size_t ntiles = (M + kLhTile - 1) / kLhTile;
-  const LhSplit sf = lh_split_k(H, (long long)ntiles * ((Hp + kLhTile - 1) / kLhTile));
-  const LhSplit sb = lh_split_k((int)Mp, (long long)((Hp + kLhTile - 1) / kLhTile) * ((H + kLhTile - 1) / kLhTile));
+  const size_t Hq = ((size_t)Hp + 7) & ~size_t(7);
+  const LhSplit sf = lh_split_k(H, lh_tiles((long long)M, Hp));
+  const LhSplit sb = lh_split_k((int)M, lh_tiles(Hp, H));
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t at = off;
-    off = (off + bytes + 255) & ~size_t(255);
+    off = align_up(off + bytes);
     return base ? base + at : nullptr;
   };
   char* z1 = take(sizeof(float) * sf.S * M * Hp);
   char* zsum = take(sizeof(float) * M * Hp);
   char* hbar = take(sizeof(float) * (size_t)B * Hp);
   char* ds = take(sizeof(float) * (size_t)B);
-  char* dzh = take(sizeof(uint16_t) * Mp * Hp);
-  char* dzl = take(sizeof(uint16_t) * Mp * Hp);
+  char* dzh = take(sizeof(uint16_t) * M * Hq);
+  char* dzl = take(sizeof(uint16_t) * M * Hq);
   char* part = take(sizeof(float) * (size_t)B * Hp);
-  char* hT = take(sizeof(uint16_t) * (size_t)H * Mp);
   char* dwp = take(sizeof(float) * sb.S * (size_t)Hp * H);
   if (ws) {
     ws->z1 = (float*)z1;
@@ -83,7 +78,6 @@ size_t lh_workspace_layout(int B, int k, int H, int Hp, char* base, LhWorkspace*
     ws->dzh = (uint16_t*)dzh;
     ws->dzl = (uint16_t*)dzl;
     ws->db1_part = (float*)part;
-    ws->hT = (uint16_t*)hT;
     ws->dw_part = (float*)dwp;
   }
   return off;
