@@ -29,7 +29,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published peak
-TRAFFIC_PROFILE = {"fused": os.path.join(ROOT, "profiles", "sup_kernel_c128_fused_hbm_bytes.md"),
+TRAFFIC_PROFILE = {"fused": os.path.join(ROOT, "profiles", "fsup_kernel_c128_fused_hbm_bytes.md"),
                    "verify": os.path.join(ROOT, "profiles", "vstat_kernel_c128_verify.md")}
 KERNEL_SOURCE = os.path.join(ROOT, "diffusion_drafter_verification_amd", "csrc", "adaflash_kernels.hip")
 METRIC = "verified draft positions/sec + achieved HBM GB/s (B=128, k=16, V=151936)"
