@@ -360,3 +360,30 @@ def test_noalloc_entry_point_rejects_sizes_beyond_its_array(lib):
     assert rc == -4 and b"no-allocation" in lib.adaflash_last_error()
     rc = f(1, *null, 4, 0, 151936, 1.0, None, None, None, 10.0, 1.0, None, None, None, None, None, None)
     assert rc == -1
+
+
+_REMARKS = """\
+x.hip:10:1: remark: Function Name: _Z6good_kv [-Rpass-analysis=kernel-resource-usage]
+   10 | __global__ void good_k() {
+      | ^
+x.hip:10:1: remark:     VGPRs: 61 [-Rpass-analysis=kernel-resource-usage]
+x.hip:10:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]
+x.hip:10:1: remark:     SGPRs Spill: 22 [-Rpass-analysis=kernel-resource-usage]
+x.hip:10:1: remark:     VGPRs Spill: 0 [-Rpass-analysis=kernel-resource-usage]
+x.hip:20:1: remark: Function Name: _Z7spill_kv [-Rpass-analysis=kernel-resource-usage]
+x.hip:20:1: remark:     ScratchSize [bytes/lane]: 20 [-Rpass-analysis=kernel-resource-usage]
+x.hip:20:1: remark:     VGPRs Spill: 5 [-Rpass-analysis=kernel-resource-usage]
+x.hip:30:1: remark: Function Name: _Z7stack_kv [-Rpass-analysis=kernel-resource-usage]
+x.hip:30:1: remark:     ScratchSize [bytes/lane]: 16 [-Rpass-analysis=kernel-resource-usage]
+x.hip:30:1: remark:     VGPRs Spill: 0 [-Rpass-analysis=kernel-resource-usage]
+"""
+
+
+def test_build_rejects_kernels_with_scratch_or_spilled_vgprs():
+    """The build's resource check flags a scratch segment and spilled VGPRs,
+    and lets SGPR spills (into VGPR lanes) pass."""
+    from diffusion_drafter_verification_amd.build import scratch_users
+    assert scratch_users(_REMARKS) == [("_Z7spill_kv", "scratch bytes per lane", 20),
+                                       ("_Z7spill_kv", "spilled VGPRs", 5),
+                                       ("_Z7stack_kv", "scratch bytes per lane", 16)]
+    assert scratch_users(_REMARKS.split("x.hip:20:1")[0]) == []
