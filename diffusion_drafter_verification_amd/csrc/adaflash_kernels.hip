@@ -81,7 +81,7 @@ struct KParams {
   float* part1;
   float* part2;
   float* rowrec;
-  const uint32_t* epoch;  // this call's epoch (advanced by the pack kernel)
+  uint32_t* epoch;  // this call's epoch (advanced by the pack step)
   int B, k, V, G;
   float kT;  // log2(e) / T (0 in greedy mode)
   float clip_c, lambda;
@@ -784,8 +784,19 @@ __device__ __forceinline__ unsigned int ukey(float x) {
 // T = 1); otherwise float records relative to the chunk maxima rec[0] and
 // rec[4] of z / T.  (Both are complete here: the finaliser runs after the
 // kernel that wrote them.)
-template <bool BF16, bool ALIGNED, int VMODE, bool LOG2REC = false>
-__device__ void finalize_request(const KParams& P, int b, FinShared& fs) {
+// What the residual kernel already knows when its last workgroup of a
+// request draws: the first rejection A and, for A < L, row A's statistics at
+// T (natural-unit maxima, sums relative to them), and the call epoch that
+// tags the residual partials.
+struct KnownRow {
+  int A = 0;
+  uint32_t ep = 0;
+  float Mp = 0.f, SpT = 0.f, Mq = 0.f, SqT = 0.f;
+};
+
+template <bool BF16, bool ALIGNED, int VMODE, bool LOG2REC = false, bool KNOWN = false>
+__device__ void finalize_request(const KParams& P, int b, FinShared& fs, const KnownRow& kr = KnownRow{}) {
+  static_assert(!KNOWN || (VMODE == 2 && !LOG2REC), "known rows: sampled verification, natural-unit records");
   const int k = P.k, V = P.V, G = P.G;
   const int tid = threadIdx.x;  // (k + 1 <= 65 rows: thread i holds position i)
   const int lane = tid & 63;
@@ -800,7 +811,7 @@ __device__ void finalize_request(const KParams& P, int b, FinShared& fs) {
     tok = x < 0 ? 0 : (x >= V ? V - 1 : x);
   }
   if constexpr (VMODE != 1) {
-    if (lane < k) acc_flag = pub_load(P.rowrec + (size_t)(r0 + lane) * kRowRec + 1);
+    if (!KNOWN && lane < k) acc_flag = pub_load(P.rowrec + (size_t)(r0 + lane) * kRowRec + 1);
     us = P.uniforms[(size_t)b * (k + 1) + k];
   }
   const int L = P.Lc[b];
@@ -849,59 +860,106 @@ __device__ void finalize_request(const KParams& P, int b, FinShared& fs) {
     // accept flags (one per lane) and G <= 128 chunk records (up to two per
     // lane), in the same fixed order in every wave: no workgroup barrier
     // separates these steps, and all threads hold the same results.
-    const unsigned long long rej = __ballot(lane < L && acc_flag == 0.f);
-    A = rej ? min((int)__builtin_ctzll(rej), L) : L;
-
-    // Row statistics at T of the row the draw reads (rejected row A or the
-    // bonus row L) and, for a rejected row, its per-chunk residual masses.
-    const int rs = r0 + A;
-    float mp[2], spT[2], mq[2], sqT[2], res[2];
+    float res[2] = {0.f, 0.f}, pj[2] = {0.f, 0.f};
+    float Mp, Mq, SpT, SqT, Zres;
+    bool resid;
+    if constexpr (KNOWN) {
+      // The residual partials of row A (waiting for this call's tags), then
+      // the known statistics; only a bonus draw (or a zero residual) reads
+      // the target chunk records of its row.
+      A = kr.A;
+      const int rs = r0 + A;
+      bool ok = true;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int jj = lane + 64 * h;
-      mp[h] = neg_inf();
-      mq[h] = neg_inf();
-      spT[h] = sqT[h] = res[h] = 0.f;
-      if (jj < G) {
-        if constexpr (LOG2REC) {
-          const size_t f0 = ((size_t)rs * G + jj) * kRec1;
-          mp[h] = tag_value(tag_load(P.part1, f0 + 1));
-          spT[h] = tag_value(tag_load(P.part1, f0 + 2));
-          if (A < L) {
-            mq[h] = tag_value(tag_load(P.part1, f0 + 4));
-            sqT[h] = tag_value(tag_load(P.part1, f0 + 5));
-            res[h] = tag_value(tag_load(P.part2, ((size_t)rs * G + jj) * kRec2 + 2));
+      for (int h = 0; h < 2; ++h) {
+        float v1[1] = {0.f};
+        const int jj = lane + 64 * h;
+        if (h == 0 || G > 64)
+          ok = poll_fields<1>(P.part2, kRec2, A < L && jj < G, rs * G + jj, 2, 1, kr.ep, v1, P.status) && ok;
+        res[h] = A < L && jj < G ? v1[0] : 0.f;
+      }
+      (void)ok;  // (a timed-out wait has flagged the status word)
+      Zres = wave_reduce<OP_SUM>(res[0] + res[1]);
+      resid = A < L && Zres > 0.f;
+      Mp = kr.Mp;
+      SpT = kr.SpT;
+      Mq = kr.Mq;
+      SqT = kr.SqT;
+      if (!resid) {
+        float mp[2], spT[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int jj = lane + 64 * h;
+          mp[h] = neg_inf();
+          spT[h] = 0.f;
+          if (jj < G) {
+            const float* rec = P.part1 + ((size_t)rs * G + jj) * kRec1;
+            mp[h] = pub_load(rec + 0);
+            spT[h] = pub_load(rec + 2);
           }
-        } else {
-          const float* rec = P.part1 + ((size_t)rs * G + jj) * kRec1;
-          mp[h] = pub_load(rec + 0);
-          spT[h] = pub_load(rec + 2);
-          if (A < L) {
-            mq[h] = pub_load(rec + 4);
-            sqT[h] = pub_load(rec + 5);
-            res[h] = pub_load(P.part2 + ((size_t)rs * G + jj) * kRec2 + 2);
+        }
+        Mp = wave_reduce<OP_MAX>(fmaxf(mp[0], mp[1]));
+#pragma unroll
+        for (int h = 0; h < 2; ++h) pj[h] = mp[h] == neg_inf() ? 0.f : spT[h] * fexp2((mp[h] - Mp) * P.kT);
+        SpT = wave_reduce<OP_SUM>(pj[0] + pj[1]);
+        Mq = neg_inf();
+        SqT = 1.f;
+      }
+    } else {
+      const unsigned long long rej = __ballot(lane < L && acc_flag == 0.f);
+      A = rej ? min((int)__builtin_ctzll(rej), L) : L;
+
+      // Row statistics at T of the row the draw reads (rejected row A or the
+      // bonus row L) and, for a rejected row, its per-chunk residual masses.
+      const int rs = r0 + A;
+      float mp[2], spT[2], mq[2], sqT[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int jj = lane + 64 * h;
+        mp[h] = neg_inf();
+        mq[h] = neg_inf();
+        spT[h] = sqT[h] = 0.f;
+        if (jj < G) {
+          if constexpr (LOG2REC) {
+            const size_t f0 = ((size_t)rs * G + jj) * kRec1;
+            mp[h] = tag_value(tag_load(P.part1, f0 + 1));
+            spT[h] = tag_value(tag_load(P.part1, f0 + 2));
+            if (A < L) {
+              mq[h] = tag_value(tag_load(P.part1, f0 + 4));
+              sqT[h] = tag_value(tag_load(P.part1, f0 + 5));
+              res[h] = tag_value(tag_load(P.part2, ((size_t)rs * G + jj) * kRec2 + 2));
+            }
+          } else {
+            const float* rec = P.part1 + ((size_t)rs * G + jj) * kRec1;
+            mp[h] = pub_load(rec + 0);
+            spT[h] = pub_load(rec + 2);
+            if (A < L) {
+              mq[h] = pub_load(rec + 4);
+              sqT[h] = pub_load(rec + 5);
+              res[h] = pub_load(P.part2 + ((size_t)rs * G + jj) * kRec2 + 2);
+            }
           }
         }
       }
-    }
-    const float Mp = wave_reduce<OP_MAX>(fmaxf(mp[0], mp[1]));
-    const float Mq = wave_reduce<OP_MAX>(fmaxf(mq[0], mq[1]));
-    float pj[2], qj[2];
+      Mp = wave_reduce<OP_MAX>(fmaxf(mp[0], mp[1]));
+      Mq = wave_reduce<OP_MAX>(fmaxf(mq[0], mq[1]));
+      float qj[2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      if constexpr (LOG2REC) {
-        pj[h] = mp[h] == neg_inf() ? 0.f : __builtin_ldexpf(spT[h], (int)fmaxf(mp[h] - Mp, -256.f));
-        qj[h] = mq[h] == neg_inf() ? 0.f : __builtin_ldexpf(sqT[h], (int)fmaxf(mq[h] - Mq, -256.f));
-      } else {
-        pj[h] = mp[h] == neg_inf() ? 0.f : spT[h] * fexp2((mp[h] - Mp) * P.kT);
-        qj[h] = mq[h] == neg_inf() ? 0.f : sqT[h] * fexp2((mq[h] - Mq) * P.kT);
+      for (int h = 0; h < 2; ++h) {
+        if constexpr (LOG2REC) {
+          pj[h] = mp[h] == neg_inf() ? 0.f : __builtin_ldexpf(spT[h], (int)fmaxf(mp[h] - Mp, -256.f));
+          qj[h] = mq[h] == neg_inf() ? 0.f : __builtin_ldexpf(sqT[h], (int)fmaxf(mq[h] - Mq, -256.f));
+        } else {
+          pj[h] = mp[h] == neg_inf() ? 0.f : spT[h] * fexp2((mp[h] - Mp) * P.kT);
+          qj[h] = mq[h] == neg_inf() ? 0.f : sqT[h] * fexp2((mq[h] - Mq) * P.kT);
+        }
       }
+      SpT = wave_reduce<OP_SUM>(pj[0] + pj[1]);
+      SqT = wave_reduce<OP_SUM>(qj[0] + qj[1]);
+      Zres = wave_reduce<OP_SUM>(res[0] + res[1]);
+      resid = A < L && Zres > 0.f;
     }
-    const float SpT = wave_reduce<OP_SUM>(pj[0] + pj[1]);
-    const float SqT = wave_reduce<OP_SUM>(qj[0] + qj[1]);
-    const float Zres = wave_reduce<OP_SUM>(res[0] + res[1]);
     const float invSp = 1.f / SpT, invSq = 1.f / SqT;
-    const bool resid = A < L && Zres > 0.f;
 
     // Chunk-level inverse CDF over the chunk masses in chunk order: the first
     // chunk whose running mass passes u_s times the total, else the last
@@ -2386,20 +2444,19 @@ __global__ __launch_bounds__(kThreads, 8) void fsup_kernel(KParams P) {
     }
     float s3[3] = {Spart, Rpart, Zpart};
     const int ops3[3] = {OP_SUM, OP_SUM, OP_SUM};
-    wg_reduce<3>(s3, ops3, fs.red);
+    wg_reduce_lead<3>(s3, ops3, fs.red);  // (fs.red is next written after the barrier below)
     if (tid == 0) {
       const size_t f0 = ((size_t)r * G + j) * kRec2;
       tag_store(P.part2, f0 + 0, s3[0], call_epoch);
       tag_store(P.part2, f0 + 1, s3[1], call_epoch);
       if (SAMPLED) tag_store(P.part2, f0 + 2, s3[2], call_epoch);
-      __hip_atomic_fetch_add(P.rowcnt + (size_t)r * kCounterStride, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    // Second row barrier: wave 0 waits for the G partial sums S and R.
+    // Second row barrier: wave 0 polls the G partial sums S and R until each
+    // carries this call's epoch (two fields per chunk: no arrival counter).
     if (wave == 0) {
       float f2[2] = {0.f, 0.f};
       const float* recs2 = (const float*)((const uint64_t*)P.part2 + (size_t)r * G * kRec2);
-      const bool ok = wait_count(P.rowcnt + (size_t)r * kCounterStride, 2 * G, P.status) &&
-                      poll_fields<2>(recs2, kRec2, lane < G, lane, 0, 2, call_epoch, f2, P.status);
+      const bool ok = poll_fields<2>(recs2, kRec2, lane < G, lane, 0, 2, call_epoch, f2, P.status);
       const float S = wave_reduce<OP_SUM>(lane < G ? f2[0] : 0.f);
       const float R = wave_reduce<OP_SUM>(lane < G ? f2[1] : 0.f);
       if (lane == 0) {
@@ -2461,8 +2518,9 @@ __global__ __launch_bounds__(kThreads, 8) void fsup_kernel(KParams P) {
 
 // The pack kernel's work for the verify-only paths on padded logits, by one
 // whole block: Lc, row_offsets (a scan in each wave, then across the waves,
-// kThreads requests at a time), Lc[B] = N, and the status word (nothing else
-// of the first kernel writes it).
+// kThreads requests at a time), Lc[B] = N, the status word (nothing else of
+// the first kernel writes it), the request counters of the residual kernel
+// and the call epoch (which only the next kernel reads).
 __device__ void pack_rows_block(const KParams& P) {
   __shared__ int s_wave[kWaves];
   __shared__ int s_bad;
@@ -2505,6 +2563,7 @@ __device__ void pack_rows_block(const KParams& P) {
     P.row_offsets[P.B] = carry;
     P.Lc[P.B] = carry;
     if (P.status) *P.status = s_bad;
+    P.epoch[0] += 1u;  // read by the next kernel of the call
   }
 }
 
@@ -2602,12 +2661,23 @@ __global__ __launch_bounds__(kThreads) void vstat_kernel(KParams P) {
   const bool draft_row = sl.n >= 0;
   const int v0 = j * kChunk;
   const void* trow = target_row_ptr<BF16>(P, b, i, sl.n);
+  const void* drow = draft_row ? draft_row_ptr<BF16>(P, b, i, sl.n) : nullptr;
+  // The chunk holding the draft token (clamped as the accept test clamps it)
+  // also publishes both logits there, for the accept test.
+  bool xhere = false;
+  float zpx = 0.f, zqx = 0.f;
+  if (draft_row) {
+    int x = (int)sload_u32(P.tokens + (size_t)b * k + i);
+    x = x < 0 ? 0 : (x >= V ? V - 1 : x);
+    xhere = x / kChunk == j;
+    if (xhere) {
+      zpx = sload_logit<BF16>(trow, x);
+      zqx = sload_logit<BF16>(drow, x);
+    }
+  }
   Chunk<BF16> cp, cq;
   load_chunk<BF16, ALIGNED>(cp, trow, v0, V);
-  if (draft_row) {
-    const void* drow = draft_row_ptr<BF16>(P, b, i, sl.n);
-    load_chunk<BF16, ALIGNED>(cq, drow, v0, V);
-  }
+  if (draft_row) load_chunk<BF16, ALIGNED>(cq, drow, v0, V);
   float m[2] = {chunk_max<BF16>(cp), draft_row ? chunk_max<BF16>(cq) : neg_inf()};
   cp.opaque();
   cq.opaque();
@@ -2632,6 +2702,10 @@ __global__ __launch_bounds__(kThreads) void vstat_kernel(KParams P) {
     pub_store(rec + 2, sv[0]);
     pub_store(rec + 4, m[1]);
     pub_store(rec + 5, sv[1]);
+    if (xhere) {
+      pub_store(rec + 6, zpx);
+      pub_store(rec + 7, zqx);
+    }
   }
 }
 
@@ -2671,7 +2745,8 @@ __device__ __forceinline__ float row16_reduce(float v) {
 // Residual masses sum max(0, p - q) of chunks kResChunks*h ... of the rejected
 // row A of request b, for the draw (s_row: that row's statistics).
 template <bool BF16, bool ALIGNED>
-__device__ void residual_of_chunks(const KParams& P, int b, int A, int h, const float (*s_row)[4], float* red) {
+__device__ void residual_of_chunks(const KParams& P, int b, int A, int h, const float (*s_row)[4], float* red,
+                                   uint32_t ep) {
   const int tid = threadIdx.x;
   const int G = P.G, k = P.k, V = P.V;
   const int r0 = b * (k + 1);
@@ -2710,18 +2785,21 @@ __device__ void residual_of_chunks(const KParams& P, int b, int A, int h, const 
 #pragma unroll
     for (int t = 0; t < kResChunks; ++t) {
       const int jt = kResChunks * h + t;
-      if (jt < G) pub_store(P.part2 + ((size_t)rA * G + jt) * kRec2 + 2, z[t]);
+      if (jt < G) tag_store(P.part2, ((size_t)rA * G + jt) * kRec2 + 2, z[t], ep);
     }
   }
 }
 
 // One workgroup per (request b, chunk j).  Each 16-lane row of the workgroup
 // takes one draft row (16 at a time): lane c folds the records of chunks c,
-// c + 16, ..., the lanes reduce them, the first lane runs the accept test.
-// Every workgroup of the request does the same and finds the same first
-// rejection A; for A < L it computes the residual mass sum max(0, p - q) of
-// its chunks of row A.  The last workgroup of the request to finish runs the
-// finaliser (no kernel of its own on this path).
+// c + 16, ..., the lanes reduce them, the first lane runs the accept test
+// with the logits at the draft token that the statistics kernel put in the
+// record of the chunk holding it.  Every workgroup of the request does the
+// same and finds the same first rejection A; for A < L it computes the
+// residual mass sum max(0, p - q) of its chunks of row A and publishes it
+// tagged with the call epoch.  The last workgroup of the request to arrive
+// draws (no kernel of its own on this path), with A and row A's statistics
+// at hand.
 template <bool BF16, bool ALIGNED>
 __global__ __launch_bounds__(kThreads) void vres_kernel(KParams P) {
   __shared__ float red[kWaves * 8];
@@ -2738,37 +2816,62 @@ __global__ __launch_bounds__(kThreads) void vres_kernel(KParams P) {
   const int j = h;                         // (workgroup h == 0 writes the row flags)
   const int L = P.Lc[b];
   if (L < 0) return;
+  const uint32_t ep = sload_u32(P.epoch);
   const int r0 = b * (k + 1);
   const int grp = tid >> 4, l16 = tid & 15;  // 16 groups of 16 lanes
   for (int i0 = 0; i0 < L; i0 += kThreads / 16) {
     const int i = i0 + grp;
     const bool live = i < L;  // uniform within the group
     const int r = r0 + i;
+    // Every lane of the group reads the token (one address) and folds its
+    // chunk records; the record of the chunk holding the token also carries
+    // both logits there (from the statistics kernel).
     int x = 0;
     float u = 0.f;
-    if (live && l16 == 0) {  // issued before the record loads
+    if (live) {
       x = P.tokens[(size_t)b * k + i];
       u = P.uniforms[(size_t)b * (k + 1) + i];
     }
-    float Mp = neg_inf(), Sp = 0.f, Mq = neg_inf(), Sq = 0.f;
+    const int xc = x < 0 ? 0 : (x >= V ? V - 1 : x);
+    const int jx = xc / kChunk;
+    float Mp = neg_inf(), Sp = 0.f, Mq = neg_inf(), Sq = 0.f, zpx = 0.f, zqx = 0.f;
     if (live) {
-      for (int c = l16; c < G; c += 16) {
+      // Two records per lane per round, all their loads issued before either
+      // is folded (one round trip for up to 32 chunks).
+      for (int c = l16; c < G; c += 32) {
+        const bool two = c + 16 < G;
         const float* rec = P.part1 + ((size_t)r * G + c) * kRec1;
-        fold_ms(Mp, Sp, pub_load(rec + 0), pub_load(rec + 2), P.kT);
-        fold_ms(Mq, Sq, pub_load(rec + 4), pub_load(rec + 5), P.kT);
+        const float* rec2 = rec + 16 * kRec1;
+        float f[8];
+        f[0] = pub_load(rec + 0);
+        f[1] = pub_load(rec + 2);
+        f[2] = pub_load(rec + 4);
+        f[3] = pub_load(rec + 5);
+        f[4] = two ? pub_load(rec2 + 0) : neg_inf();
+        f[5] = two ? pub_load(rec2 + 2) : 0.f;
+        f[6] = two ? pub_load(rec2 + 4) : neg_inf();
+        f[7] = two ? pub_load(rec2 + 5) : 0.f;
+        if (c == jx) {
+          zpx = pub_load(rec + 6);
+          zqx = pub_load(rec + 7);
+        } else if (c + 16 == jx) {
+          zpx = pub_load(rec2 + 6);
+          zqx = pub_load(rec2 + 7);
+        }
+        fold_ms(Mp, Sp, f[0], f[1], P.kT);
+        fold_ms(Mq, Sq, f[2], f[3], P.kT);
+        fold_ms(Mp, Sp, f[4], f[5], P.kT);
+        fold_ms(Mq, Sq, f[6], f[7], P.kT);
       }
     }
     const float RMp = row16_reduce<OP_MAX>(Mp), RMq = row16_reduce<OP_MAX>(Mq);
     const float SpT = row16_reduce<OP_SUM>(Mp == neg_inf() ? 0.f : Sp * fexp2((Mp - RMp) * P.kT));
     const float SqT = row16_reduce<OP_SUM>(Mq == neg_inf() ? 0.f : Sq * fexp2((Mq - RMq) * P.kT));
+    const int src = (lane & ~15) | (jx & 15);  // the lane that folded chunk jx
+    zpx = __shfl(zpx, src, 64);
+    zqx = __shfl(zqx, src, 64);
     if (live && l16 == 0) {
-      if (x < 0 || x >= V) {
-        if (j == 0) flag(P.status, ADAFLASH_FLAG_BAD_TOKEN);
-        x = x < 0 ? 0 : V - 1;
-      }
-      const void* trow = target_row_ptr<BF16>(P, b, i);
-      const void* drow = draft_row_ptr<BF16>(P, b, i);
-      const float zpx = load_logit<BF16>(trow, x), zqx = load_logit<BF16>(drow, x);
+      if ((x < 0 || x >= V) && j == 0) flag(P.status, ADAFLASH_FLAG_BAD_TOKEN);
       const float px = fexp2((zpx - RMp) * P.kT) / SpT;
       const float qx = fexp2((zqx - RMq) * P.kT) / SqT;
       const bool accept = u * qx < px;
@@ -2792,17 +2895,29 @@ __global__ __launch_bounds__(kThreads) void vres_kernel(KParams P) {
   }
   __syncthreads();
   const int A = s_first;
-  if (A < L) residual_of_chunks<BF16, ALIGNED>(P, b, A, h, s_row, red);
-  // The last of the request's GH workgroups to arrive (every store of the
-  // others complete) draws the correction or bonus token.
+  if (A < L) residual_of_chunks<BF16, ALIGNED>(P, b, A, h, s_row, red, ep);
+  // The last of the request's GH workgroups to arrive draws the correction or
+  // bonus token, with the first rejection and its row's statistics already
+  // known; it waits for each residual partial's epoch tag (the others count
+  // their arrival without waiting for those stores).
   if (tid == 0) {
-    complete_stores();
     const int old = __hip_atomic_fetch_add(P.rowcnt + (size_t)(r0 + k) * kCounterStride, 1, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);
     s_last = old == GH - 1;
   }
   __syncthreads();
-  if (s_last) finalize_request<BF16, ALIGNED, 2>(P, b, fs);
+  if (s_last) {
+    KnownRow kr;
+    kr.A = A;
+    kr.ep = ep;
+    if (A < L) {
+      kr.Mp = s_row[A][0];
+      kr.SpT = s_row[A][1];
+      kr.Mq = s_row[A][2];
+      kr.SqT = s_row[A][3];
+    }
+    finalize_request<BF16, ALIGNED, 2, false, true>(P, b, fs, kr);
+  }
 }
 
 // ----------------------------------------------------------- finalise kernel
