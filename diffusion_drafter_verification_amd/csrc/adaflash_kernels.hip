@@ -2301,17 +2301,8 @@ __global__ __launch_bounds__(kThreads, 8) void fsup_kernel(KParams P) {
   }
   if (!draft_row) return;
 
-  // Wave 1 reads the accept flags of the earlier rows while wave 0 waits for
-  // the row's records.
-  if (SAMPLED && wave == 1) {
-    const int l = tid - 64;
-    const bool rej = l < i && pub_load(P.rowrec + (size_t)(r - i + l) * kRowRec + 1) == 0.f;
-    const unsigned long long any = __ballot(rej);
-    if (l == 0) fs.i[0] = any != 0ull;
-  }
   const SupStats st = combine_sup_pow2<SAMPLED, FKL>(P, r, fs, zpx, zqx, u_acc, call_epoch);
   if (!st.alive) return;
-  const bool earlier_rejected = SAMPLED && fs.i[0] != 0;
   const float lse_q2 = st.lse_q2, lse_p2 = st.lse_p2, D = st.D, KL = st.KL;
   const float wi = P.wdecay > 0.f ? uniform(fexp2(-(float)i * kLog2e / P.wdecay)) : 1.f;
   const float c = P.clip_c, lam = uniform(wi * P.lambda), ace = uniform(wi * P.a_ce);
@@ -2330,6 +2321,14 @@ __global__ __launch_bounds__(kThreads, 8) void fsup_kernel(KParams P) {
       if (P.margins) P.margins[(size_t)b * (k + 1) + i] = st.margin;
     }
   }
+  // Only the first rejected row of a request needs its residual mass.  A
+  // rejected row reads the accept flags of the request's earlier rows here,
+  // after its own barrier, and decides after its gradient: by then most
+  // earlier rows have published theirs (a flag still "unknown" counts as not
+  // rejected, and the row computes a residual that may go unused).
+  const bool ask = SAMPLED && !accept && i > 0;  // (uniform)
+  float flag_l = 1.f;
+  if (ask && wave == 1 && lane < i) flag_l = pub_load(P.rowrec + (size_t)(r - i + lane) * kRowRec + 1);
 
   // st.xstar is the lowest chunk whose maximum is the row maximum; that chunk
   // finds the lowest index holding it.
@@ -2352,7 +2351,6 @@ __global__ __launch_bounds__(kThreads, 8) void fsup_kernel(KParams P) {
   const bool xs_here = xs < V && xo >= 0 && xo < kChunk && ((xo % (kThreads * VEC)) / VEC) == tid;
   const float zqs = xs >= 0 && xs < V ? sload_logit<true>(drow, xs) : 0.f;
 
-  const bool need_res = SAMPLED && !accept && !earlier_rejected;
   float Zpart = 0.f;
   const bool whole = v0 + kChunk <= V;
   auto store_slot = [&](int s2, const float (&g)[VEC]) {
@@ -2392,13 +2390,6 @@ __global__ __launch_bounds__(kThreads, 8) void fsup_kernel(KParams P) {
         store_slot(s2, g);
       }
     }
-    if (need_res) {
-#pragma unroll
-      for (int e = 0; e < kElems; ++e) {
-        const float q = fexp2(fmaf(cq.get(e), kLog2e, -lse_q2));
-        Zpart += fmaxf(0.f, fexp2(fmaf(cp.get(e), kLog2e, -lse_p2)) - q);
-      }
-    }
     if (xs_here) {
       const float pstar = FKL ? -afk * fexp2(st.Mp * kLog2e - lse_p2) : 0.f;
       const int xs_slot = xo / (kThreads * VEC), xs_u = xo % VEC;
@@ -2422,19 +2413,11 @@ __global__ __launch_bounds__(kThreads, 8) void fsup_kernel(KParams P) {
       const float F = sc * fmaf(-D, e_t, tpart[1][tid]);
       Rpart = F;
       Spart = fmaf(sc, e_t, F);
-      if (need_res) {
-#pragma unroll
-        for (int e = 0; e < kElems; ++e) {
-          const float q = fexp2(fmaf(cq.get(e), kLog2e, -lse_q2));
-          Zpart += fmaxf(0.f, fexp2(fmaf(cp.get(e), kLog2e, -lse_p2)) - q);
-        }
-      }
     } else {
 #pragma unroll
       for (int e = 0; e < kElems; ++e) {
         const float zq = cq.get(e), zp = cp.get(e);
         const float q = fexp2(fmaf(zq, kLog2e, -lse_q2));
-        if (need_res) Zpart += fmaxf(0.f, fexp2(fmaf(zp, kLog2e, -lse_p2)) - q);
         const float dd = (zq - zp) - D;
         const float f = q > 0.f ? q * dd : 0.f;
         const bool inU = f <= c;
@@ -2442,14 +2425,13 @@ __global__ __launch_bounds__(kThreads, 8) void fsup_kernel(KParams P) {
         Spart += inU ? f + q : 0.f;
       }
     }
-    float s3[3] = {Spart, Rpart, Zpart};
-    const int ops3[3] = {OP_SUM, OP_SUM, OP_SUM};
-    wg_reduce_lead<3>(s3, ops3, fs.red);  // (fs.red is next written after the barrier below)
+    float s2v[2] = {Spart, Rpart};
+    const int ops2[2] = {OP_SUM, OP_SUM};
+    wg_reduce_lead<2>(s2v, ops2, fs.red);  // (fs.red is next written after the barrier below)
     if (tid == 0) {
       const size_t f0 = ((size_t)r * G + j) * kRec2;
-      tag_store(P.part2, f0 + 0, s3[0], call_epoch);
-      tag_store(P.part2, f0 + 1, s3[1], call_epoch);
-      if (SAMPLED) tag_store(P.part2, f0 + 2, s3[2], call_epoch);
+      tag_store(P.part2, f0 + 0, s2v[0], call_epoch);
+      tag_store(P.part2, f0 + 1, s2v[1], call_epoch);
     }
     // Second row barrier: wave 0 polls the G partial sums S and R until each
     // carries this call's epoch (two fields per chunk: no arrival counter).
@@ -2500,11 +2482,29 @@ __global__ __launch_bounds__(kThreads, 8) void fsup_kernel(KParams P) {
     gstar = grad_exact(zqs, st.Mp, lse_q2, D, lam, lamS, c, ace) - ace;
     if constexpr (FKL) gstar -= afk * fexp2(st.Mp * kLog2e - lse_p2);
   }
-  if (fast && need_res) {
-    float z1[1] = {Zpart};
-    const int o1[1] = {OP_SUM};
-    wg_reduce<1>(z1, o1, fs.red);
-    if (tid == 0) tag_store(P.part2, ((size_t)r * G + j) * kRec2 + 2, z1[0], call_epoch);
+  // Residual mass max(0, p - q) of this chunk, for the finaliser's draw, if
+  // no earlier row of the request has been seen rejected (both paths).
+  if (SAMPLED && !accept) {  // (uniform)
+    bool need_res = true;
+    if (ask) {
+      if (wave == 1) {
+        const unsigned long long any = __ballot(flag_l == 0.f);
+        if (lane == 0) fs.i[0] = any != 0ull;
+      }
+      __syncthreads();
+      need_res = fs.i[0] == 0;
+    }
+    if (need_res) {
+#pragma unroll
+      for (int e = 0; e < kElems; ++e) {
+        const float q = fexp2(fmaf(cq.get(e), kLog2e, -lse_q2));
+        Zpart += fmaxf(0.f, fexp2(fmaf(cp.get(e), kLog2e, -lse_p2)) - q);
+      }
+      float z1[1] = {Zpart};
+      const int o1[1] = {OP_SUM};
+      wg_reduce<1>(z1, o1, fs.red);
+      if (tid == 0) tag_store(P.part2, ((size_t)r * G + j) * kRec2 + 2, z1[0], call_epoch);
+    }
   }
   if (xs_here) {
     if (P.grad) ((uint16_t*)P.grad)[(size_t)n * V + xs] = __builtin_bit_cast(uint16_t, (__bf16)gstar);
