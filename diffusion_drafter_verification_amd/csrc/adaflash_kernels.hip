@@ -2403,14 +2403,16 @@ __global__ __launch_bounds__(kThreads, 8) void fsup_kernel(KParams P) {
     // thread and s = exp(m - lse_q)) takes its sums from the pass-1 partials,
     // sum_U f = s (W_t - D e_t) and sum_U q = s e_t, and writes the gradient
     // with the fast path's formula; the other waves recompute every term from
-    // the packed logits, which stay in registers.
+    // the packed logits, which stay in registers.  So does a wave with a
+    // non-finite pass-1 sum: a -inf logit makes an infinite or undefined term
+    // (0 * inf) there, while recomputed terms with q = 0 are taken as 0.
     const float sc = fexp2(-aq - lse_q2);
     const float tb = sc * (tpart[2][tid] + fmaxf(0.f, -D));
-    const bool wskip = __ballot(!(tb <= 0.999f * c)) == 0ull;  // (uniform in the wave)
+    const float e_t = tpart[0][tid];
+    const float F = sc * fmaf(-D, e_t, tpart[1][tid]);
+    const bool wskip = __ballot(!(tb <= 0.999f * c) || !__builtin_isfinite(F)) == 0ull;  // (uniform in the wave)
     float Spart = 0.f, Rpart = 0.f;
     if (wskip) {
-      const float e_t = tpart[0][tid];
-      const float F = sc * fmaf(-D, e_t, tpart[1][tid]);
       Rpart = F;
       Spart = fmaf(sc, e_t, F);
     } else {
@@ -2473,14 +2475,15 @@ __global__ __launch_bounds__(kThreads, 8) void fsup_kernel(KParams P) {
           for (int u = 0; u < VEC; ++u) {
             const int e = s2 * VEC + u;
             g[u] = grad_exact(cq.get(e), cp.get(e), lse_q2, D, lam, lamS, c, ace);
-            if constexpr (FKL) g[u] -= afk * fexp2(fmaf(cp.get(e), kLog2e, -lse_p2));
+            if constexpr (FKL)
+              g[u] += afk * (fexp2(fmaf(cq.get(e), kLog2e, -lse_q2)) - fexp2(fmaf(cp.get(e), kLog2e, -lse_p2)));
           }
         }
         store_slot(s2, g);
       }
     }
     gstar = grad_exact(zqs, st.Mp, lse_q2, D, lam, lamS, c, ace) - ace;
-    if constexpr (FKL) gstar -= afk * fexp2(st.Mp * kLog2e - lse_p2);
+    if constexpr (FKL) gstar += afk * (fexp2(fmaf(zqs, kLog2e, -lse_q2)) - fexp2(st.Mp * kLog2e - lse_p2));
   }
   // Residual mass max(0, p - q) of this chunk, for the finaliser's draw, if
   // no earlier row of the request has been seen rejected (both paths).

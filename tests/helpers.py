@@ -90,7 +90,7 @@ def compare_grad(g_gpu, g_ref, bf16=True):
     """2e-3 absolute, or one bf16 ulp of the reference where that is larger.
     Returns the largest absolute error."""
     err = np.abs(g_gpu.astype(np.float64) - g_ref)
-    bad = err > grad_tolerance(g_ref, bf16)
+    bad = ~(err <= grad_tolerance(g_ref, bf16))  # (an undefined entry counts as an error)
     assert not bad.any(), (np.argwhere(bad)[:5], err.max())
     assert abs(float(g_ref.sum())) < 1e-9 * g_ref.shape[-1] + 1e-9
     return float(err.max()) if err.size else 0.0

@@ -131,5 +131,7 @@ def grad_tolerance(g_ref: np.ndarray, bf16: bool = True) -> np.ndarray:
 def grad_errors(g_gpu: np.ndarray, g_ref: np.ndarray, bf16: bool = True) -> dict:
     err = np.abs(g_gpu.astype(np.float64) - g_ref)
     tol = grad_tolerance(g_ref, bf16)
-    return {"max_abs": float(err.max()) if err.size else 0.0, "over_tol": int((err > tol).sum()),
+    over = ~(err <= tol)  # (an undefined entry counts as over)
+    return {"max_abs": float(np.nanmax(err)) if err.size and not np.isnan(err).all() else 0.0,
+            "over_tol": int(over.sum()), "undefined": int(np.isnan(err).sum()),
             "ulp_entries": int((np.abs(g_ref) >= 0.5).sum())}

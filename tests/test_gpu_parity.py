@@ -195,17 +195,25 @@ def test_hand_worked_draws(case):
     assert np.abs(g["margins"][:, 1] - r["margins"][:, 1]).max() < 1e-6
 
 
-def test_masked_vocabulary_entries():
-    say("masked entries")
-    bt = W.generate(small("m", B=6, k=4, V=8192, seed=11), T=1.0)
-    ninf = np.uint16(0xFF80)
+@pytest.mark.parametrize("bf16", [True, False])
+@pytest.mark.parametrize("rows", ["both", "draft", "target"])
+def test_masked_vocabulary_entries(rows, bf16):
+    """-inf logits (probability 0) in 30% of the entries of the draft rows,
+    the target rows or both: a draft entry at -inf makes an undefined term
+    0 * inf in the chunk sums of the supervision pass, a target entry at -inf
+    an infinite KL term that is always clipped."""
+    say("masked entries", rows, "bf16" if bf16 else "fp32")
+    bt = W.generate(small("m", B=6, k=4, V=8192, bf16=bf16, seed=11), T=1.0)
+    ninf = np.uint16(0xFF80) if bf16 else np.float32(-np.inf)
     rng = np.random.default_rng(0)
     mask_t = rng.random(bt.target.shape) < 0.3
     mask_d = rng.random(bt.draft.shape) < 0.3
-    bt.target[mask_t] = ninf
-    bt.draft[mask_d] = ninf
+    if rows != "draft":
+        bt.target[mask_t] = ninf
+    if rows != "target":
+        bt.draft[mask_d] = ninf
     # keep the drafts on tokens the drafter can produce
-    zq = W.bf16_bits_to_f32(bt.draft)
+    zq = W.bf16_bits_to_f32(bt.draft) if bf16 else bt.draft
     bt.tokens[:] = zq.argmax(-1)
     for c in (10.0, 0.01):
         check_verify(bt, 1.0, opd=True, c=c)
