@@ -643,6 +643,18 @@ __device__ __forceinline__ RowSlot row_slot_interleaved(const KParams& P, int s,
   return o;
 }
 
+// Slot s = b k + i of the draft positions alone (no bonus rows).
+__device__ __forceinline__ RowSlot row_slot_draft(const KParams& P, int s) {
+  RowSlot o;
+  o.b = s / P.k;
+  o.i = s - o.b * P.k;
+  const int L = P.pack_here ? clamp_len(P, o.b) : (int)sload_u32(P.Lc + o.b);
+  const int off = P.pack_here ? 0 : (int)sload_u32(P.row_offsets + o.b);
+  o.n = o.i < L ? off + o.i : -1;
+  if (L < 0 || o.i >= L) o.b = -1;
+  return o;
+}
+
 // Two values rounded to bf16 (nearest even) and packed: one v_cvt_pk_bf16_f32.
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -865,8 +877,8 @@ __device__ void finalize_request(const KParams& P, int b, FinShared& fs, const K
     bool resid;
     if constexpr (KNOWN) {
       // The residual partials of row A (waiting for this call's tags), then
-      // the known statistics; only a bonus draw (or a zero residual) reads
-      // the target chunk records of its row.
+      // the known statistics; a bonus draw waits for the bonus row's chunk
+      // statistics, and a zero residual reads row A's target records.
       A = kr.A;
       const int rs = r0 + A;
       bool ok = true;
@@ -878,7 +890,6 @@ __device__ void finalize_request(const KParams& P, int b, FinShared& fs, const K
           ok = poll_fields<1>(P.part2, kRec2, A < L && jj < G, rs * G + jj, 2, 1, kr.ep, v1, P.status) && ok;
         res[h] = A < L && jj < G ? v1[0] : 0.f;
       }
-      (void)ok;  // (a timed-out wait has flagged the status word)
       Zres = wave_reduce<OP_SUM>(res[0] + res[1]);
       resid = A < L && Zres > 0.f;
       Mp = kr.Mp;
@@ -886,13 +897,24 @@ __device__ void finalize_request(const KParams& P, int b, FinShared& fs, const K
       Mq = kr.Mq;
       SqT = kr.SqT;
       if (!resid) {
+        // Row A's target statistics: the bonus row's from the residual
+        // kernel's tagged fields, a rejected row's (zero residual) from the
+        // statistics kernel's records.
         float mp[2], spT[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int jj = lane + 64 * h;
           mp[h] = neg_inf();
           spT[h] = 0.f;
-          if (jj < G) {
+          if (A == L) {
+            float v2[2] = {neg_inf(), 0.f};
+            if (h == 0 || G > 64)
+              ok = poll_fields<2>(P.part2, kRec2, jj < G, rs * G + jj, 0, 2, kr.ep, v2, P.status) && ok;
+            if (jj < G) {
+              mp[h] = v2[0];
+              spT[h] = v2[1];
+            }
+          } else if (jj < G) {
             const float* rec = P.part1 + ((size_t)rs * G + jj) * kRec1;
             mp[h] = pub_load(rec + 0);
             spT[h] = pub_load(rec + 2);
@@ -905,6 +927,7 @@ __device__ void finalize_request(const KParams& P, int b, FinShared& fs, const K
         Mq = neg_inf();
         SqT = 1.f;
       }
+      (void)ok;  // (a timed-out wait has flagged the status word)
     } else {
       const unsigned long long rej = __ballot(lane < L && acc_flag == 0.f);
       A = rej ? min((int)__builtin_ctzll(rej), L) : L;
@@ -2641,14 +2664,16 @@ __global__ __launch_bounds__(kThreads) void gstat_kernel(KParams P) {
 // Sampled verification without supervision needs the row statistics in one
 // place only (the accept test), and the residual of one row per request, so
 // it runs without any barrier between workgroups: vstat_kernel publishes the
-// chunk statistics of every row in use and exits; vres_kernel (one workgroup
-// per request and pair of chunks) combines them, runs the accept tests, finds
-// the first rejection and, for a rejected request, computes the residual mass
-// of its chunks of that row (the one row read a second time); the last of the
-// request's workgroups draws.
+// chunk statistics of every draft row in use and exits; vres_kernel (one
+// workgroup per request and pair of chunks) combines them, runs the accept
+// tests, finds the first rejection and, for a rejected request, computes the
+// residual mass of its chunks of that row (the one row read a second time),
+// or, for a request that accepts every draft, the statistics of its chunks
+// of the bonus row (read only then); the last of the request's workgroups
+// draws.
 
-// Pass 1 of one (row, chunk): chunk maxima of z_p (and z_q for draft rows)
-// and sums of exp((z - m) / T), published as a part1 record.
+// Pass 1 of one (draft row, chunk): chunk maxima of z_p and z_q and sums of
+// exp((z - m) / T), published as a part1 record.
 template <bool BF16, bool ALIGNED>
 __global__ __launch_bounds__(kThreads) void vstat_kernel(KParams P) {
   __shared__ float red[kWaves * 8];
@@ -2657,31 +2682,29 @@ __global__ __launch_bounds__(kThreads) void vstat_kernel(KParams P) {
   const int s_ = (int)blockIdx.x / G;
   const int j = (int)blockIdx.x - s_ * G;
   if (P.pack_here && blockIdx.x == 0) pack_rows_block(P);
-  const RowSlot sl = row_slot_interleaved(P, s_, true);
+  // Draft positions only (slot s = b k + i): the bonus row of a request is
+  // read by the residual kernel, and only when every draft is accepted.
+  const RowSlot sl = row_slot_draft(P, s_);
   if (sl.b < 0) return;
   const int b = sl.b, i = sl.i;
   const int r = b * (k + 1) + i;
-  const bool draft_row = sl.n >= 0;
   const int v0 = j * kChunk;
   const void* trow = target_row_ptr<BF16>(P, b, i, sl.n);
-  const void* drow = draft_row ? draft_row_ptr<BF16>(P, b, i, sl.n) : nullptr;
+  const void* drow = draft_row_ptr<BF16>(P, b, i, sl.n);
   // The chunk holding the draft token (clamped as the accept test clamps it)
   // also publishes both logits there, for the accept test.
-  bool xhere = false;
+  int x = (int)sload_u32(P.tokens + (size_t)b * k + i);
+  x = x < 0 ? 0 : (x >= V ? V - 1 : x);
+  const bool xhere = x / kChunk == j;
   float zpx = 0.f, zqx = 0.f;
-  if (draft_row) {
-    int x = (int)sload_u32(P.tokens + (size_t)b * k + i);
-    x = x < 0 ? 0 : (x >= V ? V - 1 : x);
-    xhere = x / kChunk == j;
-    if (xhere) {
-      zpx = sload_logit<BF16>(trow, x);
-      zqx = sload_logit<BF16>(drow, x);
-    }
+  if (xhere) {
+    zpx = sload_logit<BF16>(trow, x);
+    zqx = sload_logit<BF16>(drow, x);
   }
   Chunk<BF16> cp, cq;
   load_chunk<BF16, ALIGNED>(cp, trow, v0, V);
-  if (draft_row) load_chunk<BF16, ALIGNED>(cq, drow, v0, V);
-  float m[2] = {chunk_max<BF16>(cp), draft_row ? chunk_max<BF16>(cq) : neg_inf()};
+  load_chunk<BF16, ALIGNED>(cq, drow, v0, V);
+  float m[2] = {chunk_max<BF16>(cp), chunk_max<BF16>(cq)};
   cp.opaque();
   cq.opaque();
   {
@@ -2693,10 +2716,8 @@ __global__ __launch_bounds__(kThreads) void vstat_kernel(KParams P) {
   float sv[2] = {0.f, 0.f};
 #pragma unroll
   for (int e = 0; e < kElems; ++e) sv[0] += fexp2(fmaf(cp.get(e), P.kT, ap));
-  if (draft_row) {
 #pragma unroll
-    for (int e = 0; e < kElems; ++e) sv[1] += fexp2(fmaf(cq.get(e), P.kT, aq));
-  }
+  for (int e = 0; e < kElems; ++e) sv[1] += fexp2(fmaf(cq.get(e), P.kT, aq));
   const int ops[2] = {OP_SUM, OP_SUM};
   wg_reduce_lead<2>(sv, ops, red);
   if (tid == 0) {
@@ -2789,6 +2810,53 @@ __device__ void residual_of_chunks(const KParams& P, int b, int A, int h, const 
     for (int t = 0; t < kResChunks; ++t) {
       const int jt = kResChunks * h + t;
       if (jt < G) tag_store(P.part2, ((size_t)rA * G + jt) * kRec2 + 2, z[t], ep);
+    }
+  }
+}
+
+// Statistics at T of chunks kResChunks*h ... of the bonus row L of request b
+// (a request that accepts every draft), as the statistics kernel computes
+// them for draft rows: the chunk maximum m of z_p and sum exp((z - m) / T),
+// published as epoch-tagged fields 0 and 1 of the row's part2 records.
+template <bool BF16, bool ALIGNED>
+__device__ void bonus_of_chunks(const KParams& P, int b, int L, int h, float* red, uint32_t ep) {
+  const int tid = threadIdx.x;
+  const int G = P.G, k = P.k, V = P.V;
+  const int rL = b * (k + 1) + L;
+  const void* trow = target_row_ptr<BF16>(P, b, L);
+  Chunk<BF16> cp[kResChunks];
+#pragma unroll
+  for (int t = 0; t < kResChunks; ++t) {
+    const int jt = kResChunks * h + t;
+    if (jt < G) load_chunk<BF16, ALIGNED>(cp[t], trow, jt * kChunk, V);
+  }
+  float m[kResChunks], sv[kResChunks];
+  int o[kResChunks];
+#pragma unroll
+  for (int t = 0; t < kResChunks; ++t) {
+    m[t] = kResChunks * h + t < G ? chunk_max<BF16>(cp[t]) : neg_inf();
+    o[t] = OP_MAX;
+  }
+  wg_reduce<kResChunks>(m, o, red);
+#pragma unroll
+  for (int t = 0; t < kResChunks; ++t) {
+    sv[t] = 0.f;
+    o[t] = OP_SUM;
+    if (kResChunks * h + t < G) {
+      const float a = uniform(m[t] == neg_inf() ? 0.f : -m[t] * P.kT);
+#pragma unroll
+      for (int e = 0; e < kElems; ++e) sv[t] += fexp2(fmaf(cp[t].get(e), P.kT, a));
+    }
+  }
+  wg_reduce_lead<kResChunks>(sv, o, red);
+  if (tid == 0) {
+#pragma unroll
+    for (int t = 0; t < kResChunks; ++t) {
+      const int jt = kResChunks * h + t;
+      if (jt < G) {
+        tag_store(P.part2, ((size_t)rL * G + jt) * kRec2 + 0, m[t], ep);
+        tag_store(P.part2, ((size_t)rL * G + jt) * kRec2 + 1, sv[t], ep);
+      }
     }
   }
 }
@@ -2899,6 +2967,7 @@ __global__ __launch_bounds__(kThreads) void vres_kernel(KParams P) {
   __syncthreads();
   const int A = s_first;
   if (A < L) residual_of_chunks<BF16, ALIGNED>(P, b, A, h, s_row, red, ep);
+  else bonus_of_chunks<BF16, ALIGNED>(P, b, L, h, red, ep);
   // The last of the request's GH workgroups to arrive draws the correction or
   // bonus token, with the first rejection and its row's statistics already
   // known; it waits for each residual partial's epoch tag (the others count
@@ -3067,7 +3136,8 @@ hipError_t dispatch_mode(const KParams& p, int grid, int opd, int vmode, bool t1
     e = launch_dominant(gstat_kernel<BF16, ALIGNED>, p.B * ng * p.G, st, p);
   }
   else if (vmode == 2) {
-    e = launch_dominant(vstat_kernel<BF16, ALIGNED>, grid, st, p);
+    // (draft positions only: B k slots)
+    e = launch_dominant(vstat_kernel<BF16, ALIGNED>, p.B * p.k * p.G, st, p);
     if (e != hipSuccess) return e;
     // (vres_kernel draws as well)
     const int gh = (p.G + kResChunks - 1) / kResChunks;
