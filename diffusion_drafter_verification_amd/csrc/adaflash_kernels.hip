@@ -98,6 +98,9 @@ struct KParams {
   // blocks clamp their own request's length from verify_len.
   int pack_here;
   const int32_t* verify_len;
+  // Verification alone: chunks of a row per residual workgroup (the residual
+  // grid is sized to be resident at once).
+  int res_chunks;
 };
 
 // ---------------------------------------------------------------- primitives
@@ -2747,8 +2750,8 @@ __device__ __forceinline__ void fold_ms(float& M, float& S, float m, float s, fl
   }
 }
 
-// Chunks of the rejected row per residual workgroup (fewer workgroups than
-// the GPU holds at once at B = 128).
+// Chunks of a row loaded together by a residual workgroup (one round; a
+// workgroup takes P.res_chunks chunks in rounds of this many).
 constexpr int kResChunks = 2;
 
 // Reduction inside each 16-lane row of a wave (every lane of the row gets
@@ -2766,11 +2769,12 @@ __device__ __forceinline__ float row16_reduce(float v) {
   return v;
 }
 
-// Residual masses sum max(0, p - q) of chunks kResChunks*h ... of the rejected
-// row A of request b, for the draw (s_row: that row's statistics).
+// Residual masses sum max(0, p - q) of chunks jb, jb + 1, ... (kResChunks of
+// them, up to je) of the rejected row A of request b, for the draw (s_row:
+// that row's statistics).
 template <bool BF16, bool ALIGNED>
-__device__ void residual_of_chunks(const KParams& P, int b, int A, int h, const float (*s_row)[4], float* red,
-                                   uint32_t ep) {
+__device__ void residual_of_chunks(const KParams& P, int b, int A, int jb, int je, const float (*s_row)[4],
+                                   float* red, uint32_t ep) {
   const int tid = threadIdx.x;
   const int G = P.G, k = P.k, V = P.V;
   const int r0 = b * (k + 1);
@@ -2781,8 +2785,8 @@ __device__ void residual_of_chunks(const KParams& P, int b, int A, int h, const 
   Chunk<BF16> cp[kResChunks], cq[kResChunks];
 #pragma unroll
   for (int t = 0; t < kResChunks; ++t) {
-    const int jt = kResChunks * h + t;
-    if (jt < G) {
+    const int jt = jb + t;
+    if (jt < je) {
       load_chunk<BF16, ALIGNED>(cp[t], trow, jt * kChunk, V);
       load_chunk<BF16, ALIGNED>(cq[t], drow, jt * kChunk, V);
     }
@@ -2795,7 +2799,7 @@ __device__ void residual_of_chunks(const KParams& P, int b, int A, int h, const 
   for (int t = 0; t < kResChunks; ++t) {
     z[t] = 0.f;
     o[t] = OP_SUM;
-    if (kResChunks * h + t < G) {
+    if (jb + t < je) {
 #pragma unroll
       for (int e = 0; e < kElems; ++e) {
         const float pv = mul_rn(fexp2(fmaf(cp[t].get(e), P.kT, ap)), invSp);
@@ -2808,18 +2812,19 @@ __device__ void residual_of_chunks(const KParams& P, int b, int A, int h, const 
   if (tid == 0) {
 #pragma unroll
     for (int t = 0; t < kResChunks; ++t) {
-      const int jt = kResChunks * h + t;
-      if (jt < G) tag_store(P.part2, ((size_t)rA * G + jt) * kRec2 + 2, z[t], ep);
+      const int jt = jb + t;
+      if (jt < je) tag_store(P.part2, ((size_t)rA * G + jt) * kRec2 + 2, z[t], ep);
     }
   }
 }
 
-// Statistics at T of chunks kResChunks*h ... of the bonus row L of request b
-// (a request that accepts every draft), as the statistics kernel computes
-// them for draft rows: the chunk maximum m of z_p and sum exp((z - m) / T),
-// published as epoch-tagged fields 0 and 1 of the row's part2 records.
+// Statistics at T of chunks jb, jb + 1, ... (kResChunks of them, up to je) of
+// the bonus row L of request b (a request that accepts every draft), as the
+// statistics kernel computes them for draft rows: the chunk maximum m of z_p
+// and sum exp((z - m) / T), published as epoch-tagged fields 0 and 1 of the
+// row's part2 records.
 template <bool BF16, bool ALIGNED>
-__device__ void bonus_of_chunks(const KParams& P, int b, int L, int h, float* red, uint32_t ep) {
+__device__ void bonus_of_chunks(const KParams& P, int b, int L, int jb, int je, float* red, uint32_t ep) {
   const int tid = threadIdx.x;
   const int G = P.G, k = P.k, V = P.V;
   const int rL = b * (k + 1) + L;
@@ -2827,14 +2832,14 @@ __device__ void bonus_of_chunks(const KParams& P, int b, int L, int h, float* re
   Chunk<BF16> cp[kResChunks];
 #pragma unroll
   for (int t = 0; t < kResChunks; ++t) {
-    const int jt = kResChunks * h + t;
-    if (jt < G) load_chunk<BF16, ALIGNED>(cp[t], trow, jt * kChunk, V);
+    const int jt = jb + t;
+    if (jt < je) load_chunk<BF16, ALIGNED>(cp[t], trow, jt * kChunk, V);
   }
   float m[kResChunks], sv[kResChunks];
   int o[kResChunks];
 #pragma unroll
   for (int t = 0; t < kResChunks; ++t) {
-    m[t] = kResChunks * h + t < G ? chunk_max<BF16>(cp[t]) : neg_inf();
+    m[t] = jb + t < je ? chunk_max<BF16>(cp[t]) : neg_inf();
     o[t] = OP_MAX;
   }
   wg_reduce<kResChunks>(m, o, red);
@@ -2842,7 +2847,7 @@ __device__ void bonus_of_chunks(const KParams& P, int b, int L, int h, float* re
   for (int t = 0; t < kResChunks; ++t) {
     sv[t] = 0.f;
     o[t] = OP_SUM;
-    if (kResChunks * h + t < G) {
+    if (jb + t < je) {
       const float a = uniform(m[t] == neg_inf() ? 0.f : -m[t] * P.kT);
 #pragma unroll
       for (int e = 0; e < kElems; ++e) sv[t] += fexp2(fmaf(cp[t].get(e), P.kT, a));
@@ -2852,8 +2857,8 @@ __device__ void bonus_of_chunks(const KParams& P, int b, int L, int h, float* re
   if (tid == 0) {
 #pragma unroll
     for (int t = 0; t < kResChunks; ++t) {
-      const int jt = kResChunks * h + t;
-      if (jt < G) {
+      const int jt = jb + t;
+      if (jt < je) {
         tag_store(P.part2, ((size_t)rL * G + jt) * kRec2 + 0, m[t], ep);
         tag_store(P.part2, ((size_t)rL * G + jt) * kRec2 + 1, sv[t], ep);
       }
@@ -2881,9 +2886,10 @@ __global__ __launch_bounds__(kThreads) void vres_kernel(KParams P) {
   __shared__ FinShared fs;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = P.G, k = P.k, V = P.V;
-  const int GH = (G + kResChunks - 1) / kResChunks;
+  const int RC = P.res_chunks;
+  const int GH = (G + RC - 1) / RC;
   const int b = (int)blockIdx.x / GH;
-  const int h = (int)blockIdx.x - b * GH;  // chunks kResChunks*h ...
+  const int h = (int)blockIdx.x - b * GH;  // chunks RC h ... RC h + RC - 1
   const int j = h;                         // (workgroup h == 0 writes the row flags)
   const int L = P.Lc[b];
   if (L < 0) return;
@@ -2966,8 +2972,12 @@ __global__ __launch_bounds__(kThreads) void vres_kernel(KParams P) {
   }
   __syncthreads();
   const int A = s_first;
-  if (A < L) residual_of_chunks<BF16, ALIGNED>(P, b, A, h, s_row, red, ep);
-  else bonus_of_chunks<BF16, ALIGNED>(P, b, L, h, red, ep);
+  const int je = min(G, RC * h + RC);
+  for (int jb = RC * h; jb < je; jb += kResChunks) {
+    if (jb > RC * h) __syncthreads();  // (red is read by thread 0 after the previous round)
+    if (A < L) residual_of_chunks<BF16, ALIGNED>(P, b, A, jb, je, s_row, red, ep);
+    else bonus_of_chunks<BF16, ALIGNED>(P, b, L, jb, je, red, ep);
+  }
   // The last of the request's GH workgroups to arrive draws the correction or
   // bonus token, with the first rejection and its row's statistics already
   // known; it waits for each residual partial's epoch tag (the others count
@@ -3140,7 +3150,7 @@ hipError_t dispatch_mode(const KParams& p, int grid, int opd, int vmode, bool t1
     e = launch_dominant(vstat_kernel<BF16, ALIGNED>, p.B * p.k * p.G, st, p);
     if (e != hipSuccess) return e;
     // (vres_kernel draws as well)
-    const int gh = (p.G + kResChunks - 1) / kResChunks;
+    const int gh = (p.G + p.res_chunks - 1) / p.res_chunks;
     hipLaunchKernelGGL((vres_kernel<BF16, ALIGNED>), dim3(p.B * gh), dim3(kThreads), 0, st, p);
     return hipGetLastError();
   }
@@ -3235,6 +3245,13 @@ hipError_t launch(const LaunchArgs& a) {
   p.packed = a.packed;
   p.pack_here = pack_here;
   p.verify_len = a.verify_len;
+  {
+    // Residual workgroups of verification alone: enough chunks each that the
+    // B requests' workgroups fit the GPU at once (four per CU at that
+    // kernel's register use), at least one round.
+    const long long want = ((long long)a.B * p.G + 1023) / 1024;
+    p.res_chunks = (int)(want < kResChunks ? kResChunks : (want > p.G ? p.G : want));
+  }
 
   const int vmode = a.verify ? (a.T > 0.f ? 2 : 1) : 0;
   const int rows_max = a.B * (a.k + bonus);
