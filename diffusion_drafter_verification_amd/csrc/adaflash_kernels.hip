@@ -1016,7 +1016,9 @@ __device__ void finalize_request(const KParams& P, int b, FinShared& fs, const K
     const float base = __shfl(jc < 64 ? ex[0] : ex[1], jc & 63, 64);
 
     // Scan chunk jc in index order: per-entry masses, one prefix sum over
-    // (slot, thread, entry), the lowest index whose running sum passes thr.
+    // (slot, thread, entry), the lowest index with positive mass whose
+    // running sum passes thr (a thread's start, taken from the prefix sum,
+    // can pass thr by rounding alone: a zero-mass entry is never drawn).
     const void* trow = target_row_ptr<BF16>(P, b, A);
     const void* drow = draft_row_ptr<BF16>(P, b, A);
     const int v0 = jc * kChunk;
@@ -1071,15 +1073,15 @@ __device__ void finalize_request(const KParams& P, int b, FinShared& fs, const K
         const int idx = entry_index<BF16>(v0, e);
         const float before = cum;
         cum += w[e];
-        if (w[e] > 0.f) {
+        if (w[e] > 0.f) {  // (entries past V have no mass)
           last_pos = idx;
           last_before = before;
           last_at = cum;
-        }
-        if (found == kIntMax && cum > thr && idx < V) {
-          found = idx;
-          found_before = before;
-          found_at = cum;
+          if (found == kIntMax && cum > thr) {
+            found = idx;
+            found_before = before;
+            found_at = cum;
+          }
         }
       }
       run += stot;
@@ -2428,8 +2430,9 @@ __global__ __launch_bounds__(kThreads, 8) void fsup_kernel(KParams P) {
     // thread: f_v <= s (A_t + max(0, -D)), with A_t = max e dz over the
     // thread and s = exp(m - lse_q)) takes its sums from the pass-1 partials,
     // sum_U f = s (W_t - D e_t) and sum_U q = s e_t, and writes the gradient
-    // with the fast path's formula; the other waves recompute every term from
-    // the packed logits, which stay in registers.  So does a wave with a
+    // with the fast path's formula; the other waves recompute their sums'
+    // terms in fp32 from the packed logits, which stay in registers, and keep
+    // each entry's clip decision for the gradient.  So does a wave with a
     // non-finite pass-1 sum: a -inf logit makes an infinite or undefined term
     // (0 * inf) there, while recomputed terms with q = 0 are taken as 0.
     const float sc = fexp2(-aq - lse_q2);
@@ -2438,6 +2441,8 @@ __global__ __launch_bounds__(kThreads, 8) void fsup_kernel(KParams P) {
     const float F = sc * fmaf(-D, e_t, tpart[1][tid]);
     const bool wskip = __ballot(!(tb <= 0.999f * c) || !__builtin_isfinite(F)) == 0ull;  // (uniform in the wave)
     float Spart = 0.f, Rpart = 0.f;
+    uint32_t ubits = 0u;  // (other waves) this thread's entries in U with q > 0
+    static_assert(kElems <= 32, "one bit per entry");
     if (wskip) {
       Rpart = F;
       Spart = fmaf(sc, e_t, F);
@@ -2451,6 +2456,7 @@ __global__ __launch_bounds__(kThreads, 8) void fsup_kernel(KParams P) {
         const bool inU = f <= c;
         Rpart += inU ? f : c;
         Spart += inU ? f + q : 0.f;
+        ubits |= (inU && q > 0.f ? 1u : 0u) << e;
       }
     }
     float s2v[2] = {Spart, Rpart};
@@ -2479,18 +2485,22 @@ __global__ __launch_bounds__(kThreads, 8) void fsup_kernel(KParams P) {
     if (!__builtin_amdgcn_readfirstlane(fs.i[3])) return;
     Rrow = uniform(fs.f[1]);
     const float lamS = uniform(lam * fs.f[0]);
-    // Unclipped entries: g = q (ace - lambda S + lambda (dz - D + 1)).
+    // Unclipped entries: g = q (ace - lambda S + lambda (dz - D + 1)); clipped
+    // entries (and those with q = 0, whose gradient is 0): g = q (ace -
+    // lambda S).  q = e s with e from the pass-1 cache, as on the fast path;
+    // the other waves' clip decisions are the ones their sums S and R took.
     const float c1x = fmaf(lam, 1.f - D, ace) - lamS + afk;
     const float lsc = lam * sc, csc = c1x * sc;
+    const float Dm1 = uniform(D - 1.f);  // (lsc (D - 1) + csc = sc (ace - lambda S))
     if (P.grad) {
 #pragma unroll
       for (int s2 = 0; s2 < NV; ++s2) {
         float g[VEC];
-        if (wskip) {
-          const uint4 h4 = *(const uint4*)(ecache + ((size_t)s2 * kThreads + tid) * 4);
-          const uint32_t hw[4] = {h4.x, h4.y, h4.z, h4.w};
-          float dz8[8];
-          bf16_diff8(&cq.w[s2 * 4], &cp.w[s2 * 4], dz8);
+        const uint4 h4 = *(const uint4*)(ecache + ((size_t)s2 * kThreads + tid) * 4);
+        const uint32_t hw[4] = {h4.x, h4.y, h4.z, h4.w};
+        float dz8[8];
+        bf16_diff8(&cq.w[s2 * 4], &cp.w[s2 * 4], dz8);
+        if (wskip) {  // (no entry of the wave is clipped)
 #pragma unroll
           for (int u = 0; u < VEC; ++u) {
             const float pterm = FKL ? -afk * fexp2(fmaf(cp.get(s2 * VEC + u), kLog2e, -lse_p2)) : 0.f;
@@ -2499,10 +2509,9 @@ __global__ __launch_bounds__(kThreads, 8) void fsup_kernel(KParams P) {
         } else {
 #pragma unroll
           for (int u = 0; u < VEC; ++u) {
-            const int e = s2 * VEC + u;
-            g[u] = grad_exact(cq.get(e), cp.get(e), lse_q2, D, lam, lamS, c, ace);
-            if constexpr (FKL)
-              g[u] += afk * (fexp2(fmaf(cq.get(e), kLog2e, -lse_q2)) - fexp2(fmaf(cp.get(e), kLog2e, -lse_p2)));
+            const float pterm = FKL ? -afk * fexp2(fmaf(cp.get(s2 * VEC + u), kLog2e, -lse_p2)) : 0.f;
+            const bool un = ((ubits >> (s2 * VEC + u)) & 1u) != 0u;
+            g[u] = fma_f16(hw[u / 2], u & 1, fmaf(lsc, un ? dz8[u] : Dm1, csc), pterm);
           }
         }
         store_slot(s2, g);
