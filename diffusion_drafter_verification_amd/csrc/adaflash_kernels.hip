@@ -1583,8 +1583,10 @@ __device__ __forceinline__ int shift_of(float m) {
 // with the call's epoch.  Wave 0 waits for the row's G arrivals and for the
 // records (the row barrier), reduces them, chunk j in lane j (G <= 32), and
 // hands the results to the other waves through fs.f; lse_q2 and lse_p2 are
-// in log2 units.
-template <bool SAMPLED, bool FKL, typename SH>
+// in log2 units.  EARLY: the counter wait ends with one chunk still to
+// arrive, and that chunk's record is polled for with the others' loaded
+// (measured faster where most rows take the exact path, slower otherwise).
+template <bool SAMPLED, bool FKL, typename SH, bool EARLY = false>
 __device__ SupStats combine_sup_pow2(const KParams& P, int r, SH& fs, float zpx, float zqx, float u, uint32_t ep) {
   const int tid = threadIdx.x;
   const int G = P.G;  // <= 32 (the host dispatches larger rows elsewhere)
@@ -1594,7 +1596,7 @@ __device__ SupStats combine_sup_pow2(const KParams& P, int r, SH& fs, float zpx,
     const int c = tid & 31, half = tid >> 5;
     float h[4] = {0.f, 0.f, 0.f, 0.f};
     const float* recs = (const float*)((const uint64_t*)P.part1 + (size_t)r * G * kRec1);
-    const bool ok = wait_count(P.rowcnt + (size_t)r * kCounterStride, G, P.status) &&
+    const bool ok = wait_count(P.rowcnt + (size_t)r * kCounterStride, EARLY ? G - 1 : G, P.status) &&
                     poll_fields<4>(recs, kRec1, c < G, c, 4 * half, half && !FKL ? 3 : 4, ep, h, P.status);
     float o[4];
 #pragma unroll
@@ -2347,7 +2349,7 @@ __global__ __launch_bounds__(kThreads, 8) void fsup_kernel(KParams P) {
   }
   if (!draft_row) return;
 
-  const SupStats st = combine_sup_pow2<SAMPLED, FKL>(P, r, fs, zpx, zqx, u_acc, call_epoch);
+  const SupStats st = combine_sup_pow2<SAMPLED, FKL, SupShared, !LOOSE>(P, r, fs, zpx, zqx, u_acc, call_epoch);
   if (!st.alive) return;
   const float lse_q2 = st.lse_q2, lse_p2 = st.lse_p2, D = st.D, KL = st.KL;
   const float wi = P.wdecay > 0.f ? uniform(fexp2(-(float)i * kLog2e / P.wdecay)) : 1.f;
