@@ -219,6 +219,35 @@ def test_masked_vocabulary_entries(rows, bf16):
         check_verify(bt, 1.0, opd=True, c=c)
 
 
+@pytest.mark.parametrize("c", [3.0, 4.5, 8.0])
+def test_clipped_entries_at_large_c(c):
+    """Entries clipped at a large threshold: in half of the rows one token
+    the drafter is sure of (z_q = 12) is one the target rules out (z_p =
+    -12), so q (log q - log p) there is about 24 > c.  From c = 4 the
+    supervision kernel takes its looser per-thread clip bound, below it the
+    tighter one; both must send these rows to the exact path and match the
+    oracle's clipped losses and gradients."""
+    say("clipped at large c", c)
+    bt = W.generate(small("x", B=6, k=4, V=8192, seed=21), T=1.0)
+    zt = W.bf16_bits_to_f32(bt.target).astype(np.float32)
+    zd = W.bf16_bits_to_f32(bt.draft).astype(np.float32)
+    rng = np.random.default_rng(5)
+    hit = rng.random(bt.draft.shape[:2]) < 0.5
+    v = rng.integers(0, bt.draft.shape[2], size=bt.draft.shape[:2])
+    for b, i in zip(*np.nonzero(hit)):
+        zd[b, i, v[b, i]] = 12.0
+        zt[b, i, v[b, i]] = -12.0
+    bt.target[:] = W.f32_to_bf16_bits(zt)
+    bt.draft[:] = W.f32_to_bf16_bits(zd)
+    zq = W.bf16_bits_to_f32(bt.draft).astype(np.float64)
+    zp = W.bf16_bits_to_f32(bt.target[:, :-1]).astype(np.float64)
+    lq = zq - np.logaddexp.reduce(zq, axis=-1, keepdims=True)
+    lp = zp - np.logaddexp.reduce(zp, axis=-1, keepdims=True)
+    f = np.exp(lq) * (lq - lp)
+    assert (f.max(-1) > c)[hit].all()  # (the clip is real in every such row)
+    check_verify(bt, 1.0, opd=True, c=c)
+
+
 def test_ties_take_the_lowest_index():
     say("ties")
     B, k, V = 4, 3, 9000
