@@ -2106,7 +2106,11 @@ __global__ __launch_bounds__(kThreads, (sup_min_waves<BF16, ALIGNED, VMODE, FKL>
 //    integer method);
 //  * the padding past V is -2^120, a bf16 pattern that is finite as f16;
 //  * a bonus row whose request already has a rejected draft is not loaded
-//    (the finaliser reads row L only when every draft is accepted).
+//    (the finaliser reads row L only when every draft is accepted);
+//  * the exact path writes its gradient from the pass-1 cache as well, with
+//    each entry's clip decision kept as one bit;
+//  * for large c the per-thread clip bound skips a multiplication per entry
+//    (kLooseClip).
 
 constexpr uint32_t kPadBf16x2 = 0xFB80FB80u;  // -2^120 in both halves
 
@@ -2447,10 +2451,10 @@ __global__ __launch_bounds__(kThreads, 8) void fsup_kernel(KParams P) {
   } else {
     // Exact path: clipped sums, second barrier, then the gradient.  A wave
     // whose entries cannot be clipped (the fast path's bound, taken per
-    // thread: f_v <= s (A_t + max(0, -D)), with A_t = max e dz over the
-    // thread and s = exp(m - lse_q)) takes its sums from the pass-1 partials,
-    // sum_U f = s (W_t - D e_t) and sum_U q = s e_t, and writes the gradient
-    // with the fast path's formula; the other waves recompute their sums'
+    // thread: f_v <= s (A_t + max(0, -D)), with A_t the thread's bound on
+    // e dz from pass 1 and s = exp(m - lse_q)) takes its sums from the pass-1
+    // partials, sum_U f = s (W_t - D e_t) and sum_U q = s e_t, and writes the
+    // gradient with the fast path's formula; the other waves recompute their sums'
     // terms in fp32 from the packed logits, which stay in registers, and keep
     // each entry's clip decision for the gradient.  So does a wave with a
     // non-finite pass-1 sum: a -inf logit makes an infinite or undefined term
