@@ -2635,8 +2635,11 @@ __device__ void pack_rows_block(const KParams& P) {
 // index.  One workgroup takes chunk j of kGRows consecutive rows of a request
 // (all their loads in flight together) and publishes one (max, argmax)
 // record per row, with two workgroup reductions for all its rows.  Rows
-// beyond the request's bonus row are skipped.
-constexpr int kGRows = 4;
+// beyond the request's bonus row are skipped.  One row per workgroup:
+// measured faster than two or four (c128: 56.9 against 58.5 and 59.9 us;
+// more rows hold more registers, five workgroups per CU at four rows against
+// eight at one, and leave the rows of partly used groups idle).
+constexpr int kGRows = 1;
 
 template <bool BF16, bool ALIGNED>
 __global__ __launch_bounds__(kThreads) void gstat_kernel(KParams P) {
