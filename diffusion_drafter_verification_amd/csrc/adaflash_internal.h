@@ -101,25 +101,30 @@ struct LhWorkspace {
   float* zsum;       // [B*k, Hp] their sum (when the caller keeps no copy)
   float* hbar;       // [B, Hp] pooled vectors (backward)
   float* ds;         // [B] d loss / d logit (backward)
-  uint16_t* dzh;     // [B*k, Hq] dZ1, bf16 high part (backward; Hq = Hp rounded up to 8)
-  uint16_t* dzl;     // [B*k, Hq] dZ1, bf16 remainder (backward)
+  uint16_t* dzh;     // [ceil(B*k / 8), Hp, 8] dZ1 in blocks of eight rows, bf16 high part (backward)
+  uint16_t* dzl;     // the same, bf16 remainder (backward)
   float* db1_part;   // [B, Hp] per-request column sums of dZ1 (for db1)
   float* dw_part;    // [Sb, Hp, H] split-K partial sums of dW1 (backward)
 };
 
 size_t lh_workspace_layout(int B, int k, int H, int Hp, char* base, LhWorkspace* ws);
 
-// Output tile of the length head's products (64 x 64), and the split of a
-// reduction of length K over slices for `tiles` output tiles: about 1024
-// workgroups, slices a multiple of 64 long and at least 256.
-constexpr int kLhTile = 64;
-inline long long lh_tiles(long long rows, long long cols) {
-  return ((rows + kLhTile - 1) / kLhTile) * ((cols + kLhTile - 1) / kLhTile);
-}
+// Output tiles of the length head's products: 64 x 64 for the projection
+// (about 1024 workgroups), 64 x 128 for the weight gradient (about 128
+// workgroups of four waves).  A reduction of length K is split over slices
+// for `tiles` tiles and `wgs` workgroups wanted: slices a multiple of 64, at
+// least 256 long and at most max_slice long.
+constexpr int kLhFwdTile = 64;
+constexpr int kLhTileR = 64, kLhTileC = 128;
 struct LhSplit {
   int S, kslice;
 };
-LhSplit lh_split_k(int K, long long tiles);
+LhSplit lh_split_k(int K, long long tiles, long long wgs, long long max_slice);
+// The projection h W1^T (reduction over H, tiles of [B k x H']) and the
+// weight gradient dZ1^T h (reduction over the B k rows, tiles of [H' x H],
+// slices short enough for 32-bit buffer offsets).
+LhSplit lh_split_fwd(int M, int H, int Hp);
+LhSplit lh_split_bwd(int M, int H, int Hp);
 
 struct LhArgs {
   const uint16_t* h;   // [B, k, H] bf16

@@ -74,7 +74,8 @@ def _check(lb: W.LengthHeadBatch, gamma: float):
     (9, 16, 128, 100, 1.3),    # ragged rows (M = 144) and columns
     (1, 1, 16, 1, 0.7),        # smallest shapes
     (3, 7, 32, 70, 0.9),       # k not a divisor of the tile, M = 21
-    (40, 16, 256, 64, 1.0),    # several row tiles
+    (40, 16, 256, 64, 1.0),    # several row tiles; the weight product in two slices
+    (37, 16, 400, 200, 1.1),   # every tile edge ragged: M = 592, H' = 200, H = 400
 ])
 def test_length_head_small(B, k, H, Hp, gamma):
     _check(W.length_head_inputs(B, k, H, Hp, seed=1000 + B * 7 + Hp), gamma)
