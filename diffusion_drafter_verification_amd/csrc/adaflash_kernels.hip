@@ -3287,9 +3287,12 @@ hipError_t launch(const LaunchArgs& a) {
   p.verify_len = a.verify_len;
   {
     // Residual workgroups of verification alone: enough chunks each that the
-    // B requests' workgroups fit the GPU at once (four per CU at that
-    // kernel's register use), at least one round.
-    const long long want = ((long long)a.B * p.G + 1023) / 1024;
+    // B requests' workgroups take two slots per CU (512), at least one
+    // round.  At B = 128, V = 151936 that is four workgroups of five chunks
+    // per request (129 us per verification call, against 132 with seven
+    // workgroups of three, 132 with five of four, 131 with four of six and
+    // 133 with two of ten).
+    const long long want = ((long long)a.B * p.G + 511) / 512;
     p.res_chunks = (int)(want < kResChunks ? kResChunks : (want > p.G ? p.G : want));
   }
 
