@@ -124,3 +124,35 @@ def test_cached_projection_equals_recomputed(B):
     z = f1["z1"].double().cpu().numpy()
     scale = np.abs(hh) @ np.abs(LH.bf16_to_f64(lb.W1)).T
     assert np.all(np.abs(z - ref) <= 1e-4 * scale + 1e-9)
+
+
+@pytest.mark.parametrize("B", [128, 9])
+def test_unaligned_weight_gradient_output(B):
+    """A dW1 that is not 16-byte aligned takes the workspace and the slice sum
+    instead of the weight product's direct 16-byte stores (one slice at these
+    sizes); its values equal those of an aligned dW1, and so do the other
+    outputs."""
+    import torch
+    import diffusion_drafter_verification_amd as ada
+    lb = W.length_head_inputs(B, 16, 4096 if B == 128 else 128, 256 if B == 128 else 100, seed=77 + B)
+    h = _dev(lb.hidden.view(np.int16), torch.bfloat16)
+    W1 = _dev(lb.W1.view(np.int16), torch.bfloat16)
+    b1, w2 = _dev(lb.b1), _dev(lb.w2)
+    A, L = _dev(lb.accept_len), _dev(lb.verify_len)
+    Bn, k, H = lb.hidden.shape
+    Hp = lb.W1.shape[0]
+    ws = ada.length_head_workspace(Bn, k, H, Hp)
+    outs = []
+    for offset in (0, 1):
+        store = torch.full((Hp * H + 4,), float("nan"), dtype=torch.float32, device="cuda")
+        dW1 = store[offset:offset + Hp * H].view(Hp, H)
+        assert (dW1.data_ptr() % 16 == 0) == (offset == 0)
+        o = {"loss": torch.empty(Bn, device="cuda"), "dW1": dW1, "db1": torch.empty(Hp, device="cuda"),
+             "dw2": torch.empty(Hp, device="cuda"), "db2": torch.empty(1, device="cuda")}
+        ada.adaflash_length_head_backward(h, W1, b1, w2, lb.b2, A, L, o["loss"], o["dW1"], o["db1"], o["dw2"],
+                                          o["db2"], ws)
+        torch.cuda.synchronize()
+        outs.append({key: v.clone() for key, v in o.items()})
+    assert torch.isfinite(outs[1]["dW1"]).all()
+    for key in ("loss", "dW1", "db1", "dw2", "db2"):
+        assert torch.equal(outs[0][key], outs[1][key]), key
